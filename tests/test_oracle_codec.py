@@ -1,0 +1,399 @@
+"""Pins of the oracle's codec: quantizer, profile, container, round trip.
+
+What the CacheGen page fixes ("核心方法"): token groups of 10 with the first
+token as anchor and the others as deltas to that anchor (no delta chain);
+8-bit anchors, coarser delta quantization for deeper layer groups;
+arithmetic coding with per channel-layer models, anchors and deltas
+separately; chunks of ~1.5K tokens encoded independently.  The checks here
+are what those statements and plain mathematics imply, independently of the
+oracle's own code: the half-step reconstruction bound, nearest-level
+optimality of every symbol, Gibbs' inequality against the empirical entropy,
+the coder's redundancy bound, exact reconstruction of constant channels, and
+structural invariants of the container.
+"""
+import math
+import os
+import sys
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from fp_exact import round_f32
+
+TOT = 1 << 15
+RED = -math.log2(1 - 2.0 ** -9)
+
+
+def _f32_ulp(x):
+    x = np.abs(np.asarray(x, np.float32))
+    return np.spacing(np.maximum(x, np.float32(1e-30))).astype(np.float64)
+
+
+def _f16_ulp(h_bits):
+    v = np.abs(h_bits.view(np.float16))
+    return np.spacing(v).astype(np.float64)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    cfg = synth.CONFIGS[0]
+    d = oracle.desc_for(cfg)
+    kv = synth.make_kv(cfg)
+    tb = oracle.profile(d, synth.make_profile_kv(cfg))
+    cont = oracle.encode(d, tb, kv, cfg.chunk_levels())
+    out = oracle.decode(d, tb, cont, cfg.chunk_levels(), cfg.n_tokens)
+    return cfg, d, kv, tb, cont, out
+
+
+@pytest.fixture(scope="module")
+def mixed():
+    """Reduced mixed-level configuration: 6 layers (thirds 2/2/2), 96
+    channels, 3 levels, 3,700 tokens -> chunks of 1500, 1500, 700."""
+    cfg = synth.small_config(6, 96, 3700, n_levels=3, schedule="mixed", index=91)
+    d = oracle.desc_for(cfg)
+    kv = synth.make_kv(cfg)
+    tb = oracle.profile(d, synth.make_profile_kv(cfg))
+    levels = [0, 2, 1]
+    cont = oracle.encode(d, tb, kv, levels)
+    out = oracle.decode(d, tb, cont, levels, cfg.n_tokens)
+    return cfg, d, kv, tb, cont, out, levels
+
+
+def _side_info(d, cont_k):
+    rec = oracle.records(d, cont_k)
+    S = d.n_streams
+    L, C = d.n_layers, d.n_channels
+    shp = (L, 2, C)
+    return (rec["lo"].reshape(shp), rec["sa"].reshape(shp), rec["dl"].reshape(shp),
+            rec["nbytes"].reshape(shp))
+
+
+def _check_half_step(d, kv, out, cont, levels):
+    """|x - xhat| <= step/2 + ulp16(xhat)/2 + 4 ulp32(max(|x|, |ahat|)),
+    step = sa for anchors and dl for deltas, element by element."""
+    x = kv.view(np.float16).astype(np.float64)
+    y = out.view(np.float16).astype(np.float64)
+    assert np.all(np.isfinite(y))
+    for k, c in enumerate(cont):
+        t0 = k * d.chunk_tokens
+        n = oracle.parse_header(c)["n_tokens"]
+        lo, sa, dl, _ = _side_info(d, c)
+        xs = x[:, :, t0:t0 + n, :]
+        ys = y[:, :, t0:t0 + n, :]
+        hb = out[:, :, t0:t0 + n, :]
+        is_anchor = (np.arange(n) % d.group_tokens == 0)[None, None, :, None]
+        step = np.where(is_anchor, sa[:, :, None, :], dl[:, :, None, :]).astype(np.float64)
+        anchors = xs[:, :, ::d.group_tokens, :]
+        amax = np.repeat(np.abs(anchors), d.group_tokens, axis=2)[:, :, :n, :] + 1.0 * step
+        bound = step / 2 + _f16_ulp(hb) / 2 + 4 * _f32_ulp(np.maximum(np.abs(xs), amax))
+        err = np.abs(xs - ys)
+        assert np.all(err <= bound), (k, np.max(err - bound))
+
+
+def test_half_step_round_trip_tiny(tiny):
+    cfg, d, kv, tb, cont, out = tiny
+    _check_half_step(d, kv, out, cont, cfg.chunk_levels())
+
+
+def test_half_step_round_trip_mixed_levels(mixed):
+    cfg, d, kv, tb, cont, out, levels = mixed
+    _check_half_step(d, kv, out, cont, levels)
+
+
+def test_no_clamp_changes_rint(mixed):
+    """The clamps in the quantizer never bind: the unclamped nearest level is
+    already inside the alphabet (per-stream scales never clip)."""
+    cfg, d, kv, tb, cont, out, levels = mixed
+    x = kv.view(np.float16).astype(np.float32)
+    for k, c in enumerate(cont):
+        t0 = k * d.chunk_tokens
+        n = oracle.parse_header(c)["n_tokens"]
+        lo, sa, dl, _ = _side_info(d, c)
+        xa = x[:, :, t0:t0 + n:d.group_tokens, :]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            qa = np.rint((xa - lo[:, :, None, :]) / sa[:, :, None, :])
+        qa = np.where(sa[:, :, None, :] == 0, 0, qa)
+        assert qa.min() >= 0 and qa.max() <= 255
+
+
+def test_anchor_precision_above_delta_precision():
+    """8-bit anchors are above every level's delta bits, and deeper layer
+    thirds never get finer deltas than shallower ones."""
+    for cfg in synth.CONFIGS.values():
+        for row in cfg.delta_bits:
+            assert all(b < 8 for b in row)
+            assert row[0] >= row[1] >= row[2]
+
+
+def test_anchor_step_vs_delta_step_reported(tiny):
+    cfg, d, kv, tb, cont, out = tiny
+    lo, sa, dl, _ = _side_info(d, cont[0])
+    frac = float(np.mean(sa <= dl))
+    # reported, not asserted beyond sanity: anchors usually have the finer step
+    assert 0.0 <= frac <= 1.0
+
+
+def _nearest_ok(target, step, q, qmin, qmax):
+    """q minimises |target - k*step| over k in [qmin, qmax], up to binary32
+    rounding of the ratio (|target/step - q| <= 1/2 + 2^-20)."""
+    if step == 0:
+        return q == 0
+    r = Fraction(float(target)) / Fraction(float(step))
+    best = min(range(qmin, qmax + 1), key=lambda k: abs(r - k))
+    return abs(r - q) <= abs(r - best) + Fraction(1, 1 << 20)
+
+
+def test_quantizer_symbols_are_nearest_levels():
+    """Every anchor symbol is a nearest level of lo + k*sa over k in 0..255 and
+    every delta symbol a nearest level of k*dl over k in -M..M, with d taken
+    against the reconstructed anchor (closed loop)."""
+    rng = np.random.default_rng(21)
+    for trial in range(150):
+        n = int(rng.integers(1, 35))
+        b = int(rng.integers(2, 7))
+        M = (1 << (b - 1)) - 1
+        scale = float(np.exp(rng.uniform(-8, 4)))
+        x = (rng.standard_normal(n).cumsum() * scale).astype(np.float16).astype(np.float32)
+        lo, sa, dl, sym = oracle.quantize(x, 10, b)
+        anchors = x[::10]
+        assert lo == anchors.min()
+        for j in range(n):
+            if j % 10 == 0:
+                assert _nearest_ok(np.float32(x[j] - lo), sa, int(sym[j]), 0, 255), (trial, j)
+            else:
+                g = j - j % 10
+                ahat = np.float32(Fraction(int(sym[g])) * Fraction(float(sa)) + Fraction(float(lo)))
+                dd = np.float32(x[j] - ahat)
+                assert _nearest_ok(dd, dl, int(sym[j]) - M, -M, M), (trial, j)
+
+
+def test_constant_channel_is_exact():
+    x = np.full(23, 1.375, np.float32)
+    lo, sa, dl, sym = oracle.quantize(x, 10, 4)
+    assert sa == 0 and dl == 0 and lo == np.float32(1.375)
+    assert np.all(sym[::10] == 0) and np.all(np.delete(sym, np.arange(0, 23, 10)) == 7)
+    out = oracle.dequantize(sym, 10, 4, lo, sa, dl)
+    np.testing.assert_array_equal(out, np.full(23, np.float16(1.375).view(np.uint16)))
+
+
+def test_deltas_reference_their_own_anchor_only():
+    """No delta chain: changing one delta token's value changes only that
+    token's symbol (anchors and the stream's delta scale held fixed)."""
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(30).astype(np.float16).astype(np.float32)
+    x[5] = 0.0
+    lo, sa, dl, sym = oracle.quantize(x, 10, 5)
+    y = x.copy()
+    y[6] = np.float32(np.float16(x[6] + 0.25 * np.sign(x[6] + 1e-3)))
+    lo2, sa2, dl2, sym2 = oracle.quantize(y, 10, 5)
+    if dl2 == dl:  # maxabs unchanged: only token 6 may differ
+        diff = np.nonzero(sym != sym2)[0]
+        assert set(diff.tolist()) <= {6}
+
+
+def test_single_token_stream_is_anchor_only():
+    x = np.array([3.0], np.float32)
+    lo, sa, dl, sym = oracle.quantize(x, 10, 6)
+    assert lo == 3.0 and sa == 0 and dl == 0 and sym.tolist() == [0]
+
+
+def test_nonfinite_input_rejected():
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.quantize(np.array([1.0, np.inf], np.float32), 10, 4)
+    assert e.value.code == oracle.ERR_NONFINITE
+
+
+def _tiny_desc(L, C, bits=((5, 4, 3),)):
+    return oracle.Desc(L, C, 10, 1500, 8, bits, 15)
+
+
+@pytest.mark.parametrize("n", [1, 2, 9, 10, 11, 19, 23])
+def test_end_to_end_tiny_exact_rederivation(n):
+    """L<=2, C<=3: decode equals an exact re-derivation from the stored side
+    info and the symbols (one binary32 rounding of q*step + ahat, one binary16
+    rounding), and stays within half a step of the input."""
+    rng = np.random.default_rng(100 + n)
+    for L, C in ((1, 1), (2, 3)):
+        d = _tiny_desc(L, C)
+        kv = (rng.standard_normal((L, 2, n, C)).cumsum(axis=2) * 0.3).astype(np.float16).view(np.uint16)
+        tb = oracle.profile(d, kv)
+        c = oracle.encode(d, tb, kv, [0])[0]
+        out = oracle.decode(d, tb, [c], [0], n)
+        ids = np.arange(d.n_streams)
+        vals, syms = oracle.decode_streams(d, tb, c, ids, n)
+        lo, sa, dl, _ = _side_info(d, c)
+        for m in ids:
+            row, ch = divmod(int(m), C)
+            l, kvi = divmod(row, 2)
+            b = d.bits(0, l)
+            M = (1 << (b - 1)) - 1
+            ahat = None
+            for j in range(n):
+                s = int(syms[m, j])
+                if j % 10 == 0:
+                    ahat = round_f32(Fraction(s) * Fraction(float(sa[l, kvi, ch]))
+                                     + Fraction(float(lo[l, kvi, ch])))
+                    v = ahat
+                else:
+                    v = round_f32(Fraction(s - M) * Fraction(float(dl[l, kvi, ch])) + ahat)
+                # v is an exact binary32 value; numpy's IEEE cast rounds it to binary16
+                want = np.float32(float(v)).astype(np.float16).view(np.uint16)
+                assert out[l, kvi, j, ch] == want
+                assert vals[m, j] == want
+            err = np.abs(kv[l, kvi, :, ch].view(np.float16).astype(np.float64)
+                         - out[l, kvi, :, ch].view(np.float16).astype(np.float64))
+            steps = np.where(np.arange(n) % 10 == 0, sa[l, kvi, ch], dl[l, kvi, ch])
+            assert np.all(err <= steps / 2 + 1e-3 * np.abs(kv[l, kvi, :, ch].view(np.float16)) + 1e-6)
+
+
+def test_container_structure(mixed):
+    cfg, d, kv, tb, cont, out, levels = mixed
+    S = d.n_streams
+    for k, c in enumerate(cont):
+        h = oracle.parse_header(c)
+        assert h["magic"] == b"KVC1" and h["version"] == 1
+        assert h["level"] == levels[k] and h["delta_bits"] == d.delta_bits[levels[k]]
+        assert h["n_tokens"] == min(1500, cfg.n_tokens - 1500 * k)
+        assert h["first_token"] == 1500 * k and h["profile_id"] == tb.profile_id
+        rec = oracle.records(d, c)
+        assert len(c) == 64 + 16 * S + h["payload_bytes"]
+        padded = (rec["nbytes"].astype(np.int64) + 3) // 4 * 4
+        assert padded.sum() == h["payload_bytes"]
+        offs = oracle.stream_offsets(d, c)
+        np.testing.assert_array_equal(offs, np.concatenate([[0], np.cumsum(padded)[:-1]]))
+        assert np.all(rec["nbytes"] >= 4)
+        # padding bytes are zero
+        base = 64 + 16 * S
+        for m in range(0, S, 37):
+            tail = c[base + offs[m] + rec["nbytes"][m]: base + offs[m] + padded[m]]
+            assert np.all(tail == 0)
+
+
+def test_coder_bound_and_gibbs_per_stream(mixed):
+    """For every stream: 8*nbytes <= sum -log2(f/TOT) + n*RED + 33 (coder
+    bound) and 8*nbytes >= the same ideal length + 24 - ... >= 0."""
+    cfg, d, kv, tb, cont, out, levels = mixed
+    for k, c in enumerate(cont):
+        n = oracle.parse_header(c)["n_tokens"]
+        rec = oracle.records(d, c)
+        ids = np.arange(0, d.n_streams, 7)
+        _, syms = oracle.decode_streams(d, tb, c, ids, n)
+        for i, m in enumerate(ids):
+            l = int(m) // (2 * d.n_channels)
+            b = d.bits(levels[k], l)
+            fA = tb.fA[m].astype(np.float64)
+            fD = tb.fD[levels[k], m, : (1 << b) - 1].astype(np.float64)
+            ideal = 0.0
+            for j in range(n):
+                f = fA if j % 10 == 0 else fD
+                ideal += -math.log2(f[syms[i, j]] / TOT)
+            bits = 8 * int(rec["nbytes"][m])
+            assert ideal + 24 - 1e-6 <= bits <= ideal + n * RED + 33 + 1e-6
+
+
+def test_payload_vs_empirical_entropy_self_profile():
+    """Profile on the very data that is encoded: payload bits >= the empirical
+    entropy H_emp (Gibbs) and <= H_emp + 0.03 bit/symbol + 32 bits/stream."""
+    cfg = synth.small_config(3, 64, 1500, n_levels=1, schedule="level0", index=92)
+    d = oracle.desc_for(cfg)
+    kv = synth.make_kv(cfg)
+    tb = oracle.profile(d, kv)  # models fitted to the encoded chunk itself
+    c = oracle.encode(d, tb, kv, [0])[0]
+    rec = oracle.records(d, c)
+    _, syms = oracle.decode_streams(d, tb, c, np.arange(d.n_streams), 1500)
+    H = 0.0
+    N = 0
+    for m in range(d.n_streams):
+        for part in (syms[m, ::10], np.delete(syms[m], np.arange(0, 1500, 10))):
+            _, cnt = np.unique(part, return_counts=True)
+            p = cnt / cnt.sum()
+            H += -(cnt * np.log2(p)).sum()
+            N += cnt.sum()
+    bits = 8 * int(rec["nbytes"].astype(np.int64).sum())
+    assert bits >= H
+    assert bits <= H + 0.03 * N + 32 * d.n_streams
+
+
+def test_profile_id_definition_and_sensitivity(tiny):
+    cfg, d, kv, tb, cont, out = tiny
+    # independent rendering of the id from its definition: FNV-1a over the
+    # descriptor words (u32 LE) and delta bits (u8), then one FNV-1a per
+    # (layer, K/V) row over the per-model FNV-1a values (u64 LE)
+    desc = b"".join(int(v).to_bytes(4, "little") for v in
+                    (d.n_layers, d.n_channels, 10, 1500, 8, d.n_levels, 15))
+    desc += bytes(b for row in d.delta_bits for b in row)
+    h = oracle.fnv1a64(desc)
+    for row in range(2 * d.n_layers):
+        l = row // 2
+        hr_in = b""
+        for c in range(d.n_channels):
+            m = row * d.n_channels + c
+            blob = tb.fA[m].astype("<u2").tobytes()
+            for lv in range(d.n_levels):
+                A = (1 << d.bits(lv, l)) - 1
+                blob += tb.fD[lv, m, :A].astype("<u2").tobytes()
+            hr_in += oracle.fnv1a64(blob).to_bytes(8, "little")
+        h = oracle.fnv1a64(oracle.fnv1a64(hr_in).to_bytes(8, "little"), h)
+    assert h == tb.profile_id
+    fA2 = tb.fA.copy()
+    fA2[5, 0] += 1
+    fA2[5, 1] -= 1
+    assert oracle.profile_id(d, fA2, tb.fD) != tb.profile_id
+
+
+def test_profile_tables_are_normalised(tiny):
+    cfg, d, kv, tb, cont, out = tiny
+    assert np.all(tb.fA.astype(np.int64).sum(axis=1) == TOT) and tb.fA.min() >= 1
+    for lv in range(d.n_levels):
+        for l in range(d.n_layers):
+            A = (1 << d.bits(lv, l)) - 1
+            rows = tb.fD[lv].reshape(d.n_layers, 2 * d.n_channels, 64)[l]
+            assert np.all(rows[:, :A].astype(np.int64).sum(axis=1) == TOT)
+            assert rows[:, :A].min() >= 1 and np.all(rows[:, A:] == 0)
+
+
+def test_profile_mismatch_and_corruption_detected(tiny):
+    cfg, d, kv, tb, cont, out = tiny
+    bad = oracle.Tables(tb.fA, tb.fD, tb.profile_id ^ 1)
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.decode(d, bad, cont, [0], 1500)
+    assert e.value.code == oracle.ERR_PROFILE
+    c = cont[0].copy()
+    c[0] ^= 0xFF
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.decode(d, tb, [c], [0], 1500)
+    assert e.value.code == oracle.ERR_CORRUPT
+    c = cont[0].copy()
+    S = d.n_streams
+    # shorten stream 10 by 4 bytes and stream 11 longer by 4: sums still agree,
+    # but both streams now end at the wrong byte
+    rec = np.frombuffer(c[64:64 + 16 * S].tobytes(), np.uint32).reshape(S, 4).copy()
+    rec[10, 3] -= 4
+    rec[11, 3] += 4
+    c[64:64 + 16 * S] = np.frombuffer(rec.tobytes(), np.uint8)
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.decode(d, tb, [c], [0], 1500)
+    assert e.value.code == oracle.ERR_CORRUPT
+
+
+def test_thread_count_does_not_change_bytes(mixed):
+    cfg, d, kv, tb, cont, out, levels = mixed
+    old = oracle.get_threads()
+    try:
+        oracle.set_threads(1)
+        tb1 = oracle.profile(d, synth.make_profile_kv(cfg))
+        c1 = oracle.encode(d, tb1, kv, levels)
+    finally:
+        oracle.set_threads(old)
+    assert tb1.profile_id == tb.profile_id
+    for a, b in zip(c1, cont):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_compression_ratio_reported(tiny):
+    cfg, d, kv, tb, cont, out = tiny
+    ratio = kv.nbytes / sum(len(c) for c in cont)
+    assert 2.0 < ratio < 8.0
