@@ -1,0 +1,187 @@
+/*
+ * kvc.h -- C ABI of libkvc, an MI355X (gfx950) KV-cache codec in the style of
+ * CacheGen ("CacheGen: KV Cache Compression and Streaming for Fast Large
+ * Language Model Serving", SIGCOMM 2024; wiki summary page, section 核心方法).
+ *
+ * The page's pipeline: split the KV cache along tokens into chunks of about
+ * 1.5K tokens; inside a chunk, group tokens by 10 with the first token as an
+ * 8-bit anchor and the others as deltas to it; quantize deltas more coarsely
+ * for deeper thirds of the layers; arithmetic-code the symbols against
+ * distributions profiled offline per channel-layer combination (anchors and
+ * deltas separately); store each chunk at several compression levels; on
+ * restore, fetch chunks, decode them on the GPU and concatenate them into the
+ * KV cache.  The exact numeric definitions used here (quantizers, range
+ * coder, container layout, profile id) are the ones written out in the
+ * project's design notes; all entry points below follow them.
+ *
+ * Conventions (all entry points):
+ *  - Tensor arguments are DEVICE pointers owned by the caller; host arrays are
+ *    marked "host".  The library never allocates or frees device memory and
+ *    keeps no device state between calls: scratch space is the caller's
+ *    workspace `ws` of at least the size returned by the matching *_ws_bytes
+ *    query (any alignment of 256 bytes or more).
+ *  - Every call is asynchronous on `stream` (a hipStream_t, e.g. torch's
+ *    current stream).  Argument and shape errors are returned synchronously
+ *    before anything is launched or written.
+ *  - Errors found on the device (corrupt bitstream, profile mismatch,
+ *    non-finite input, output capacity) are written to the caller's device
+ *    word `*dev_status`: each call first sets it to 0 (stream-ordered), then
+ *    the first error code seen (a negative kvc_status) replaces the 0.  Read
+ *    it after synchronizing the stream.  On such an error the contents of the
+ *    output are unspecified, but nothing outside the output and `ws` is
+ *    written.
+ *  - KV layout: binary16 bit patterns in [layer][K=0,V=1][token][channel],
+ *    channel fastest; C channels per K and per V (kv_heads * head_dim).
+ *  - Calls on distinct workspaces may run concurrently; calls sharing a
+ *    workspace must be ordered on one stream.
+ */
+#ifndef KVC_H_
+#define KVC_H_
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_ERR_INVALID_ARG = -1,     /* bad descriptor, null pointer, bad level */
+  KVC_ERR_SHAPE = -2,           /* token ranges / sizes inconsistent */
+  KVC_ERR_PROFILE_MISMATCH = -3,/* container made with other tables */
+  KVC_ERR_CORRUPT_STREAM = -4,  /* bad header, bad lengths, undecodable bytes */
+  KVC_ERR_NONFINITE = -5,       /* inf / NaN in the KV to encode or profile */
+  KVC_ERR_CAPACITY = -6,        /* workspace or output buffer too small */
+  KVC_ERR_HIP = -7,             /* a HIP runtime call failed */
+  KVC_ERR_UNIMPLEMENTED = -8
+} kvc_status;
+
+/* Codec descriptor: the page's constants (chunks of ~1.5K tokens, groups of
+ * 10 tokens, 8-bit anchors, coarser deltas for deeper layer thirds).
+ * Supported: group_tokens in [1, chunk_tokens], anchor_bits == 8,
+ * cdf_prec_bits == 15, n_levels in [1, 4], delta_bits in [2, 6]. */
+typedef struct {
+  uint32_t n_layers;         /* L >= 1 */
+  uint32_t n_channels;       /* C >= 1, per K and per V */
+  uint32_t group_tokens;     /* 10 */
+  uint32_t chunk_tokens;     /* 1500 */
+  uint32_t anchor_bits;      /* 8 */
+  uint32_t n_levels;         /* compression levels held by the tables */
+  uint8_t delta_bits[4][3];  /* [level][layer third], third(l) = 3l / L */
+  uint32_t cdf_prec_bits;    /* 15 */
+} kvc_codec_desc;
+
+/* One encoded chunk handed to the decoder (a fetched bitstream). */
+typedef struct {
+  const uint8_t *container; /* device pointer to the chunk's container */
+  uint64_t container_bytes; /* its size in bytes */
+  uint32_t first_token;     /* destination token offset in kv_out */
+  uint32_t n_tokens;        /* tokens in the chunk; must equal the header */
+  uint32_t level;           /* compression level; must equal the header */
+  uint32_t reserved;        /* 0 */
+} kvc_chunk_ref;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int kvc_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char *kvc_status_str(kvc_status s);
+
+/* KVC_OK if the descriptor is supported, else KVC_ERR_INVALID_ARG. */
+kvc_status kvc_validate_desc(const kvc_codec_desc *d);
+
+/* ---------------------------------------------------------------- tables */
+/* Size in bytes of the profiled tables blob: a 128-byte header, then the
+ * anchor cumulative frequencies [2LC][264] u16, then the delta cumulative
+ * frequencies [n_levels][2LC][64] u16.  0 if the descriptor is invalid. */
+uint64_t kvc_tables_bytes(const kvc_codec_desc *d);
+
+/* Workspace bytes needed by kvc_profile. */
+uint64_t kvc_profile_ws_bytes(const kvc_codec_desc *d);
+
+/*
+ * Offline profiling (CacheGen page, 核心方法 step 3 and 关键观察 observation
+ * 3: distributions profiled per channel-layer combination and reused across
+ * contexts of the same model).  kv_fp16: profiling KV [L][2][T][C]; it is
+ * split into chunks of chunk_tokens and every chunk is quantized (anchors
+ * once, deltas once per level); symbol counts are normalised to 2^15 per
+ * model.  Writes the tables blob (kvc_tables_bytes bytes) including its
+ * 64-bit profile id.  Device errors: KVC_ERR_NONFINITE.
+ */
+kvc_status kvc_profile(const kvc_codec_desc *d, const uint16_t *kv_fp16, uint32_t T,
+                       void *tables_out, void *ws, uint64_t ws_bytes, int32_t *dev_status,
+                       hipStream_t stream);
+
+/* ---------------------------------------------------------------- encode */
+/* Upper bound of one chunk's container for n_tokens tokens. */
+uint64_t kvc_container_bound(const kvc_codec_desc *d, uint32_t n_tokens);
+
+/* Upper bound of all containers of a T-token context (sum over chunks). */
+uint64_t kvc_encode_bound(const kvc_codec_desc *d, uint32_t T);
+
+/* Workspace bytes needed by kvc_encode for a T-token context. */
+uint64_t kvc_encode_ws_bytes(const kvc_codec_desc *d, uint32_t T);
+
+/*
+ * Encode a T-token KV cache (CacheGen page, 核心方法 steps 1-3: chunking,
+ * change-based anchor/delta encoding, layer-wise quantization, arithmetic
+ * coding).  Chunk k = tokens [k*chunk_tokens, ...) is coded at level
+ * chunk_levels[k] (host array of ceil(T / chunk_tokens) entries) into one
+ * container; containers are written back to back into `out` (device,
+ * out_cap bytes) and chunk_offsets_out (device, n_chunks + 1 u64) receives
+ * each container's start offset and, last, the total size.
+ * Device errors: KVC_ERR_NONFINITE, KVC_ERR_CAPACITY (out_cap too small; the
+ * offsets are still written, `out` is not).
+ */
+kvc_status kvc_encode(const kvc_codec_desc *d, const void *tables, const uint16_t *kv_fp16,
+                      uint32_t T, const uint8_t *chunk_levels, uint8_t *out, uint64_t out_cap,
+                      uint64_t *chunk_offsets_out, void *ws, uint64_t ws_bytes,
+                      int32_t *dev_status, hipStream_t stream);
+
+/* ---------------------------------------------------------------- decode */
+/* Workspace bytes needed by kvc_decode / kvc_decode_index for n_chunks. */
+uint64_t kvc_decode_ws_bytes(const kvc_codec_desc *d, uint32_t n_chunks);
+
+/*
+ * Decode fetched chunks back into the KV cache (CacheGen page, 核心方法: the
+ * online side decodes each chunk's bitstream to tensors and concatenates the
+ * chunks into the KV cache).  chunks: host array of n_chunks references whose
+ * token ranges [first_token, first_token + n_tokens) must be disjoint and
+ * inside [0, T_total).  kv_out: device [L][2][T_total][C] binary16; tokens
+ * outside the chunks' ranges are not written.  One call runs the bitstream
+ * index (per-stream offsets, header checks) and then the fused range-decode /
+ * dequantize / store kernel.
+ * Device errors: KVC_ERR_PROFILE_MISMATCH, KVC_ERR_CORRUPT_STREAM.
+ */
+kvc_status kvc_decode(const kvc_codec_desc *d, const void *tables, const kvc_chunk_ref *chunks,
+                      uint32_t n_chunks, uint16_t *kv_out, uint32_t T_total, void *ws,
+                      uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream);
+
+/*
+ * The bitstream index alone: validates the containers' headers against the
+ * tables and writes offsets_out (device, [n_chunks][2LC] u32): each stream's
+ * byte offset from the start of its container's payload (exclusive prefix
+ * sum of the 4-byte-padded stream lengths).  Used by kvc_decode; exported for
+ * inspection and tests.
+ */
+kvc_status kvc_decode_index(const kvc_codec_desc *d, const void *tables,
+                            const kvc_chunk_ref *chunks, uint32_t n_chunks, uint32_t *offsets_out,
+                            void *ws, uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream);
+
+/*
+ * Debug form of kvc_decode: same kernels, but writes the decoded symbols
+ * (u8: anchor 0..255, delta q + M) to sym_out [L][2][T_total][C] instead of
+ * binary16 values.
+ */
+kvc_status kvc_decode_symbols(const kvc_codec_desc *d, const void *tables,
+                              const kvc_chunk_ref *chunks, uint32_t n_chunks, uint8_t *sym_out,
+                              uint32_t T_total, void *ws, uint64_t ws_bytes, int32_t *dev_status,
+                              hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H_ */

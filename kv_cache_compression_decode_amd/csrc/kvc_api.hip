@@ -1,0 +1,313 @@
+// Host side of the libkvc C ABI: argument validation, workspace layout and
+// the stream-ordered launch sequences of profile / encode / decode.
+#include <algorithm>
+#include <vector>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+hipError_t launch_reset_status(int32_t *status, hipStream_t stream);
+hipError_t launch_load_chunks(const ChunkInfo *host_chunks, uint32_t n_chunks,
+                              ChunkInfo *dev_chunks, hipStream_t stream);
+hipError_t launch_index(const Desc &d, const ChunkInfo *dev_chunks, uint32_t n_chunks,
+                        uint64_t *row_sums, uint8_t *hdr_ok, uint32_t *offsets, uint8_t *valid,
+                        uint64_t *payload, const uint8_t *tables, int check_header_flag,
+                        int32_t *status, hipStream_t stream);
+hipError_t launch_decode(const Desc &d, const ChunkInfo *dev_chunks, uint32_t n_chunks,
+                         const uint8_t *valid, const uint32_t *offsets, const uint8_t *tables,
+                         void *out, uint32_t T_total, bool symbols, int32_t *status,
+                         hipStream_t stream);
+hipError_t launch_encode(const Desc &d, const uint8_t *tables, const uint16_t *kv, uint32_t T,
+                         const ChunkInfo *dev_chunks, uint32_t n_chunks, uint8_t *records,
+                         uint64_t *row_sums, uint8_t *hdr_ok, uint32_t *offsets, uint8_t *valid,
+                         uint64_t *payload, uint64_t *chunk_off_ws, uint32_t *fits, uint8_t *out,
+                         uint64_t out_cap, uint64_t *chunk_off_out, int32_t *status,
+                         hipStream_t stream);
+hipError_t launch_profile(const Desc &d, const uint16_t *kv, uint32_t T, uint8_t *tables,
+                          uint32_t *counts, uint64_t *model_hash, uint64_t *row_hash,
+                          int32_t *status, hipStream_t stream);
+}  // namespace kvc
+
+using namespace kvc;
+
+namespace {
+
+bool desc_ok(const kvc_codec_desc *d) {
+  if (!d) return false;
+  if (d->n_layers < 1 || d->n_layers > 32767) return false;
+  if (d->n_channels < 1 || d->n_channels > (1u << 24)) return false;
+  if ((uint64_t)2 * d->n_layers * d->n_channels >= (1ull << 31)) return false;
+  if (d->chunk_tokens < 1 || d->chunk_tokens > 65535) return false;
+  if (d->group_tokens < 1 || d->group_tokens > d->chunk_tokens) return false;
+  if (d->anchor_bits != 8 || d->cdf_prec_bits != kPrec) return false;
+  if (d->n_levels < 1 || d->n_levels > 4) return false;
+  for (uint32_t lv = 0; lv < d->n_levels; ++lv)
+    for (int t = 0; t < 3; ++t)
+      if (d->delta_bits[lv][t] < 2 || d->delta_bits[lv][t] > 6) return false;
+  return true;
+}
+
+Desc to_desc(const kvc_codec_desc *d) {
+  Desc r;
+  r.L = d->n_layers;
+  r.C = d->n_channels;
+  r.G = d->group_tokens;
+  r.chunk = d->chunk_tokens;
+  r.nlev = d->n_levels;
+  for (int lv = 0; lv < 4; ++lv)
+    for (int t = 0; t < 3; ++t) r.bits[lv][t] = lv < (int)d->n_levels ? d->delta_bits[lv][t] : 0;
+  return r;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Workspace layout shared by decode and encode (encode adds its tail).
+struct WsLayout {
+  uint64_t chunks, rows, hdr, valid, payload, offsets, records, chunk_off, fits, total;
+};
+
+WsLayout ws_layout(const Desc &d, uint32_t K, bool encode) {
+  const uint64_t S = n_streams(d);
+  WsLayout w;
+  w.chunks = 0;
+  w.rows = align256(w.chunks + (uint64_t)K * sizeof(ChunkInfo));
+  w.hdr = align256(w.rows + (uint64_t)K * 2 * d.L * 8);
+  w.valid = align256(w.hdr + K);
+  w.payload = align256(w.valid + K);
+  w.offsets = align256(w.payload + (uint64_t)K * 8);
+  uint64_t end = w.offsets + (uint64_t)K * S * 4;
+  w.records = w.chunk_off = w.fits = 0;
+  if (encode) {
+    w.records = align256(end);
+    w.chunk_off = align256(w.records + (uint64_t)K * S * kRecBytes);
+    w.fits = align256(w.chunk_off + (uint64_t)(K + 1) * 8);
+    end = w.fits + 4;
+  }
+  w.total = align256(end);
+  return w;
+}
+
+uint64_t container_bound_n(const Desc &d, uint32_t n) {
+  const uint64_t S = n_streams(d);
+  return kHdrBytes + kRecBytes * S + S * pad4(4ull + 2ull * n);
+}
+
+kvc_status hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
+
+kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc_chunk_ref *chunks,
+                         uint32_t n_chunks, void *out, uint32_t T_total, void *ws,
+                         uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream, int mode,
+                         uint32_t *offsets_out) {
+  // mode 0: values, 1: symbols, 2: index only
+  if (!desc_ok(dd)) return KVC_ERR_INVALID_ARG;
+  const Desc d = to_desc(dd);
+  if (!tables || !aligned(tables, 16) || !dev_status || !aligned(dev_status, 4))
+    return KVC_ERR_INVALID_ARG;
+  if (n_chunks > 65535) return KVC_ERR_SHAPE;
+  if (n_chunks && !chunks) return KVC_ERR_INVALID_ARG;
+  if (mode != 2 && n_chunks && (!out || !aligned(out, mode == 0 ? 2 : 1)))
+    return KVC_ERR_INVALID_ARG;
+  if (mode == 2 && n_chunks && (!offsets_out || !aligned(offsets_out, 4)))
+    return KVC_ERR_INVALID_ARG;
+  const WsLayout w = ws_layout(d, n_chunks, false);
+  if (n_chunks && (!ws || !aligned(ws, 256))) return KVC_ERR_INVALID_ARG;
+  if (ws_bytes < w.total) return KVC_ERR_CAPACITY;
+  const uint64_t S = n_streams(d);
+  std::vector<ChunkInfo> info(n_chunks);
+  std::vector<std::pair<uint32_t, uint32_t>> ranges(n_chunks);
+  for (uint32_t k = 0; k < n_chunks; ++k) {
+    const kvc_chunk_ref &c = chunks[k];
+    if (!c.container || !aligned(c.container, 4)) return KVC_ERR_INVALID_ARG;
+    if (c.level >= d.nlev || c.reserved != 0) return KVC_ERR_INVALID_ARG;
+    if (c.n_tokens < 1 || c.n_tokens > d.chunk) return KVC_ERR_SHAPE;
+    if (mode != 2 && (uint64_t)c.first_token + c.n_tokens > T_total) return KVC_ERR_SHAPE;
+    if (c.container_bytes < kHdrBytes + kRecBytes * S) return KVC_ERR_SHAPE;
+    info[k].cont = c.container;
+    info[k].records = c.container + kHdrBytes;
+    info[k].cont_bytes = c.container_bytes;
+    info[k].first_token = c.first_token;
+    info[k].n_tokens = c.n_tokens;
+    info[k].level = c.level;
+    info[k].pad0 = 0;
+    info[k].pad1 = 0;
+    ranges[k] = {c.first_token, c.first_token + c.n_tokens};
+  }
+  if (mode != 2) {
+    std::sort(ranges.begin(), ranges.end());
+    for (uint32_t k = 1; k < n_chunks; ++k)
+      if (ranges[k].first < ranges[k - 1].second) return KVC_ERR_SHAPE;
+  }
+  hipError_t e = launch_reset_status(dev_status, stream);
+  if (e != hipSuccess || n_chunks == 0) return hip_status(e);
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  ChunkInfo *dch = reinterpret_cast<ChunkInfo *>(base + w.chunks);
+  uint32_t *offs = mode == 2 ? offsets_out : reinterpret_cast<uint32_t *>(base + w.offsets);
+  e = launch_load_chunks(info.data(), n_chunks, dch, stream);
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  e = launch_index(d, dch, n_chunks, reinterpret_cast<uint64_t *>(base + w.rows), base + w.hdr,
+                   offs, base + w.valid, reinterpret_cast<uint64_t *>(base + w.payload),
+                   static_cast<const uint8_t *>(tables), 1, dev_status, stream);
+  if (e != hipSuccess || mode == 2) return hip_status(e);
+  e = launch_decode(d, dch, n_chunks, base + w.valid, offs, static_cast<const uint8_t *>(tables),
+                    out, T_total, mode == 1, dev_status, stream);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvc_version(void) { return 100; }
+
+const char *kvc_status_str(kvc_status s) {
+  switch (s) {
+    case KVC_OK: return "ok";
+    case KVC_ERR_INVALID_ARG: return "invalid argument";
+    case KVC_ERR_SHAPE: return "inconsistent shape or token range";
+    case KVC_ERR_PROFILE_MISMATCH: return "container was encoded with other tables";
+    case KVC_ERR_CORRUPT_STREAM: return "corrupt container or bitstream";
+    case KVC_ERR_NONFINITE: return "non-finite value in the input";
+    case KVC_ERR_CAPACITY: return "buffer or workspace too small";
+    case KVC_ERR_HIP: return "HIP runtime error";
+    case KVC_ERR_UNIMPLEMENTED: return "not implemented";
+  }
+  return "unknown status";
+}
+
+kvc_status kvc_validate_desc(const kvc_codec_desc *d) {
+  return desc_ok(d) ? KVC_OK : KVC_ERR_INVALID_ARG;
+}
+
+uint64_t kvc_tables_bytes(const kvc_codec_desc *dd) {
+  if (!desc_ok(dd)) return 0;
+  const uint64_t S = 2ull * dd->n_layers * dd->n_channels;
+  return kTablesHdr + S * kAnchorStride * 2 + (uint64_t)dd->n_levels * S * kDeltaStride * 2;
+}
+
+uint64_t kvc_profile_ws_bytes(const kvc_codec_desc *dd) {
+  if (!desc_ok(dd)) return 0;
+  const uint64_t S = 2ull * dd->n_layers * dd->n_channels;
+  const uint64_t counts = S * (kAnchorAlpha + (uint64_t)dd->n_levels * kDeltaStride) * 4;
+  return align256(counts) + align256(S * 8) + align256(2ull * dd->n_layers * 8);
+}
+
+kvc_status kvc_profile(const kvc_codec_desc *dd, const uint16_t *kv_fp16, uint32_t T,
+                       void *tables_out, void *ws, uint64_t ws_bytes, int32_t *dev_status,
+                       hipStream_t stream) {
+  if (!desc_ok(dd)) return KVC_ERR_INVALID_ARG;
+  if (!kv_fp16 || !aligned(kv_fp16, 2) || !tables_out || !aligned(tables_out, 16) || !ws ||
+      !aligned(ws, 256) || !dev_status || !aligned(dev_status, 4))
+    return KVC_ERR_INVALID_ARG;
+  if (T < 1) return KVC_ERR_SHAPE;
+  if (ws_bytes < kvc_profile_ws_bytes(dd)) return KVC_ERR_CAPACITY;
+  const Desc d = to_desc(dd);
+  const uint64_t S = n_streams(d);
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  const uint64_t counts_bytes = S * (kAnchorAlpha + (uint64_t)d.nlev * kDeltaStride) * 4;
+  uint32_t *counts = reinterpret_cast<uint32_t *>(base);
+  uint64_t *model_hash = reinterpret_cast<uint64_t *>(base + align256(counts_bytes));
+  uint64_t *row_hash = reinterpret_cast<uint64_t *>(base + align256(counts_bytes) + align256(S * 8));
+  hipError_t e = launch_reset_status(dev_status, stream);
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  e = launch_profile(d, kv_fp16, T, static_cast<uint8_t *>(tables_out), counts, model_hash,
+                     row_hash, dev_status, stream);
+  return hip_status(e);
+}
+
+uint64_t kvc_container_bound(const kvc_codec_desc *dd, uint32_t n_tokens) {
+  if (!desc_ok(dd)) return 0;
+  return container_bound_n(to_desc(dd), n_tokens);
+}
+
+uint64_t kvc_encode_bound(const kvc_codec_desc *dd, uint32_t T) {
+  if (!desc_ok(dd)) return 0;
+  const Desc d = to_desc(dd);
+  uint64_t total = 0;
+  for (uint64_t t0 = 0; t0 < T; t0 += d.chunk)
+    total += container_bound_n(d, (uint32_t)std::min<uint64_t>(d.chunk, T - t0));
+  return total;
+}
+
+uint64_t kvc_encode_ws_bytes(const kvc_codec_desc *dd, uint32_t T) {
+  if (!desc_ok(dd)) return 0;
+  const Desc d = to_desc(dd);
+  const uint32_t K = (uint32_t)((T + (uint64_t)d.chunk - 1) / d.chunk);
+  return ws_layout(d, K, true).total;
+}
+
+kvc_status kvc_encode(const kvc_codec_desc *dd, const void *tables, const uint16_t *kv_fp16,
+                      uint32_t T, const uint8_t *chunk_levels, uint8_t *out, uint64_t out_cap,
+                      uint64_t *chunk_offsets_out, void *ws, uint64_t ws_bytes,
+                      int32_t *dev_status, hipStream_t stream) {
+  if (!desc_ok(dd)) return KVC_ERR_INVALID_ARG;
+  const Desc d = to_desc(dd);
+  if (!tables || !aligned(tables, 16) || !kv_fp16 || !aligned(kv_fp16, 2) || !chunk_levels ||
+      !out || !aligned(out, 4) || !chunk_offsets_out || !aligned(chunk_offsets_out, 8) || !ws ||
+      !aligned(ws, 256) || !dev_status || !aligned(dev_status, 4))
+    return KVC_ERR_INVALID_ARG;
+  if (T < 1) return KVC_ERR_SHAPE;
+  const uint64_t K64 = (T + (uint64_t)d.chunk - 1) / d.chunk;
+  if (K64 > 65535) return KVC_ERR_SHAPE;
+  const uint32_t K = (uint32_t)K64;
+  const uint64_t S = n_streams(d);
+  // every stream offset inside a chunk's payload is a u32
+  if (S * pad4(4ull + 2ull * d.chunk) > 0xFFFFFFFFull) return KVC_ERR_SHAPE;
+  const WsLayout w = ws_layout(d, K, true);
+  if (ws_bytes < w.total) return KVC_ERR_CAPACITY;
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  std::vector<ChunkInfo> info(K);
+  for (uint32_t k = 0; k < K; ++k) {
+    if (chunk_levels[k] >= d.nlev) return KVC_ERR_INVALID_ARG;
+    const uint64_t t0 = (uint64_t)k * d.chunk;
+    info[k].cont = nullptr;
+    info[k].records = base + w.records + (uint64_t)k * S * kRecBytes;
+    info[k].cont_bytes = 0;
+    info[k].first_token = (uint32_t)t0;
+    info[k].n_tokens = (uint32_t)std::min<uint64_t>(d.chunk, T - t0);
+    info[k].level = chunk_levels[k];
+    info[k].pad0 = 0;
+    info[k].pad1 = 0;
+  }
+  hipError_t e = launch_reset_status(dev_status, stream);
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  ChunkInfo *dch = reinterpret_cast<ChunkInfo *>(base + w.chunks);
+  e = launch_load_chunks(info.data(), K, dch, stream);
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  e = launch_encode(d, static_cast<const uint8_t *>(tables), kv_fp16, T, dch, K,
+                    base + w.records, reinterpret_cast<uint64_t *>(base + w.rows), base + w.hdr,
+                    reinterpret_cast<uint32_t *>(base + w.offsets), base + w.valid,
+                    reinterpret_cast<uint64_t *>(base + w.payload),
+                    reinterpret_cast<uint64_t *>(base + w.chunk_off),
+                    reinterpret_cast<uint32_t *>(base + w.fits), out, out_cap, chunk_offsets_out,
+                    dev_status, stream);
+  return hip_status(e);
+}
+
+uint64_t kvc_decode_ws_bytes(const kvc_codec_desc *dd, uint32_t n_chunks) {
+  if (!desc_ok(dd)) return 0;
+  return ws_layout(to_desc(dd), n_chunks, false).total;
+}
+
+kvc_status kvc_decode(const kvc_codec_desc *d, const void *tables, const kvc_chunk_ref *chunks,
+                      uint32_t n_chunks, uint16_t *kv_out, uint32_t T_total, void *ws,
+                      uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream) {
+  return decode_common(d, tables, chunks, n_chunks, kv_out, T_total, ws, ws_bytes, dev_status,
+                       stream, 0, nullptr);
+}
+
+kvc_status kvc_decode_symbols(const kvc_codec_desc *d, const void *tables,
+                              const kvc_chunk_ref *chunks, uint32_t n_chunks, uint8_t *sym_out,
+                              uint32_t T_total, void *ws, uint64_t ws_bytes, int32_t *dev_status,
+                              hipStream_t stream) {
+  return decode_common(d, tables, chunks, n_chunks, sym_out, T_total, ws, ws_bytes, dev_status,
+                       stream, 1, nullptr);
+}
+
+kvc_status kvc_decode_index(const kvc_codec_desc *d, const void *tables,
+                            const kvc_chunk_ref *chunks, uint32_t n_chunks, uint32_t *offsets_out,
+                            void *ws, uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream) {
+  return decode_common(d, tables, chunks, n_chunks, nullptr, 0, ws, ws_bytes, dev_status, stream,
+                       2, offsets_out);
+}
+
+}  // extern "C"

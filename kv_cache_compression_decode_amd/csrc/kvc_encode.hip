@@ -1,0 +1,342 @@
+// Encode: binary16 KV [L][2][T][C] -> one container per chunk.
+//
+// CacheGen page, 核心方法: chunks of ~1.5K tokens coded independently;
+// change-based encoding (10-token groups, 8-bit anchor, deltas to the
+// anchor); layer-wise delta quantization (coarser for deeper thirds);
+// arithmetic coding with per channel-layer models.
+//
+// Kernels (one wavefront per (chunk, row, 64-channel block); lane = channel,
+// so every token's 64 inputs are one coalesced 128-byte load):
+//   k_encode_stats : per stream lo / sa / dl and the exact coded length
+//                    (the length depends only on the range evolution, so no
+//                    bytes are produced); records go to the workspace;
+//   (index kernels): per-stream payload offsets from those lengths;
+//   k_encode_layout: container start offsets, capacity check;
+//   k_encode_emit  : quantize and range-encode into the final position, with
+//                    the carry resolved by holding back the last byte that
+//                    a carry can still reach (plus the run of 0xFF after it);
+//   k_encode_header: the 64-byte headers.
+#include "kvc_internal.h"
+
+namespace kvc {
+
+namespace {
+
+__device__ inline void stage_tables(const Desc &d, const uint8_t *tables, uint32_t m0,
+                                    uint32_t nv, uint32_t level, uint16_t *sA, uint16_t *sD,
+                                    uint32_t lane) {
+  const uint32_t S = n_streams(d);
+  const uint4 *srcA =
+      reinterpret_cast<const uint4 *>(tables + kTablesHdr + (uint64_t)m0 * kAnchorStride * 2);
+  uint4 *dstA = reinterpret_cast<uint4 *>(sA);
+  const uint32_t nA = nv * (kAnchorStride * 2 / 16);
+  for (uint32_t i = lane; i < nA; i += kWave) dstA[i] = srcA[i];
+  const uint64_t delta_off = kTablesHdr + (uint64_t)S * kAnchorStride * 2;
+  const uint4 *srcD = reinterpret_cast<const uint4 *>(
+      tables + delta_off + ((uint64_t)level * S + m0) * kDeltaStride * 2);
+  uint4 *dstD = reinterpret_cast<uint4 *>(sD);
+  const uint32_t nD = nv * (kDeltaStride * 2 / 16);
+  for (uint32_t i = lane; i < nD; i += kWave) dstD[i] = srcD[i];
+}
+
+// Little-endian byte sink into 4-byte words, bounded by `cap` bytes.
+struct ByteSink {
+  uint32_t *wp;
+  uint32_t acc, nacc, count, cap;
+  bool overflow;
+  __device__ inline void put(uint32_t b) {
+    if (count >= cap) {
+      overflow = true;
+      return;
+    }
+    acc |= (b & 0xFFu) << (8 * nacc);
+    ++count;
+    if (++nacc == 4) {
+      *wp++ = acc;
+      acc = 0;
+      nacc = 0;
+    }
+  }
+  __device__ inline void flush() {
+    if (nacc) *wp = acc;  // the rest of the word is zero padding
+  }
+};
+
+// Range encoder with the carry applied through a held-back byte.
+struct RangeEncoder {
+  uint64_t low;  // up to 33 bits between shifts
+  uint32_t range;
+  uint32_t cache;
+  uint32_t nff;  // 0xFF bytes pending after `cache`
+  bool have_cache;
+  bool bad;
+
+  __device__ inline void shift_low(ByteSink &out) {
+    const uint32_t top = (uint32_t)(low >> 24);  // 9 bits: carry in bit 8
+    if (top != 0xFFu) {
+      const uint32_t carry = top >> 8;
+      if (have_cache) {
+        out.put(cache + carry);
+        for (; nff; --nff) out.put(0xFFu + carry);
+      } else if (carry) {
+        bad = true;  // a carry past the first byte cannot happen
+      }
+      cache = top & 0xFFu;
+      have_cache = true;
+    } else if (!have_cache) {
+      cache = 0xFFu;
+      have_cache = true;
+    } else {
+      ++nff;
+    }
+    low = (low & 0x00FFFFFFull) << 8;
+  }
+
+  __device__ inline void encode(uint32_t cum, uint32_t f, ByteSink &out) {
+    const uint32_t r = range >> kPrec;
+    low += (uint64_t)r * cum;
+    range = r * f;
+    while (range < (1u << 24)) {
+      shift_low(out);
+      range <<= 8;
+    }
+  }
+
+  __device__ inline void finish(ByteSink &out) {
+    for (int i = 0; i < 4; ++i) shift_low(out);
+    if (have_cache) {
+      out.put(cache);
+      for (; nff; --nff) out.put(0xFFu);
+    }
+  }
+};
+
+}  // namespace
+
+// Statistics and exact coded length of every stream.
+__global__ __launch_bounds__(64) void k_encode_stats(Desc d, const ChunkInfo *__restrict__ ci,
+                                                     const uint8_t *__restrict__ tables,
+                                                     const uint16_t *__restrict__ kv, uint32_t T,
+                                                     uint8_t *__restrict__ records,
+                                                     int32_t *status) {
+  const uint32_t cb = blockIdx.x, row = blockIdx.y, k = blockIdx.z;
+  __shared__ uint16_t sA[kWave * kAnchorStride];
+  __shared__ uint16_t sD[kWave * kDeltaStride];
+  const uint32_t lane = threadIdx.x;
+  const uint32_t S = n_streams(d);
+  const uint32_t c0 = cb * kWave;
+  const uint32_t nv = d.C - c0 < kWave ? d.C - c0 : kWave;
+  const uint32_t m0 = row * d.C + c0;
+  const ChunkInfo c = ci[k];
+  const uint32_t level = c.level;
+  const uint32_t b = d.bits[level][third_of(row >> 1, d.L)];
+  const int32_t M = (1 << (b - 1)) - 1;
+  stage_tables(d, tables, m0, nv, level, sA, sD, lane);
+  __syncthreads();
+  if (lane >= nv) return;
+  const uint32_t m = m0 + lane;
+  const uint16_t *ta = sA + lane * kAnchorStride;
+  const uint16_t *td = sD + lane * kDeltaStride;
+
+  const uint64_t ld = d.C;
+  const uint16_t *x = kv + ((uint64_t)row * T + c.first_token) * ld + c0 + lane;
+  const uint32_t n = c.n_tokens;
+  float lo, sa, maxabs;
+  if (!stream_stats(x, ld, n, d.G, lo, sa, maxabs)) set_status(status, KVC_ERR_NONFINITE);
+  const float dl = maxabs / (float)M;
+
+  // coded length = 4 + number of renormalisation shifts
+  uint32_t range = 0xFFFFFFFFu;
+  uint32_t shifts = 0;
+  float ahat = 0.0f;
+  uint32_t g = 0;
+  for (uint32_t j = 0; j < n; ++j) {
+    const float v = h2f(x[(uint64_t)j * ld]);
+    uint32_t f;
+    if (g == 0) {
+      const uint32_t qa = quant_anchor(v, lo, sa);
+      ahat = __builtin_fmaf((float)qa, sa, lo);
+      f = (uint32_t)ta[qa + 1] - ta[qa];
+    } else {
+      const uint32_t s = (uint32_t)(quant_delta(v - ahat, dl, M) + M);
+      f = (uint32_t)td[s + 1] - td[s];
+    }
+    g = g + 1 == d.G ? 0 : g + 1;
+    if (f == 0 || f > kTot) {  // damaged tables
+      set_status(status, KVC_ERR_CORRUPT_STREAM);
+      f = 1;
+    }
+    range = (range >> kPrec) * f;
+    while (range < (1u << 24)) {
+      range <<= 8;
+      ++shifts;
+    }
+  }
+  uint32_t *rec = reinterpret_cast<uint32_t *>(records + ((uint64_t)k * S + m) * kRecBytes);
+  rec[0] = __builtin_bit_cast(uint32_t, lo);
+  rec[1] = __builtin_bit_cast(uint32_t, sa);
+  rec[2] = __builtin_bit_cast(uint32_t, dl);
+  rec[3] = 4u + shifts;
+}
+
+// Container start offsets (one thread; chunk counts are small).
+__global__ void k_encode_layout(Desc d, uint32_t n_chunks, const uint64_t *__restrict__ payload,
+                                uint64_t *__restrict__ chunk_off_ws,
+                                uint64_t *__restrict__ chunk_off_out, uint64_t out_cap,
+                                uint32_t *__restrict__ fits, int32_t *status) {
+  if (threadIdx.x != 0) return;
+  const uint64_t fixed = (uint64_t)kHdrBytes + (uint64_t)kRecBytes * n_streams(d);
+  uint64_t acc = 0;
+  for (uint32_t k = 0; k < n_chunks; ++k) {
+    chunk_off_ws[k] = acc;
+    chunk_off_out[k] = acc;
+    acc += fixed + payload[k];
+  }
+  chunk_off_ws[n_chunks] = acc;
+  chunk_off_out[n_chunks] = acc;
+  bool ok = acc <= out_cap;
+  for (uint32_t k = 0; k < n_chunks; ++k) ok = ok && payload[k] <= 0xFFFFFFFFull;
+  *fits = ok ? 1u : 0u;
+  if (!ok) set_status(status, KVC_ERR_CAPACITY);
+}
+
+__global__ __launch_bounds__(64) void k_encode_emit(
+    Desc d, const ChunkInfo *__restrict__ ci, const uint8_t *__restrict__ tables,
+    const uint16_t *__restrict__ kv, uint32_t T, const uint8_t *__restrict__ records,
+    const uint32_t *__restrict__ offsets, const uint64_t *__restrict__ chunk_off,
+    const uint32_t *__restrict__ fits, uint8_t *__restrict__ out, int32_t *status) {
+  if (*fits == 0) return;
+  const uint32_t cb = blockIdx.x, row = blockIdx.y, k = blockIdx.z;
+  __shared__ uint16_t sA[kWave * kAnchorStride];
+  __shared__ uint16_t sD[kWave * kDeltaStride];
+  const uint32_t lane = threadIdx.x;
+  const uint32_t S = n_streams(d);
+  const uint32_t c0 = cb * kWave;
+  const uint32_t nv = d.C - c0 < kWave ? d.C - c0 : kWave;
+  const uint32_t m0 = row * d.C + c0;
+  const ChunkInfo c = ci[k];
+  const uint32_t level = c.level;
+  const uint32_t b = d.bits[level][third_of(row >> 1, d.L)];
+  const int32_t M = (1 << (b - 1)) - 1;
+  stage_tables(d, tables, m0, nv, level, sA, sD, lane);
+  __syncthreads();
+  if (lane >= nv) return;
+  const uint32_t m = m0 + lane;
+  const uint16_t *ta = sA + lane * kAnchorStride;
+  const uint16_t *td = sD + lane * kDeltaStride;
+
+  const uint32_t *rin = reinterpret_cast<const uint32_t *>(records + ((uint64_t)k * S + m) * kRecBytes);
+  const float lo = __builtin_bit_cast(float, rin[0]);
+  const float sa = __builtin_bit_cast(float, rin[1]);
+  const float dl = __builtin_bit_cast(float, rin[2]);
+  const uint32_t nbytes = rin[3];
+
+  uint8_t *cont = out + chunk_off[k];
+  uint32_t *rout = reinterpret_cast<uint32_t *>(cont + kHdrBytes + (uint64_t)m * kRecBytes);
+  rout[0] = rin[0];
+  rout[1] = rin[1];
+  rout[2] = rin[2];
+  rout[3] = nbytes;
+
+  ByteSink sink;
+  sink.wp = reinterpret_cast<uint32_t *>(cont + kHdrBytes + (uint64_t)kRecBytes * S +
+                                         offsets[(uint64_t)k * S + m]);
+  sink.acc = 0;
+  sink.nacc = 0;
+  sink.count = 0;
+  sink.cap = nbytes;
+  sink.overflow = false;
+  RangeEncoder enc;
+  enc.low = 0;
+  enc.range = 0xFFFFFFFFu;
+  enc.cache = 0;
+  enc.nff = 0;
+  enc.have_cache = false;
+  enc.bad = false;
+
+  const uint64_t ld = d.C;
+  const uint16_t *x = kv + ((uint64_t)row * T + c.first_token) * ld + c0 + lane;
+  const uint32_t n = c.n_tokens;
+  float ahat = 0.0f;
+  uint32_t g = 0;
+  for (uint32_t j = 0; j < n; ++j) {
+    const float v = h2f(x[(uint64_t)j * ld]);
+    uint32_t cs, f;
+    if (g == 0) {
+      const uint32_t qa = quant_anchor(v, lo, sa);
+      ahat = __builtin_fmaf((float)qa, sa, lo);
+      cs = ta[qa];
+      f = (uint32_t)ta[qa + 1] - cs;
+    } else {
+      const uint32_t s = (uint32_t)(quant_delta(v - ahat, dl, M) + M);
+      cs = td[s];
+      f = (uint32_t)td[s + 1] - cs;
+    }
+    g = g + 1 == d.G ? 0 : g + 1;
+    if (f == 0 || f > kTot) f = 1;  // damaged tables: already reported by the stats pass
+    enc.encode(cs, f, sink);
+  }
+  enc.finish(sink);
+  sink.flush();
+  if (enc.bad || sink.overflow || sink.count != nbytes) set_status(status, KVC_ERR_CORRUPT_STREAM);
+}
+
+__global__ void k_encode_header(Desc d, const ChunkInfo *__restrict__ ci, uint32_t n_chunks,
+                                const uint8_t *__restrict__ tables,
+                                const uint64_t *__restrict__ payload,
+                                const uint64_t *__restrict__ chunk_off,
+                                const uint32_t *__restrict__ fits, uint8_t *__restrict__ out) {
+  if (*fits == 0) return;
+  for (uint32_t k = threadIdx.x; k < n_chunks; k += blockDim.x) {
+    const ChunkInfo c = ci[k];
+    uint32_t *h = reinterpret_cast<uint32_t *>(out + chunk_off[k]);
+    const uint32_t level = c.level;
+    const uint64_t pid = *reinterpret_cast<const uint64_t *>(tables + 48);
+    h[0] = kContainerMagic;
+    h[1] = kFormatVersion | (level << 16) | (8u << 24);
+    h[2] = d.G | (kPrec << 16) | ((uint32_t)d.bits[level][0] << 24);
+    h[3] = (uint32_t)d.bits[level][1] | ((uint32_t)d.bits[level][2] << 8);
+    h[4] = d.L;
+    h[5] = d.C;
+    h[6] = c.n_tokens;
+    h[7] = c.first_token;
+    h[8] = (uint32_t)pid;
+    h[9] = (uint32_t)(pid >> 32);
+    h[10] = (uint32_t)payload[k];
+    h[11] = (uint32_t)(payload[k] >> 32);
+    h[12] = d.chunk;
+    h[13] = n_streams(d);
+    h[14] = 0;
+    h[15] = 0;
+  }
+}
+
+hipError_t launch_index(const Desc &d, const ChunkInfo *dev_chunks, uint32_t n_chunks,
+                        uint64_t *row_sums, uint8_t *hdr_ok, uint32_t *offsets, uint8_t *valid,
+                        uint64_t *payload, const uint8_t *tables, int check_header_flag,
+                        int32_t *status, hipStream_t stream);
+
+// Stream-ordered encode sequence; dev_chunks already holds the chunk table
+// (records pointing into the workspace record array).
+hipError_t launch_encode(const Desc &d, const uint8_t *tables, const uint16_t *kv, uint32_t T,
+                         const ChunkInfo *dev_chunks, uint32_t n_chunks, uint8_t *records,
+                         uint64_t *row_sums, uint8_t *hdr_ok, uint32_t *offsets, uint8_t *valid,
+                         uint64_t *payload, uint64_t *chunk_off_ws, uint32_t *fits, uint8_t *out,
+                         uint64_t out_cap, uint64_t *chunk_off_out, int32_t *status,
+                         hipStream_t stream) {
+  const dim3 grid((d.C + kWave - 1) / kWave, 2u * d.L, n_chunks);
+  hipLaunchKernelGGL(k_encode_stats, grid, dim3(kWave), 0, stream, d, dev_chunks, tables, kv, T,
+                     records, status);
+  hipError_t e = launch_index(d, dev_chunks, n_chunks, row_sums, hdr_ok, offsets, valid, payload,
+                              tables, 0, status, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_encode_layout, dim3(1), dim3(64), 0, stream, d, n_chunks, payload,
+                     chunk_off_ws, chunk_off_out, out_cap, fits, status);
+  hipLaunchKernelGGL(k_encode_emit, grid, dim3(kWave), 0, stream, d, dev_chunks, tables, kv, T,
+                     records, offsets, chunk_off_ws, fits, out, status);
+  hipLaunchKernelGGL(k_encode_header, dim3(1), dim3(256), 0, stream, d, dev_chunks, n_chunks,
+                     tables, payload, chunk_off_ws, fits, out);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

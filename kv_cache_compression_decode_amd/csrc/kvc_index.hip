@@ -1,0 +1,190 @@
+// Bitstream index: every (chunk, layer, K/V, channel) stream's payload
+// offset, as the exclusive prefix sum of the 4-byte-padded stream lengths in
+// (layer, K/V, channel) order, plus container header validation.
+//
+// Two launches over a (row = layer*2 + kv, chunk) grid:
+//   k_index_rows : per row, the sum of padded lengths (u64); the row-0 block
+//                  validates the chunk's header against the descriptor and
+//                  the tables' profile id;
+//   k_index_scan : per row, the base offset (sum of earlier rows) and a block
+//                  scan of the row's C lengths; the last row checks that the
+//                  total equals the header's payload size and that the
+//                  container size adds up, and marks the chunk decodable.
+// The decoder only touches chunks marked valid, so a corrupt container can
+// never send it outside the container.
+#include "kvc_internal.h"
+
+namespace kvc {
+
+__device__ inline uint32_t ld_u32(const uint8_t *p) {
+  // 4-byte aligned by construction (containers start 4-aligned, records are 16 B)
+  return *reinterpret_cast<const uint32_t *>(p);
+}
+__device__ inline uint64_t ld_u64(const uint8_t *p) {
+  return (uint64_t)ld_u32(p) | ((uint64_t)ld_u32(p + 4) << 32);
+}
+
+__global__ void k_load_chunks(ChunkBatch batch, ChunkInfo *dst, uint32_t first, uint32_t count) {
+  const uint32_t i = threadIdx.x;
+  if (i < count) dst[first + i] = batch.c[i];
+}
+
+__global__ void k_reset_status(int32_t *status) {
+  if (threadIdx.x == 0) *status = 0;
+}
+
+__device__ int32_t check_header(const Desc &d, const ChunkInfo &ci, const uint8_t *tables) {
+  const uint8_t *h = ci.cont;
+  if (ld_u32(h) != kContainerMagic) return KVC_ERR_CORRUPT_STREAM;
+  const uint32_t w1 = ld_u32(h + 4);  // version u16, level u8, anchor_bits u8
+  if ((w1 & 0xFFFFu) != kFormatVersion) return KVC_ERR_CORRUPT_STREAM;
+  const uint32_t level = (w1 >> 16) & 0xFFu;
+  if (level != ci.level || ((w1 >> 24) & 0xFFu) != 8u) return KVC_ERR_CORRUPT_STREAM;
+  const uint32_t w2 = ld_u32(h + 8);  // group u16, prec u8, bits[0] u8
+  const uint32_t w3 = ld_u32(h + 12); // bits[1] u8, bits[2] u8, reserved u16
+  if ((w2 & 0xFFFFu) != d.G || ((w2 >> 16) & 0xFFu) != kPrec) return KVC_ERR_CORRUPT_STREAM;
+  if (level >= d.nlev) return KVC_ERR_CORRUPT_STREAM;
+  if (((w2 >> 24) & 0xFFu) != d.bits[level][0] || (w3 & 0xFFu) != d.bits[level][1] ||
+      ((w3 >> 8) & 0xFFu) != d.bits[level][2])
+    return KVC_ERR_CORRUPT_STREAM;
+  if (ld_u32(h + 16) != d.L || ld_u32(h + 20) != d.C) return KVC_ERR_CORRUPT_STREAM;
+  if (ld_u32(h + 24) != ci.n_tokens) return KVC_ERR_CORRUPT_STREAM;
+  if (ld_u32(h + 48) != d.chunk || ld_u32(h + 52) != n_streams(d)) return KVC_ERR_CORRUPT_STREAM;
+  const uint64_t pid = ld_u64(h + 32);
+  const uint64_t tpid = *reinterpret_cast<const uint64_t *>(tables + 48);
+  if (pid != tpid) return KVC_ERR_PROFILE_MISMATCH;
+  return KVC_OK;
+}
+
+__global__ __launch_bounds__(256) void k_index_rows(Desc d, const ChunkInfo *__restrict__ ci,
+                                                    uint64_t *__restrict__ row_sums,
+                                                    uint8_t *__restrict__ hdr_ok,
+                                                    const uint8_t *__restrict__ tables,
+                                                    int check_header_flag, int32_t *status) {
+  const uint32_t row = blockIdx.x, k = blockIdx.y;
+  const uint32_t nrows = 2u * d.L;
+  const ChunkInfo c = ci[k];
+  const uint8_t *rec = c.records + (uint64_t)row * d.C * kRecBytes;
+  uint64_t acc = 0;
+  for (uint32_t ch = threadIdx.x; ch < d.C; ch += blockDim.x)
+    acc += pad4(ld_u32(rec + (uint64_t)ch * kRecBytes + 12));
+  // block reduction
+  __shared__ uint64_t red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (uint32_t s = blockDim.x / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    row_sums[(uint64_t)k * nrows + row] = red[0];
+    if (row == 0) {
+      int32_t st = KVC_OK;
+      if (check_header_flag) st = check_header(d, c, tables);
+      hdr_ok[k] = st == KVC_OK ? 1 : 0;
+      if (st != KVC_OK) set_status(status, st);
+    }
+  }
+}
+
+// Inclusive scan of one value per thread over a 256-thread block.
+__device__ inline uint64_t block_scan_incl(uint64_t v, uint64_t *tmp) {
+  const uint32_t t = threadIdx.x;
+  tmp[t] = v;
+  __syncthreads();
+  for (uint32_t off = 1; off < blockDim.x; off <<= 1) {
+    const uint64_t add = t >= off ? tmp[t - off] : 0;
+    __syncthreads();
+    tmp[t] += add;
+    __syncthreads();
+  }
+  const uint64_t r = tmp[t];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(256) void k_index_scan(Desc d, const ChunkInfo *__restrict__ ci,
+                                                    const uint64_t *__restrict__ row_sums,
+                                                    const uint8_t *__restrict__ hdr_ok,
+                                                    uint32_t *__restrict__ offsets,
+                                                    uint8_t *__restrict__ valid,
+                                                    uint64_t *__restrict__ payload,
+                                                    int check_header_flag, int32_t *status) {
+  const uint32_t row = blockIdx.x, k = blockIdx.y;
+  const uint32_t nrows = 2u * d.L;
+  const uint32_t S = n_streams(d);
+  const ChunkInfo c = ci[k];
+  __shared__ uint64_t tmp[256];
+  __shared__ uint64_t base_sh;
+  if (threadIdx.x == 0) {
+    uint64_t b = 0;
+    for (uint32_t r = 0; r < row; ++r) b += row_sums[(uint64_t)k * nrows + r];
+    base_sh = b;
+  }
+  __syncthreads();
+  uint64_t running = base_sh;
+  const uint8_t *rec = c.records + (uint64_t)row * d.C * kRecBytes;
+  uint32_t *out = offsets + (uint64_t)k * S + (uint64_t)row * d.C;
+  for (uint32_t t0 = 0; t0 < d.C; t0 += blockDim.x) {
+    const uint32_t ch = t0 + threadIdx.x;
+    const uint64_t v = ch < d.C ? pad4(ld_u32(rec + (uint64_t)ch * kRecBytes + 12)) : 0;
+    const uint64_t incl = block_scan_incl(v, tmp);
+    if (ch < d.C) out[ch] = (uint32_t)(running + incl - v);
+    // the tile's total is the last thread's inclusive value
+    const uint64_t tile_total = tmp[blockDim.x - 1];
+    __syncthreads();
+    running += tile_total;
+  }
+  if (row == nrows - 1 && threadIdx.x == 0) {
+    const uint64_t total = running;
+    payload[k] = total;
+    uint8_t ok = 1;
+    if (check_header_flag) {
+      ok = hdr_ok[k];
+      if (ok) {
+        const uint64_t hp = ld_u64(c.cont + 40);
+        const uint64_t want = (uint64_t)kHdrBytes + (uint64_t)kRecBytes * S + total;
+        // every stream offset must fit in 32 bits
+        if (hp != total || c.cont_bytes != want || total > 0xFFFFFFFFull) {
+          ok = 0;
+          set_status(status, KVC_ERR_CORRUPT_STREAM);
+        }
+      }
+    }
+    valid[k] = ok;
+  }
+}
+
+// Host launchers shared by decode and encode.  The chunk table travels as
+// kernel arguments, so the caller's host array may be released at once.
+hipError_t launch_load_chunks(const ChunkInfo *host_chunks, uint32_t n_chunks,
+                              ChunkInfo *dev_chunks, hipStream_t stream) {
+  for (uint32_t first = 0; first < n_chunks; first += kMaxChunksPerBatch) {
+    const uint32_t count =
+        n_chunks - first < kMaxChunksPerBatch ? n_chunks - first : kMaxChunksPerBatch;
+    ChunkBatch b;
+    for (uint32_t i = 0; i < count; ++i) b.c[i] = host_chunks[first + i];
+    hipLaunchKernelGGL(k_load_chunks, dim3(1), dim3(kMaxChunksPerBatch), 0, stream, b,
+                       dev_chunks, first, count);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_index(const Desc &d, const ChunkInfo *dev_chunks, uint32_t n_chunks,
+                        uint64_t *row_sums, uint8_t *hdr_ok, uint32_t *offsets, uint8_t *valid,
+                        uint64_t *payload, const uint8_t *tables, int check_header_flag,
+                        int32_t *status, hipStream_t stream) {
+  const dim3 grid(2u * d.L, n_chunks);
+  hipLaunchKernelGGL(k_index_rows, grid, dim3(256), 0, stream, d, dev_chunks, row_sums, hdr_ok,
+                     tables, check_header_flag, status);
+  hipLaunchKernelGGL(k_index_scan, grid, dim3(256), 0, stream, d, dev_chunks, row_sums, hdr_ok,
+                     offsets, valid, payload, check_header_flag, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_reset_status(int32_t *status, hipStream_t stream) {
+  hipLaunchKernelGGL(k_reset_status, dim3(1), dim3(64), 0, stream, status);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

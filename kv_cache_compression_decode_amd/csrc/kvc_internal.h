@@ -1,0 +1,159 @@
+// Internal definitions shared by the libkvc kernels and host code.
+//
+// Layouts (little-endian, all written and read only by this library and by
+// whoever follows the same published format):
+//   container  : 64-byte header, 2LC records of 16 bytes {f32 lo, f32 sa,
+//                f32 dl, u32 nbytes}, then the payload: the streams'
+//                bytes in (layer, K/V, channel) order, each zero-padded to a
+//                multiple of 4 bytes.
+//   tables blob: 128-byte header, anchor cumulative frequencies
+//                [2LC][ANCHOR_STRIDE] u16, delta cumulative frequencies
+//                [n_levels][2LC][DELTA_STRIDE] u16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+constexpr uint32_t kPrec = 15;
+constexpr uint32_t kTot = 1u << kPrec;
+constexpr uint32_t kAnchorAlpha = 256;
+constexpr uint32_t kAnchorStride = 264;  // u16 entries per anchor model: cum[0..256] + pad
+constexpr uint32_t kDeltaStride = 64;    // u16 entries per delta model: cum[0..A] + pad
+constexpr uint32_t kHdrBytes = 64;
+constexpr uint32_t kRecBytes = 16;
+constexpr uint32_t kTablesHdr = 128;
+constexpr uint32_t kWave = 64;
+constexpr uint32_t kMaxChunksPerBatch = 64;
+
+constexpr uint32_t kContainerMagic = 0x3143564Bu;  // "KVC1"
+constexpr uint32_t kTablesMagic = 0x5443564Bu;     // "KVCT"
+constexpr uint32_t kFormatVersion = 1;
+
+// Per-chunk description kept in the workspace.
+struct ChunkInfo {
+  const uint8_t *cont;     // container (decode) or nullptr (encode)
+  const uint8_t *records;  // the chunk's 2LC stream records
+  uint64_t cont_bytes;     // container size (decode)
+  uint32_t first_token;    // destination token (decode) / source token (encode)
+  uint32_t n_tokens;
+  uint32_t level;
+  uint32_t pad0;
+  uint64_t pad1;
+};
+static_assert(sizeof(ChunkInfo) == 48, "ChunkInfo layout");
+
+struct ChunkBatch {
+  ChunkInfo c[kMaxChunksPerBatch];
+};
+
+// Descriptor values used inside kernels.
+struct Desc {
+  uint32_t L, C, G, chunk, nlev;
+  uint8_t bits[4][3];
+};
+
+__host__ __device__ inline uint32_t third_of(uint32_t l, uint32_t L) { return (3u * l) / L; }
+__host__ __device__ inline uint32_t n_streams(const Desc &d) { return 2u * d.L * d.C; }
+__host__ __device__ inline uint64_t pad4(uint64_t v) { return (v + 3u) & ~uint64_t(3); }
+
+// 64-bit FNV-1a (Fowler / Noll / Vo), published offset basis and prime.
+constexpr uint64_t kFnvOffset = 0xcbf29ce484222325ull;
+constexpr uint64_t kFnvPrime = 0x100000001b3ull;
+__host__ __device__ inline uint64_t fnv_byte(uint64_t h, uint32_t b) {
+  return (h ^ (b & 0xFFu)) * kFnvPrime;
+}
+__host__ __device__ inline uint64_t fnv_u16(uint64_t h, uint32_t v) {
+  h = fnv_byte(h, v);
+  return fnv_byte(h, v >> 8);
+}
+__host__ __device__ inline uint64_t fnv_u32(uint64_t h, uint32_t v) {
+  h = fnv_u16(h, v);
+  return fnv_u16(h, v >> 16);
+}
+__host__ __device__ inline uint64_t fnv_u64(uint64_t h, uint64_t v) {
+  h = fnv_u32(h, (uint32_t)v);
+  return fnv_u32(h, (uint32_t)(v >> 32));
+}
+
+// Record the first device-side error of a call.
+__device__ inline void set_status(int32_t *st, int32_t code) {
+  atomicCAS(st, 0, code);
+}
+
+// binary16 bits -> binary32 (exact) and binary32 -> binary16 bits (round to
+// nearest even in the default rounding mode; subnormals kept).
+__device__ inline float h2f(uint16_t b) {
+  _Float16 h = __builtin_bit_cast(_Float16, b);
+  return (float)h;
+}
+__device__ inline uint16_t f2h(float f) {
+  _Float16 h = (_Float16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Byte-swap a 32-bit word: the payload is a big-endian byte string.
+__device__ inline uint32_t bswap32(uint32_t v) { return __builtin_bswap32(v); }
+
+__device__ inline bool is_finite(float v) { return __builtin_isfinite(v); }
+
+// --------------------------------------------------------------- quantizer
+// One stream = column c of x (stride `ld` elements), tokens 0..n-1.
+// Anchors: j % G == 0, 8-bit affine over [min, max] of the anchors
+// (first occurrence kept on ties: strict comparisons).
+__device__ inline uint32_t quant_anchor(float x, float lo, float sa) {
+  if (sa == 0.0f) return 0u;
+  float v = __builtin_rintf((x - lo) / sa);
+  int q = (int)v;
+  q = q < 0 ? 0 : q;
+  q = q > 255 ? 255 : q;
+  return (uint32_t)q;
+}
+
+__device__ inline int32_t quant_delta(float d, float dl, int32_t M) {
+  if (dl == 0.0f) return 0;
+  float v = __builtin_rintf(d / dl);
+  int q = (int)v;
+  q = q < -M ? -M : q;
+  q = q > M ? M : q;
+  return q;
+}
+
+// Stream statistics: lo, sa (anchor scale) and maxabs of the closed-loop
+// deltas.  Returns false if a value is not finite.
+__device__ inline bool stream_stats(const uint16_t *__restrict__ x, uint64_t ld, uint32_t n,
+                                    uint32_t G, float &lo_out, float &sa_out, float &maxabs_out) {
+  float lo = h2f(x[0]);
+  float hi = lo;
+  for (uint32_t j = G; j < n; j += G) {
+    const float v = h2f(x[(uint64_t)j * ld]);
+    if (v < lo) lo = v;
+    if (v > hi) hi = v;
+  }
+  const float sa = (hi - lo) / 255.0f;
+  bool finite = true;
+  float maxabs = 0.0f;
+  float ahat = 0.0f;
+  for (uint32_t j = 0; j < n; ++j) {
+    const float v = h2f(x[(uint64_t)j * ld]);
+    finite = finite && is_finite(v);
+    if (j % G == 0) {
+      ahat = __builtin_fmaf((float)quant_anchor(v, lo, sa), sa, lo);
+    } else {
+      const float a = __builtin_fabsf(v - ahat);
+      if (a > maxabs) maxabs = a;
+    }
+  }
+  lo_out = lo;
+  sa_out = sa;
+  maxabs_out = maxabs;
+  return finite;
+}
+
+// Workspace layout helpers.
+__host__ __device__ inline uint64_t align256(uint64_t v) { return (v + 255u) & ~uint64_t(255); }
+
+}  // namespace kvc

@@ -1,0 +1,121 @@
+"""CPU checks of the C ABI boundary: the library loads, exports every entry
+point declared in include/kvc.h, and its host-side queries and validation
+behave as documented (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kv_cache_compression_decode_amd as kvc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "kvc.h")).read()
+    return sorted(set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kvc.LIB_PATH):
+        from kv_cache_compression_decode_amd import build
+
+        build.build()
+    return kvc.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert set(names) == set(kvc.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_desc_layout_matches_header():
+    assert ctypes.sizeof(kvc.CodecDesc) == 40
+    assert kvc.CodecDesc.cdf_prec_bits.offset == 36
+    assert ctypes.sizeof(kvc.ChunkRef) == 32
+
+
+def test_validate_desc(L):
+    d = kvc.make_desc(4, 512)
+    assert L.kvc_validate_desc(ctypes.byref(d)) == 0
+    bad = kvc.make_desc(4, 512, delta_bits=((7, 5, 4),))
+    assert L.kvc_validate_desc(ctypes.byref(bad)) == kvc.ERR_INVALID_ARG
+    bad = kvc.make_desc(4, 512)
+    bad.anchor_bits = 6
+    assert L.kvc_validate_desc(ctypes.byref(bad)) == kvc.ERR_INVALID_ARG
+    bad = kvc.make_desc(0, 512)
+    assert L.kvc_validate_desc(ctypes.byref(bad)) == kvc.ERR_INVALID_ARG
+
+
+def test_size_queries(L):
+    d = kvc.make_desc(80, 1024, delta_bits=((6, 5, 4), (5, 4, 3), (4, 3, 2)))
+    S = 2 * 80 * 1024
+    assert L.kvc_tables_bytes(ctypes.byref(d)) == 128 + S * 528 + 3 * S * 128
+    assert L.kvc_container_bound(ctypes.byref(d), 1500) == 64 + 16 * S + S * 3004
+    assert L.kvc_encode_bound(ctypes.byref(d), 16000) == 10 * (64 + 16 * S + S * 3004) + (
+        64 + 16 * S + S * 2004)
+    assert L.kvc_decode_ws_bytes(ctypes.byref(d), 11) >= 11 * S * 4
+    assert L.kvc_encode_ws_bytes(ctypes.byref(d), 16000) >= 11 * S * 20
+
+
+def test_status_strings(L):
+    for code in range(0, -9, -1):
+        assert isinstance(L.kvc_status_str(code), bytes)
+    assert kvc.status_str(kvc.ERR_CORRUPT_STREAM) == "corrupt container or bitstream"
+
+
+def test_synchronous_argument_errors(L):
+    """Argument errors return before any launch (null pointers, bad levels)."""
+    d = kvc.make_desc(2, 64)
+    st = L.kvc_decode(ctypes.byref(d), None, None, 0, None, 0, None, 0, None, None)
+    assert st == kvc.ERR_INVALID_ARG
+    refs = (kvc.ChunkRef * 1)()
+    refs[0].container = 4096
+    refs[0].container_bytes = 64 + 16 * 256 + 16
+    refs[0].n_tokens = 10
+    refs[0].level = 3  # only one level
+    status = ctypes.c_int32()
+    st = L.kvc_decode(ctypes.byref(d), ctypes.c_void_p(256), refs, 1, ctypes.c_void_p(256), 100,
+                      ctypes.c_void_p(256), 1 << 20, ctypes.byref(status), None)
+    assert st == kvc.ERR_INVALID_ARG
+
+
+def test_overlapping_chunks_rejected(L):
+    d = kvc.make_desc(2, 64)
+    refs = (kvc.ChunkRef * 2)()
+    for i in range(2):
+        refs[i].container = 4096 * (i + 1)
+        refs[i].container_bytes = 64 + 16 * 256 + 4 * 256
+        refs[i].first_token = 5 * i  # [0,10) and [5,15) overlap
+        refs[i].n_tokens = 10
+        refs[i].level = 0
+    status = ctypes.c_int32()
+    st = L.kvc_decode(ctypes.byref(d), ctypes.c_void_p(256), refs, 2, ctypes.c_void_p(256), 100,
+                      ctypes.c_void_p(256), 1 << 20, ctypes.byref(status), None)
+    assert st == kvc.ERR_SHAPE
+
+
+def test_small_workspace_rejected(L):
+    d = kvc.make_desc(2, 64)
+    refs = (kvc.ChunkRef * 1)()
+    refs[0].container = 4096
+    refs[0].container_bytes = 64 + 16 * 256 + 4 * 256
+    refs[0].n_tokens = 10
+    status = ctypes.c_int32()
+    st = L.kvc_decode(ctypes.byref(d), ctypes.c_void_p(256), refs, 1, ctypes.c_void_p(256), 100,
+                      ctypes.c_void_p(256), 16, ctypes.byref(status), None)
+    assert st == kvc.ERR_CAPACITY
+
+
+def test_no_oracle_in_product():
+    """The product sources neither import nor link the oracle."""
+    pkg = os.path.join(ROOT, "kv_cache_compression_decode_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "import oracle" not in text and "kvc_oracle" not in text, f

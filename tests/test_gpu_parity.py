@@ -1,0 +1,251 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Every comparison is element by element and bit-exact: tables (integer
+frequencies and the profile id), containers (bytes), the bitstream index
+(offsets), decoded symbols and the decoded binary16 KV (0 ulp).  Inputs are
+the seeded synthetic KV of ``synth``; expected values come only from
+``oracle``.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_decode_amd as kvc
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+
+
+def _t(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+
+
+def _gpu_freqs(d: kvc.CodecDesc, tables: torch.Tensor):
+    """Frequencies from the device tables blob (layout of include/kvc.h)."""
+    S = d.n_streams
+    blob = tables.cpu().numpy()
+    a = blob[128:128 + S * 528].view(np.uint16).reshape(S, 264)
+    fA = np.diff(a[:, :257].astype(np.int64), axis=1)
+    dl = blob[128 + S * 528:].view(np.uint16).reshape(d.n_levels, S, 64)
+    return a, fA, dl
+
+
+class Case:
+    def __init__(self, cfg, levels, tables_from="gpu"):
+        self.cfg = cfg
+        self.levels = levels
+        self.kv = synth.make_kv(cfg)
+        self.kvp = synth.make_profile_kv(cfg)
+        self.od = oracle.desc_for(cfg)
+        self.otb = oracle.profile(self.od, self.kvp)
+        self.ocont = oracle.encode(self.od, self.otb, self.kv, levels)
+        self.oout = oracle.decode(self.od, self.otb, self.ocont, levels, cfg.n_tokens)
+        self.d = kvc.make_desc(cfg.n_layers, cfg.n_channels, cfg.delta_bits)
+        self.tables = kvc.profile(self.d, _t(self.kvp))
+        self.kv_dev = _t(self.kv)
+
+
+CASES = {
+    "tiny": lambda: Case(synth.CONFIGS[0], synth.CONFIGS[0].chunk_levels()),
+    # ragged channel count (96 = 64 + 32), 6 layers, partial last chunk of 700 tokens
+    "mixed": lambda: Case(synth.small_config(6, 96, 3700, n_levels=3, index=91), [0, 2, 1]),
+    # C = 70 (ragged block), 5 layers (thirds 2/1/2), last chunk of 11 tokens
+    "ragged": lambda: Case(synth.small_config(5, 70, 1511, n_levels=2, index=94), [1, 0]),
+    # per-channel rho, one token in the last chunk
+    "rho": lambda: Case(synth.small_config(3, 64, 3001, n_levels=1, index=95, rho_mode=1), [0, 0, 0]),
+}
+
+
+@pytest.fixture(scope="module", params=sorted(CASES))
+def case(request):
+    print(f"\n[gpu case] {request.param}", flush=True)
+    return CASES[request.param]()
+
+
+def test_profile_tables_bit_exact(case):
+    d = case.d
+    a, fA, dl = _gpu_freqs(d, case.tables)
+    np.testing.assert_array_equal(fA, case.otb.fA.astype(np.int64))
+    assert np.all(a[:, 257:] == 0xFFFF) and np.all(a[:, 0] == 0)
+    for lv in range(d.n_levels):
+        for m in range(d.n_streams):
+            l = m // (2 * d.n_channels)
+            A = (1 << case.od.bits(lv, l)) - 1
+            f = np.diff(dl[lv, m, :A + 1].astype(np.int64))
+            np.testing.assert_array_equal(f, case.otb.fD[lv, m, :A].astype(np.int64))
+            assert np.all(dl[lv, m, A + 1:] == 0xFFFF)
+    assert kvc.profile_id(case.tables) == case.otb.profile_id
+
+
+def test_encode_containers_bit_exact(case):
+    enc = kvc.encode(case.d, case.tables, case.kv_dev, case.levels)
+    assert enc.n_chunks == len(case.ocont)
+    for k in range(enc.n_chunks):
+        got = enc.container(k).cpu().numpy()
+        assert got.shape == case.ocont[k].shape, k
+        assert np.array_equal(got, case.ocont[k]), k
+
+
+def _upload_oracle(case):
+    """Oracle containers placed back to back in device memory."""
+    sizes = [len(c) for c in case.ocont]
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    blob = np.concatenate(case.ocont)
+    enc = kvc.Encoded(torch.from_numpy(blob).to(DEV), [int(x) for x in offs], list(case.levels),
+                      [min(1500, case.cfg.n_tokens - 1500 * k) for k in range(len(sizes))], 1500)
+    return enc
+
+
+def test_index_offsets_bit_exact(case):
+    enc = _upload_oracle(case)
+    offs = kvc.decode_index(case.d, case.tables, kvc.chunk_refs(enc)).cpu().numpy().view(np.uint32)
+    for k, c in enumerate(case.ocont):
+        np.testing.assert_array_equal(offs[k], oracle.stream_offsets(case.od, c))
+
+
+def test_decode_oracle_containers_bit_exact(case):
+    enc = _upload_oracle(case)
+    out = kvc.decode(case.d, case.tables, kvc.chunk_refs(enc), case.cfg.n_tokens)
+    got = out.cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, case.oout)
+
+
+def test_decode_symbols_bit_exact(case):
+    enc = _upload_oracle(case)
+    sym = kvc.decode_symbols(case.d, case.tables, kvc.chunk_refs(enc), case.cfg.n_tokens).cpu().numpy()
+    S = case.od.n_streams
+    C = case.cfg.n_channels
+    for k, c in enumerate(case.ocont):
+        n = min(1500, case.cfg.n_tokens - 1500 * k)
+        ids = np.arange(S)
+        _, osym = oracle.decode_streams(case.od, case.otb, c, ids, n)
+        g = sym[:, :, 1500 * k:1500 * k + n, :]  # [L][2][n][C]
+        g = g.transpose(0, 1, 3, 2).reshape(S, n)
+        np.testing.assert_array_equal(g.astype(np.int32), osym)
+
+
+def test_round_trip_gpu_encode_gpu_decode(case):
+    enc = kvc.encode(case.d, case.tables, case.kv_dev, case.levels)
+    out = kvc.decode(case.d, case.tables, kvc.chunk_refs(enc), case.cfg.n_tokens)
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint16), case.oout)
+
+
+def test_decode_is_deterministic(case):
+    enc = _upload_oracle(case)
+    a = kvc.decode(case.d, case.tables, kvc.chunk_refs(enc), case.cfg.n_tokens)
+    b = kvc.decode(case.d, case.tables, kvc.chunk_refs(enc), case.cfg.n_tokens)
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------- edge cases
+@pytest.fixture(scope="module")
+def mixed():
+    return CASES["mixed"]()
+
+
+def test_decode_subset_to_other_positions(mixed):
+    """Chunks may be decoded in any order to any disjoint token ranges; tokens
+    not covered are left untouched."""
+    enc = _upload_oracle(mixed)
+    T_total = 5000
+    refs = kvc.chunk_refs(enc, chunks=[2, 0], first_tokens=[100, 2000])
+    out = torch.full((6, 2, T_total, 96), 0x7BCD, dtype=torch.int16, device=DEV)
+    kvc.decode(mixed.d, mixed.tables, refs, T_total, out=out)
+    got = out.cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got[:, :, 100:800], mixed.oout[:, :, 3000:3700])
+    np.testing.assert_array_equal(got[:, :, 2000:3500], mixed.oout[:, :, 0:1500])
+    untouched = np.ones(T_total, bool)
+    untouched[100:800] = False
+    untouched[2000:3500] = False
+    assert np.all(got[:, :, untouched] == 0x7BCD)
+
+
+def test_decode_zero_chunks_is_a_no_op(mixed):
+    out = torch.full((6, 2, 10, 96), 7, dtype=torch.int16, device=DEV)
+    kvc.decode(mixed.d, mixed.tables, [], 10, out=out)
+    assert torch.all(out == 7)
+
+
+def test_profile_mismatch_is_reported(mixed):
+    enc = _upload_oracle(mixed)
+    bad_tables = mixed.tables.clone()
+    bad_tables[48] ^= 1  # flip one bit of the profile id
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.decode(mixed.d, bad_tables, kvc.chunk_refs(enc), mixed.cfg.n_tokens)
+    assert e.value.code == kvc.ERR_PROFILE_MISMATCH
+
+
+def test_corrupt_containers_are_reported(mixed):
+    S = mixed.od.n_streams
+    # bad magic
+    enc = _upload_oracle(mixed)
+    enc.blob[enc.offsets[1]] ^= 0xFF
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.decode(mixed.d, mixed.tables, kvc.chunk_refs(enc), mixed.cfg.n_tokens)
+    assert e.value.code == kvc.ERR_CORRUPT_STREAM
+    # two stream lengths changed by +-4: sums agree, both streams end wrongly
+    enc = _upload_oracle(mixed)
+    rec = enc.blob[64:64 + 16 * S].view(torch.int32).view(S, 4)
+    rec[10, 3] -= 4
+    rec[11, 3] += 4
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.decode(mixed.d, mixed.tables, kvc.chunk_refs(enc), mixed.cfg.n_tokens)
+    assert e.value.code == kvc.ERR_CORRUPT_STREAM
+    # payload size in the header disagrees with the stream lengths
+    enc = _upload_oracle(mixed)
+    enc.blob[40] ^= 4
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.decode(mixed.d, mixed.tables, kvc.chunk_refs(enc), mixed.cfg.n_tokens)
+    assert e.value.code == kvc.ERR_CORRUPT_STREAM
+
+
+def test_overlap_rejected_synchronously(mixed):
+    enc = _upload_oracle(mixed)
+    refs = kvc.chunk_refs(enc, chunks=[0, 1], first_tokens=[0, 1000])
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.decode(mixed.d, mixed.tables, refs, mixed.cfg.n_tokens)
+    assert e.value.code == kvc.ERR_SHAPE
+
+
+def test_encode_capacity_error(mixed):
+    wsp = kvc.EncodeWorkspace(mixed.d, mixed.cfg.n_tokens, DEV)
+    wsp.cap = 1000  # far too small
+    kvc.encode_async(mixed.d, mixed.tables, mixed.kv_dev, mixed.levels, wsp)
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.read_status(wsp.status, "encode")
+    assert e.value.code == kvc.ERR_CAPACITY
+
+
+def test_nonfinite_input_reported(mixed):
+    kv = mixed.kv.copy()
+    kv[1, 0, 17, 5] = 0x7C00  # +inf
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.encode(mixed.d, mixed.tables, _t(kv), mixed.levels)
+    assert e.value.code == kvc.ERR_NONFINITE
+
+
+def test_constant_and_extreme_channels_bit_exact():
+    """Constant channels (zero scales), tiny subnormal-range values and values
+    near the binary16 maximum, against the oracle."""
+    cfg = synth.small_config(3, 64, 1500, n_levels=1, index=96)
+    kv = synth.make_kv(cfg).copy()
+    kv[0, 0, :, 0] = np.float16(1.5).view(np.uint16)
+    kv[0, 1, :, 3] = 0
+    rng = np.random.default_rng(0)
+    kv[1, 0, :, 7] = (rng.integers(1, 40, 1500)).astype(np.uint16)  # subnormals
+    kv[2, 1, :, 9] = np.float16(60000.0).view(np.uint16) - rng.integers(0, 50, 1500).astype(np.uint16)
+    kv[2, 1, ::10, 9] = np.float16(-60000.0).view(np.uint16)
+    kvp = np.concatenate([kv, kv, kv], axis=2)
+    od = oracle.desc_for(cfg)
+    otb = oracle.profile(od, kvp)
+    oc = oracle.encode(od, otb, kv, [0])
+    oo = oracle.decode(od, otb, oc, [0], 1500)
+    d = kvc.make_desc(3, 64, cfg.delta_bits)
+    tables = kvc.profile(d, _t(kvp))
+    assert kvc.profile_id(tables) == otb.profile_id
+    enc = kvc.encode(d, tables, _t(kv), [0])
+    assert np.array_equal(enc.container(0).cpu().numpy(), oc[0])
+    out = kvc.decode(d, tables, kvc.chunk_refs(enc), 1500)
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint16), oo)
