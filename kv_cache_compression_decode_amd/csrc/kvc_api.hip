@@ -8,18 +8,18 @@
 namespace kvc {
 hipError_t launch_reset_status(int32_t *status, hipStream_t stream);
 hipError_t launch_load_chunks(const ChunkInfo *host_chunks, uint32_t n_chunks,
-                              ChunkInfo *dev_chunks, hipStream_t stream);
+                              ChunkInfo *dev_chunks, uint32_t *flags, hipStream_t stream);
 hipError_t launch_index(const Desc &d, const ChunkInfo *dev_chunks, uint32_t n_chunks,
-                        uint64_t *row_sums, uint8_t *hdr_ok, uint32_t *offsets, uint8_t *valid,
+                        uint64_t *row_sums, uint32_t *flags, uint32_t *offsets, uint8_t *valid,
                         uint64_t *payload, const uint8_t *tables, int check_header_flag,
                         int32_t *status, hipStream_t stream);
 hipError_t launch_decode(const Desc &d, const ChunkInfo *dev_chunks, uint32_t n_chunks,
-                         const uint8_t *valid, const uint32_t *offsets, const uint8_t *tables,
-                         void *out, uint32_t T_total, bool symbols, int32_t *status,
-                         hipStream_t stream);
+                         uint32_t level_mask, const uint8_t *valid, const uint32_t *offsets,
+                         const uint8_t *tables, void *out, uint32_t T_total, bool symbols,
+                         int32_t *status, hipStream_t stream);
 hipError_t launch_encode(const Desc &d, const uint8_t *tables, const uint16_t *kv, uint32_t T,
                          const ChunkInfo *dev_chunks, uint32_t n_chunks, uint8_t *records,
-                         uint64_t *row_sums, uint8_t *hdr_ok, uint32_t *offsets, uint8_t *valid,
+                         uint64_t *row_sums, uint32_t *flags, uint32_t *offsets, uint8_t *valid,
                          uint64_t *payload, uint64_t *chunk_off_ws, uint32_t *fits, uint8_t *out,
                          uint64_t out_cap, uint64_t *chunk_off_out, int32_t *status,
                          hipStream_t stream);
@@ -72,7 +72,7 @@ WsLayout ws_layout(const Desc &d, uint32_t K, bool encode) {
   w.chunks = 0;
   w.rows = align256(w.chunks + (uint64_t)K * sizeof(ChunkInfo));
   w.hdr = align256(w.rows + (uint64_t)K * 2 * d.L * 8);
-  w.valid = align256(w.hdr + K);
+  w.valid = align256(w.hdr + (uint64_t)K * 4);
   w.payload = align256(w.valid + K);
   w.offsets = align256(w.payload + (uint64_t)K * 8);
   uint64_t end = w.offsets + (uint64_t)K * S * 4;
@@ -115,6 +115,7 @@ kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc
   const uint64_t S = n_streams(d);
   std::vector<ChunkInfo> info(n_chunks);
   std::vector<std::pair<uint32_t, uint32_t>> ranges(n_chunks);
+  uint32_t level_mask = 0;
   for (uint32_t k = 0; k < n_chunks; ++k) {
     const kvc_chunk_ref &c = chunks[k];
     if (!c.container || !aligned(c.container, 4)) return KVC_ERR_INVALID_ARG;
@@ -131,6 +132,7 @@ kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc
     info[k].pad0 = 0;
     info[k].pad1 = 0;
     ranges[k] = {c.first_token, c.first_token + c.n_tokens};
+    level_mask |= 1u << c.level;
   }
   if (mode != 2) {
     std::sort(ranges.begin(), ranges.end());
@@ -142,14 +144,17 @@ kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc
   uint8_t *base = static_cast<uint8_t *>(ws);
   ChunkInfo *dch = reinterpret_cast<ChunkInfo *>(base + w.chunks);
   uint32_t *offs = mode == 2 ? offsets_out : reinterpret_cast<uint32_t *>(base + w.offsets);
-  e = launch_load_chunks(info.data(), n_chunks, dch, stream);
+  e = launch_load_chunks(info.data(), n_chunks, dch, reinterpret_cast<uint32_t *>(base + w.hdr),
+                         stream);
   if (e != hipSuccess) return KVC_ERR_HIP;
-  e = launch_index(d, dch, n_chunks, reinterpret_cast<uint64_t *>(base + w.rows), base + w.hdr,
+  e = launch_index(d, dch, n_chunks, reinterpret_cast<uint64_t *>(base + w.rows),
+                   reinterpret_cast<uint32_t *>(base + w.hdr),
                    offs, base + w.valid, reinterpret_cast<uint64_t *>(base + w.payload),
                    static_cast<const uint8_t *>(tables), 1, dev_status, stream);
   if (e != hipSuccess || mode == 2) return hip_status(e);
-  e = launch_decode(d, dch, n_chunks, base + w.valid, offs, static_cast<const uint8_t *>(tables),
-                    out, T_total, mode == 1, dev_status, stream);
+  e = launch_decode(d, dch, n_chunks, level_mask, base + w.valid, offs,
+                    static_cast<const uint8_t *>(tables), out, T_total, mode == 1, dev_status,
+                    stream);
   return hip_status(e);
 }
 
@@ -271,10 +276,11 @@ kvc_status kvc_encode(const kvc_codec_desc *dd, const void *tables, const uint16
   hipError_t e = launch_reset_status(dev_status, stream);
   if (e != hipSuccess) return KVC_ERR_HIP;
   ChunkInfo *dch = reinterpret_cast<ChunkInfo *>(base + w.chunks);
-  e = launch_load_chunks(info.data(), K, dch, stream);
+  e = launch_load_chunks(info.data(), K, dch, reinterpret_cast<uint32_t *>(base + w.hdr), stream);
   if (e != hipSuccess) return KVC_ERR_HIP;
   e = launch_encode(d, static_cast<const uint8_t *>(tables), kv_fp16, T, dch, K,
-                    base + w.records, reinterpret_cast<uint64_t *>(base + w.rows), base + w.hdr,
+                    base + w.records, reinterpret_cast<uint64_t *>(base + w.rows),
+                    reinterpret_cast<uint32_t *>(base + w.hdr),
                     reinterpret_cast<uint32_t *>(base + w.offsets), base + w.valid,
                     reinterpret_cast<uint64_t *>(base + w.payload),
                     reinterpret_cast<uint64_t *>(base + w.chunk_off),

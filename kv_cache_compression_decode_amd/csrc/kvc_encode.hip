@@ -312,7 +312,7 @@ __global__ void k_encode_header(Desc d, const ChunkInfo *__restrict__ ci, uint32
 }
 
 hipError_t launch_index(const Desc &d, const ChunkInfo *dev_chunks, uint32_t n_chunks,
-                        uint64_t *row_sums, uint8_t *hdr_ok, uint32_t *offsets, uint8_t *valid,
+                        uint64_t *row_sums, uint32_t *flags, uint32_t *offsets, uint8_t *valid,
                         uint64_t *payload, const uint8_t *tables, int check_header_flag,
                         int32_t *status, hipStream_t stream);
 
@@ -320,14 +320,14 @@ hipError_t launch_index(const Desc &d, const ChunkInfo *dev_chunks, uint32_t n_c
 // (records pointing into the workspace record array).
 hipError_t launch_encode(const Desc &d, const uint8_t *tables, const uint16_t *kv, uint32_t T,
                          const ChunkInfo *dev_chunks, uint32_t n_chunks, uint8_t *records,
-                         uint64_t *row_sums, uint8_t *hdr_ok, uint32_t *offsets, uint8_t *valid,
+                         uint64_t *row_sums, uint32_t *flags, uint32_t *offsets, uint8_t *valid,
                          uint64_t *payload, uint64_t *chunk_off_ws, uint32_t *fits, uint8_t *out,
                          uint64_t out_cap, uint64_t *chunk_off_out, int32_t *status,
                          hipStream_t stream) {
   const dim3 grid((d.C + kWave - 1) / kWave, 2u * d.L, n_chunks);
   hipLaunchKernelGGL(k_encode_stats, grid, dim3(kWave), 0, stream, d, dev_chunks, tables, kv, T,
                      records, status);
-  hipError_t e = launch_index(d, dev_chunks, n_chunks, row_sums, hdr_ok, offsets, valid, payload,
+  hipError_t e = launch_index(d, dev_chunks, n_chunks, row_sums, flags, offsets, valid, payload,
                               tables, 0, status, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_encode_layout, dim3(1), dim3(64), 0, stream, d, n_chunks, payload,

@@ -24,10 +24,18 @@ __device__ inline uint64_t ld_u64(const uint8_t *p) {
   return (uint64_t)ld_u32(p) | ((uint64_t)ld_u32(p + 4) << 32);
 }
 
-__global__ void k_load_chunks(ChunkBatch batch, ChunkInfo *dst, uint32_t first, uint32_t count) {
+__global__ void k_load_chunks(ChunkBatch batch, ChunkInfo *dst, uint32_t *flags, uint32_t first,
+                              uint32_t count) {
   const uint32_t i = threadIdx.x;
-  if (i < count) dst[first + i] = batch.c[i];
+  if (i < count) {
+    dst[first + i] = batch.c[i];
+    flags[first + i] = 0;
+  }
 }
+
+// Per-chunk problem flags, OR-ed by the row blocks.
+constexpr uint32_t kFlagHeader = 1u;  // header does not match descriptor / tables
+constexpr uint32_t kFlagShort = 2u;   // a stream shorter than its 4 flush bytes
 
 __global__ void k_reset_status(int32_t *status) {
   if (threadIdx.x == 0) *status = 0;
@@ -58,7 +66,7 @@ __device__ int32_t check_header(const Desc &d, const ChunkInfo &ci, const uint8_
 
 __global__ __launch_bounds__(256) void k_index_rows(Desc d, const ChunkInfo *__restrict__ ci,
                                                     uint64_t *__restrict__ row_sums,
-                                                    uint8_t *__restrict__ hdr_ok,
+                                                    uint32_t *__restrict__ flags,
                                                     const uint8_t *__restrict__ tables,
                                                     int check_header_flag, int32_t *status) {
   const uint32_t row = blockIdx.x, k = blockIdx.y;
@@ -66,8 +74,12 @@ __global__ __launch_bounds__(256) void k_index_rows(Desc d, const ChunkInfo *__r
   const ChunkInfo c = ci[k];
   const uint8_t *rec = c.records + (uint64_t)row * d.C * kRecBytes;
   uint64_t acc = 0;
-  for (uint32_t ch = threadIdx.x; ch < d.C; ch += blockDim.x)
-    acc += pad4(ld_u32(rec + (uint64_t)ch * kRecBytes + 12));
+  bool short_stream = false;
+  for (uint32_t ch = threadIdx.x; ch < d.C; ch += blockDim.x) {
+    const uint32_t nb = ld_u32(rec + (uint64_t)ch * kRecBytes + 12);
+    short_stream = short_stream || nb < 4u;
+    acc += pad4(nb);
+  }
   // block reduction
   __shared__ uint64_t red[256];
   red[threadIdx.x] = acc;
@@ -76,13 +88,18 @@ __global__ __launch_bounds__(256) void k_index_rows(Desc d, const ChunkInfo *__r
     if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
     __syncthreads();
   }
+  if (check_header_flag && __syncthreads_or(short_stream) && threadIdx.x == 0) {
+    atomicOr(&flags[k], kFlagShort);
+    set_status(status, KVC_ERR_CORRUPT_STREAM);
+  }
   if (threadIdx.x == 0) {
     row_sums[(uint64_t)k * nrows + row] = red[0];
-    if (row == 0) {
-      int32_t st = KVC_OK;
-      if (check_header_flag) st = check_header(d, c, tables);
-      hdr_ok[k] = st == KVC_OK ? 1 : 0;
-      if (st != KVC_OK) set_status(status, st);
+    if (row == 0 && check_header_flag) {
+      const int32_t st = check_header(d, c, tables);
+      if (st != KVC_OK) {
+        atomicOr(&flags[k], kFlagHeader);
+        set_status(status, st);
+      }
     }
   }
 }
@@ -105,7 +122,7 @@ __device__ inline uint64_t block_scan_incl(uint64_t v, uint64_t *tmp) {
 
 __global__ __launch_bounds__(256) void k_index_scan(Desc d, const ChunkInfo *__restrict__ ci,
                                                     const uint64_t *__restrict__ row_sums,
-                                                    const uint8_t *__restrict__ hdr_ok,
+                                                    const uint32_t *__restrict__ flags,
                                                     uint32_t *__restrict__ offsets,
                                                     uint8_t *__restrict__ valid,
                                                     uint64_t *__restrict__ payload,
@@ -140,7 +157,7 @@ __global__ __launch_bounds__(256) void k_index_scan(Desc d, const ChunkInfo *__r
     payload[k] = total;
     uint8_t ok = 1;
     if (check_header_flag) {
-      ok = hdr_ok[k];
+      ok = flags[k] == 0;
       if (ok) {
         const uint64_t hp = ld_u64(c.cont + 40);
         const uint64_t want = (uint64_t)kHdrBytes + (uint64_t)kRecBytes * S + total;
@@ -158,26 +175,26 @@ __global__ __launch_bounds__(256) void k_index_scan(Desc d, const ChunkInfo *__r
 // Host launchers shared by decode and encode.  The chunk table travels as
 // kernel arguments, so the caller's host array may be released at once.
 hipError_t launch_load_chunks(const ChunkInfo *host_chunks, uint32_t n_chunks,
-                              ChunkInfo *dev_chunks, hipStream_t stream) {
+                              ChunkInfo *dev_chunks, uint32_t *flags, hipStream_t stream) {
   for (uint32_t first = 0; first < n_chunks; first += kMaxChunksPerBatch) {
     const uint32_t count =
         n_chunks - first < kMaxChunksPerBatch ? n_chunks - first : kMaxChunksPerBatch;
     ChunkBatch b;
     for (uint32_t i = 0; i < count; ++i) b.c[i] = host_chunks[first + i];
     hipLaunchKernelGGL(k_load_chunks, dim3(1), dim3(kMaxChunksPerBatch), 0, stream, b,
-                       dev_chunks, first, count);
+                       dev_chunks, flags, first, count);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_index(const Desc &d, const ChunkInfo *dev_chunks, uint32_t n_chunks,
-                        uint64_t *row_sums, uint8_t *hdr_ok, uint32_t *offsets, uint8_t *valid,
+                        uint64_t *row_sums, uint32_t *flags, uint32_t *offsets, uint8_t *valid,
                         uint64_t *payload, const uint8_t *tables, int check_header_flag,
                         int32_t *status, hipStream_t stream) {
   const dim3 grid(2u * d.L, n_chunks);
-  hipLaunchKernelGGL(k_index_rows, grid, dim3(256), 0, stream, d, dev_chunks, row_sums, hdr_ok,
+  hipLaunchKernelGGL(k_index_rows, grid, dim3(256), 0, stream, d, dev_chunks, row_sums, flags,
                      tables, check_header_flag, status);
-  hipLaunchKernelGGL(k_index_scan, grid, dim3(256), 0, stream, d, dev_chunks, row_sums, hdr_ok,
+  hipLaunchKernelGGL(k_index_scan, grid, dim3(256), 0, stream, d, dev_chunks, row_sums, flags,
                      offsets, valid, payload, check_header_flag, status);
   return hipGetLastError();
 }

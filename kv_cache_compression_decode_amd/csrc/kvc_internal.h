@@ -91,6 +91,12 @@ __device__ inline float h2f(uint16_t b) {
   return (float)h;
 }
 __device__ inline uint16_t f2h(float f) {
+  // The value must be rounded to binary32 first.  Without this register
+  // barrier the backend folds an fma that feeds the conversion into one
+  // mixed-precision fma (v_fma_mixlo_f16) that rounds only once, straight to
+  // binary16, which differs from fp16(fp32(a*b+c)) in rare double-rounding
+  // cases.
+  __asm__("" : "+v"(f));
   _Float16 h = (_Float16)f;
   return __builtin_bit_cast(uint16_t, h);
 }

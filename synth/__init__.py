@@ -103,11 +103,14 @@ CONFIGS = {
 
 def small_config(n_layers: int, n_channels: int, n_tokens: int, n_levels: int = 3,
                  schedule: str = "mixed", index: int = 90, rho_mode: int = 0,
-                 outlier_frac: float = 0.01) -> Config:
-    """A reduced configuration with the same value model, for quick tests."""
+                 outlier_frac: float = 0.01, rho: Optional[float] = None) -> Config:
+    """A reduced configuration with the same value model, for quick tests
+    (`rho` overrides the constant AR(1) coefficient, e.g. 0 for white noise)."""
+    lo = 0.8 if rho_mode else (0.9 if rho is None else rho)
+    hi = 0.97 if rho_mode else lo
     return Config(index, f"small-{n_layers}L-{n_channels}ch-{n_tokens}", n_layers,
-                  n_channels, n_tokens, rho_mode, 0.8 if rho_mode else 0.9, 0.97 if rho_mode else 0.9,
-                  outlier_frac, 8.0, n_levels, schedule, "reduced test configuration")
+                  n_channels, n_tokens, rho_mode, lo, hi, outlier_frac, 8.0, n_levels, schedule,
+                  "reduced test configuration")
 
 
 # --------------------------------------------------------------------------

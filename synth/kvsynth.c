@@ -91,32 +91,37 @@ static inline void normals2(uint64_t seed, uint32_t w0, uint32_t w1,
   *n1 = rad * sin(ang);
 }
 
-/* binary64 -> binary16, round to nearest, ties to even (generator-local). */
+/* binary64 -> binary16, round to nearest, ties to even (generator-local),
+ * on the bit patterns. */
 static uint16_t to_half(double v) {
-  union {
-    double d;
-    uint64_t u;
-  } b = {v};
-  const uint16_t sign = (uint16_t)((b.u >> 48) & 0x8000u);
-  const double a = fabs(v);
-  if (a != a) return (uint16_t)(sign | 0x7E00u);
-  if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u);
-  if (a < 0x1p-14) {
-    /* subnormal range: units of 2^-24 */
-    const double q = nearbyint(a * 0x1p24); /* default mode: ties to even */
-    return (uint16_t)(sign | (uint16_t)q);
+  uint64_t u;
+  memcpy(&u, &v, 8);
+  const uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
+  const uint64_t a = u & 0x7FFFFFFFFFFFFFFFull;
+  if (a >= 0x7FF0000000000000ull) return (uint16_t)(sign | (a > 0x7FF0000000000000ull ? 0x7E00u : 0x7C00u));
+  const int e = (int)(a >> 52) - 1023;
+  if (e > 15) return (uint16_t)(sign | 0x7C00u);
+  const uint64_t m53 = (a & ((1ull << 52) - 1)) | (e > -1023 ? (1ull << 52) : 0);
+  if (e >= -14) {
+    uint64_t hm = m53 >> 42; /* 11 significant bits incl. the hidden one */
+    const uint64_t rest = m53 & ((1ull << 42) - 1), half = 1ull << 41;
+    if (rest > half || (rest == half && (hm & 1))) hm += 1;
+    int he = e + 15;
+    if (hm == 0x800) {
+      hm = 0x400;
+      he += 1;
+    }
+    if (he >= 31) return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | (uint16_t)(he << 10) | (uint16_t)(hm & 0x3FF));
   }
-  int e;
-  const double m = frexp(a, &e); /* a = m * 2^e, m in [0.5, 1) */
-  /* 11 significant bits: scale to [1024, 2048) */
-  double q = nearbyint(m * 2048.0);
-  if (q == 2048.0) {
-    q = 1024.0;
-    e += 1;
-  }
-  const int biased = e - 1 + 15;
-  if (biased >= 31) return (uint16_t)(sign | 0x7C00u);
-  return (uint16_t)(sign | (uint16_t)(biased << 10) | ((uint16_t)q - 1024u));
+  /* subnormal: value / 2^-24 = m53 * 2^(e - 52 + 24) = m53 >> rs */
+  const int rs = 28 - e;
+  if (rs >= 64) return sign;
+  const uint64_t q = m53 >> rs;
+  const uint64_t rem = m53 & ((1ull << rs) - 1), half = 1ull << (rs - 1);
+  uint64_t r = q;
+  if (rem > half || (rem == half && (q & 1))) r += 1;
+  return (uint16_t)(sign | (uint16_t)r);
 }
 
 /*

@@ -55,6 +55,11 @@ CASES = {
     "ragged": lambda: Case(synth.small_config(5, 70, 1511, n_levels=2, index=94), [1, 0]),
     # per-channel rho, one token in the last chunk
     "rho": lambda: Case(synth.small_config(3, 64, 3001, n_levels=1, index=95, rho_mode=1), [0, 0, 0]),
+    # white noise (no token locality): long, high-entropy streams
+    "noise": lambda: Case(synth.small_config(3, 128, 3000, n_levels=2, index=98, rho=0.0), [0, 1]),
+    # nine chunks in one call: two chunk groups per workgroup grid, mixed levels
+    "many": lambda: Case(synth.small_config(2, 64, 13000, n_levels=3, index=99),
+                         [0, 1, 2, 2, 1, 0, 0, 2, 1]),
 }
 
 
