@@ -13,10 +13,12 @@ hipError_t launch_index(const Desc &d, const ChunkInfo *dev_chunks, uint32_t n_c
                         uint64_t *row_sums, uint32_t *flags, uint32_t *offsets, uint8_t *valid,
                         uint64_t *payload, const uint8_t *tables, int check_header_flag,
                         int32_t *status, hipStream_t stream);
-hipError_t launch_decode(const Desc &d, const ChunkInfo *dev_chunks, uint32_t n_chunks,
-                         uint32_t level_mask, const uint8_t *valid, const uint32_t *offsets,
-                         const uint8_t *tables, void *out, uint32_t T_total, bool symbols,
-                         int32_t *status, hipStream_t stream);
+hipError_t launch_load_groups(const DecodeGroup *host_groups, uint32_t n_groups,
+                              DecodeGroup *dev_groups, hipStream_t stream);
+hipError_t launch_decode(const Desc &d, const ChunkInfo *dev_chunks, const DecodeGroup *groups,
+                         uint32_t n_groups, uint32_t max_levels_hint, const uint8_t *valid,
+                         const uint32_t *offsets, const uint8_t *tables, void *out,
+                         uint32_t T_total, bool symbols, int32_t *status, hipStream_t stream);
 hipError_t launch_encode(const Desc &d, const uint8_t *tables, const uint16_t *kv, uint32_t T,
                          const ChunkInfo *dev_chunks, uint32_t n_chunks, uint8_t *records,
                          uint64_t *row_sums, uint32_t *flags, uint32_t *offsets, uint8_t *valid,
@@ -63,14 +65,15 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Workspace layout shared by decode and encode (encode adds its tail).
 struct WsLayout {
-  uint64_t chunks, rows, hdr, valid, payload, offsets, records, chunk_off, fits, total;
+  uint64_t chunks, groups, rows, hdr, valid, payload, offsets, records, chunk_off, fits, total;
 };
 
 WsLayout ws_layout(const Desc &d, uint32_t K, bool encode) {
   const uint64_t S = n_streams(d);
   WsLayout w;
   w.chunks = 0;
-  w.rows = align256(w.chunks + (uint64_t)K * sizeof(ChunkInfo));
+  w.groups = align256(w.chunks + (uint64_t)K * sizeof(ChunkInfo));
+  w.rows = align256(w.groups + (uint64_t)K * sizeof(DecodeGroup));
   w.hdr = align256(w.rows + (uint64_t)K * 2 * d.L * 8);
   w.valid = align256(w.hdr + (uint64_t)K * 4);
   w.payload = align256(w.valid + K);
@@ -115,7 +118,6 @@ kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc
   const uint64_t S = n_streams(d);
   std::vector<ChunkInfo> info(n_chunks);
   std::vector<std::pair<uint32_t, uint32_t>> ranges(n_chunks);
-  uint32_t level_mask = 0;
   for (uint32_t k = 0; k < n_chunks; ++k) {
     const kvc_chunk_ref &c = chunks[k];
     if (!c.container || !aligned(c.container, 4)) return KVC_ERR_INVALID_ARG;
@@ -132,7 +134,6 @@ kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc
     info[k].pad0 = 0;
     info[k].pad1 = 0;
     ranges[k] = {c.first_token, c.first_token + c.n_tokens};
-    level_mask |= 1u << c.level;
   }
   if (mode != 2) {
     std::sort(ranges.begin(), ranges.end());
@@ -152,7 +153,31 @@ kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc
                    offs, base + w.valid, reinterpret_cast<uint64_t *>(base + w.payload),
                    static_cast<const uint8_t *>(tables), 1, dev_status, stream);
   if (e != hipSuccess || mode == 2) return hip_status(e);
-  e = launch_decode(d, dch, n_chunks, level_mask, base + w.valid, offs,
+  // decode groups: the chunks in call order, split into near-equal groups of
+  // at most kGroupChunks; a group's workgroups stage the models of every level
+  // the group uses
+  std::vector<DecodeGroup> groups;
+  uint32_t max_levels = 1;
+  {
+    const uint32_t ng = (n_chunks + kGroupChunks - 1) / kGroupChunks;
+    for (uint32_t gi = 0; gi < ng; ++gi) {
+      const uint32_t a = (uint32_t)((uint64_t)n_chunks * gi / ng);
+      const uint32_t b = (uint32_t)((uint64_t)n_chunks * (gi + 1) / ng);
+      DecodeGroup g{};
+      g.level = 0;
+      g.count = b - a;
+      for (uint32_t i = a; i < b; ++i) {
+        g.chunk[i - a] = i;
+        g.level |= 1u << chunks[i].level;
+      }
+      max_levels = std::max<uint32_t>(max_levels, (uint32_t)__builtin_popcount(g.level));
+      groups.push_back(g);
+    }
+  }
+  DecodeGroup *dgr = reinterpret_cast<DecodeGroup *>(base + w.groups);
+  e = launch_load_groups(groups.data(), (uint32_t)groups.size(), dgr, stream);
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  e = launch_decode(d, dch, dgr, (uint32_t)groups.size(), max_levels, base + w.valid, offs,
                     static_cast<const uint8_t *>(tables), out, T_total, mode == 1, dev_status,
                     stream);
   return hip_status(e);

@@ -187,6 +187,24 @@ hipError_t launch_load_chunks(const ChunkInfo *host_chunks, uint32_t n_chunks,
   return hipGetLastError();
 }
 
+__global__ void k_load_groups(GroupBatch batch, DecodeGroup *dst, uint32_t first, uint32_t count) {
+  const uint32_t i = threadIdx.x;
+  if (i < count) dst[first + i] = batch.g[i];
+}
+
+hipError_t launch_load_groups(const DecodeGroup *host_groups, uint32_t n_groups,
+                              DecodeGroup *dev_groups, hipStream_t stream) {
+  for (uint32_t first = 0; first < n_groups; first += kMaxChunksPerBatch) {
+    const uint32_t count =
+        n_groups - first < kMaxChunksPerBatch ? n_groups - first : kMaxChunksPerBatch;
+    GroupBatch b;
+    for (uint32_t i = 0; i < count; ++i) b.g[i] = host_groups[first + i];
+    hipLaunchKernelGGL(k_load_groups, dim3(1), dim3(kMaxChunksPerBatch), 0, stream, b,
+                       dev_groups, first, count);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_index(const Desc &d, const ChunkInfo *dev_chunks, uint32_t n_chunks,
                         uint64_t *row_sums, uint32_t *flags, uint32_t *offsets, uint8_t *valid,
                         uint64_t *payload, const uint8_t *tables, int check_header_flag,

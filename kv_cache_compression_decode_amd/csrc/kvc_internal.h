@@ -50,6 +50,20 @@ struct ChunkBatch {
   ChunkInfo c[kMaxChunksPerBatch];
 };
 
+// A group of up to kGroupChunks chunks of one compression level, decoded by
+// one workgroup per (row, channel block).
+constexpr uint32_t kGroupChunks = 8;
+struct DecodeGroup {
+  uint32_t level;  // bit l set: the group holds chunks of level l
+  uint32_t count;
+  uint32_t chunk[kGroupChunks];  // indices into the call's chunk table
+};
+static_assert(sizeof(DecodeGroup) == 40, "DecodeGroup layout");
+
+struct GroupBatch {
+  DecodeGroup g[kMaxChunksPerBatch];
+};
+
 // Descriptor values used inside kernels.
 struct Desc {
   uint32_t L, C, G, chunk, nlev;
