@@ -1,0 +1,133 @@
+"""GPU parity at the full workload sizes (configurations 1-4), through the C ABI.
+
+At these sizes the oracle checks what it can compute in seconds on the host:
+ * the profiled tables, completely (every frequency of every model, and the
+   profile id);
+ * sampled chunks (the first, the last - partial where the context is not a
+   multiple of 1,500 tokens - and one in the middle): the GPU containers are
+   byte-identical to the oracle's and the GPU-decoded binary16 KV equals the
+   oracle's decode of its own containers, element by element;
+and for every chunk, properties that hold at any size: container invariants
+(header fields, stream lengths summing to the payload) and the half-step
+reconstruction bound on every element, evaluated on the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_decode_amd as kvc
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+
+
+def _check_tables(d, tables, otb, od):
+    S = d.n_streams
+    blob = tables.cpu().numpy()
+    a = blob[128:128 + S * 528].view(np.uint16).reshape(S, 264)
+    np.testing.assert_array_equal(np.diff(a[:, :257].astype(np.int32), axis=1), otb.fA.astype(np.int32))
+    dl = blob[128 + S * 528:].view(np.uint16).reshape(d.n_levels, S, 64)
+    for lv in range(d.n_levels):
+        for third in range(3):
+            b = od.delta_bits[lv][third]
+            A = (1 << b) - 1
+            layers = [l for l in range(d.n_layers) if od.third(l) == third]
+            ms = np.concatenate([np.arange(2 * l * d.n_channels, 2 * (l + 1) * d.n_channels)
+                                 for l in layers])
+            got = np.diff(dl[lv, ms, :A + 1].astype(np.int32), axis=1)
+            np.testing.assert_array_equal(got, otb.fD[lv, ms, :A].astype(np.int32))
+    assert kvc.profile_id(tables) == otb.profile_id
+
+
+def _half_step_on_gpu(d, enc, kv_dev, out, cfg):
+    """|x - xhat| <= step/2 + step 2^-14 + ulp16(xhat)/2 + 4 ulp32(max(|x|, |a|+step))
+    for every element, step = sa (anchor tokens) or dl (delta tokens).  The
+    step 2^-14 term covers the binary32 quotient x/step rounding across a
+    half-integer (at most qmax 2^-23 step with qmax <= 255)."""
+    S = d.n_streams
+    L, C = cfg.n_layers, cfg.n_channels
+    for k in range(enc.n_chunks):
+        c = enc.container(k)
+        n = enc.n_tokens[k]
+        t0 = 1500 * k
+        rec = c[64:64 + 16 * S].view(torch.float32).view(S, 4)
+        sa = rec[:, 1].reshape(L, 2, 1, C)
+        dl = rec[:, 2].reshape(L, 2, 1, C)
+        x = kv_dev[:, :, t0:t0 + n].view(torch.float16).float()
+        y = out[:, :, t0:t0 + n].view(torch.float16).float()
+        assert torch.isfinite(y).all()
+        is_anchor = (torch.arange(n, device=DEV) % 10 == 0).view(1, 1, n, 1)
+        step = torch.where(is_anchor, sa, dl)
+        # unit in the last place: binary16 (normal spacing 2^(e-11), subnormal
+        # 2^-24) and binary32 (2^(e-24)) with |v| = m 2^e, m in [0.5, 1)
+        _, e16 = torch.frexp(y.abs())
+        ulp16 = torch.clamp(torch.ldexp(torch.ones_like(y), e16 - 11), min=2.0 ** -24)
+        big = torch.maximum(x.abs(), x[:, :, ::10].abs().repeat_interleave(10, dim=2)[:, :, :n] + step)
+        _, e32 = torch.frexp(big)
+        ulp32 = torch.clamp(torch.ldexp(torch.ones_like(big), e32 - 24), min=2.0 ** -149)
+        bound = step / 2 + step * 2.0 ** -14 + ulp16 / 2 + 4 * ulp32
+        err = (x - y).abs()
+        bad = (err > bound)
+        assert not bad.any(), (k, int(bad.sum()), float((err - bound).max()))
+
+
+def _sample_chunks(cfg):
+    ks = {0, cfg.n_chunks - 1, cfg.n_chunks // 2}
+    return sorted(ks)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_full_size_config(idx):
+    cfg = synth.CONFIGS[idx]
+    print(f"\n[fullsize] config {idx} {cfg.name}: generating", flush=True)
+    p = synth.params(cfg)
+    kv = synth.make_kv(cfg, p=p)
+    kvp = synth.make_profile_kv(cfg, p=p)
+    levels = cfg.chunk_levels()
+    d = kvc.make_desc(cfg.n_layers, cfg.n_channels, cfg.delta_bits)
+    od = oracle.desc_for(cfg)
+
+    print("[fullsize] gpu profile / encode / decode", flush=True)
+    kv_dev = _t(kv)
+    tables = kvc.profile(d, _t(kvp))
+    enc = kvc.encode(d, tables, kv_dev, levels)
+    out = kvc.decode(d, tables, kvc.chunk_refs(enc), cfg.n_tokens)
+    torch.cuda.synchronize()
+
+    print("[fullsize] oracle profile", flush=True)
+    otb = oracle.profile(od, kvp)
+    del kvp
+    _check_tables(d, tables, otb, od)
+
+    print("[fullsize] container invariants", flush=True)
+    S = d.n_streams
+    for k in range(enc.n_chunks):
+        hdr = oracle.parse_header(enc.container(k)[:64].cpu().numpy())
+        assert hdr["magic"] == b"KVC1" and hdr["level"] == levels[k]
+        assert hdr["n_tokens"] == enc.n_tokens[k] and hdr["first_token"] == 1500 * k
+        assert hdr["profile_id"] == otb.profile_id
+        nb = enc.container(k)[64:64 + 16 * S].view(torch.int32).view(S, 4)[:, 3].long()
+        assert int(((nb + 3) // 4 * 4).sum()) == hdr["payload_bytes"]
+        assert enc.offsets[k + 1] - enc.offsets[k] == 64 + 16 * S + hdr["payload_bytes"]
+
+    print("[fullsize] half-step bound on every element", flush=True)
+    _half_step_on_gpu(d, enc, kv_dev, out, cfg)
+
+    for k in _sample_chunks(cfg):
+        print(f"[fullsize] oracle chunk {k} (level {levels[k]})", flush=True)
+        oc = oracle.encode_chunk(od, otb, kv, k, levels[k])
+        assert np.array_equal(enc.container(k).cpu().numpy(), oc), f"container {k}"
+        n = enc.n_tokens[k]
+        oo = np.zeros((cfg.n_layers, 2, n, cfg.n_channels), np.uint16)
+        oracle.decode_chunk_into(od, otb, oc, 0, n, levels[k], oo)
+        got = out[:, :, 1500 * k:1500 * k + n].cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(got, oo)
+    ratio = cfg.fp16_bytes() / enc.total_bytes()
+    print(f"[fullsize] config {idx}: bit-exact on sampled chunks, compression {ratio:.3f}", flush=True)

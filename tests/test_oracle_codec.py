@@ -72,8 +72,10 @@ def _side_info(d, cont_k):
 
 
 def _check_half_step(d, kv, out, cont, levels):
-    """|x - xhat| <= step/2 + ulp16(xhat)/2 + 4 ulp32(max(|x|, |ahat|)),
-    step = sa for anchors and dl for deltas, element by element."""
+    """|x - xhat| <= step/2 + step 2^-14 + ulp16(xhat)/2 + 4 ulp32(max(|x|, |ahat|)),
+    step = sa for anchors and dl for deltas, element by element.  The
+    step 2^-14 term covers the binary32 quotient (x - lo)/sa or d/dl rounding
+    across a half-integer (at most qmax 2^-23 step, qmax <= 255)."""
     x = kv.view(np.float16).astype(np.float64)
     y = out.view(np.float16).astype(np.float64)
     assert np.all(np.isfinite(y))
@@ -88,7 +90,7 @@ def _check_half_step(d, kv, out, cont, levels):
         step = np.where(is_anchor, sa[:, :, None, :], dl[:, :, None, :]).astype(np.float64)
         anchors = xs[:, :, ::d.group_tokens, :]
         amax = np.repeat(np.abs(anchors), d.group_tokens, axis=2)[:, :, :n, :] + 1.0 * step
-        bound = step / 2 + _f16_ulp(hb) / 2 + 4 * _f32_ulp(np.maximum(np.abs(xs), amax))
+        bound = step / 2 + step * 2.0 ** -14 + _f16_ulp(hb) / 2 + 4 * _f32_ulp(np.maximum(np.abs(xs), amax))
         err = np.abs(xs - ys)
         assert np.all(err <= bound), (k, np.max(err - bound))
 
