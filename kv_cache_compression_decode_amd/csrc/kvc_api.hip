@@ -16,9 +16,10 @@ hipError_t launch_index(const Desc &d, const ChunkInfo *dev_chunks, uint32_t n_c
 hipError_t launch_load_groups(const DecodeGroup *host_groups, uint32_t n_groups,
                               DecodeGroup *dev_groups, hipStream_t stream);
 hipError_t launch_decode(const Desc &d, const ChunkInfo *dev_chunks, const DecodeGroup *groups,
-                         uint32_t n_groups, uint32_t max_levels_hint, const uint8_t *valid,
+                         uint32_t n_groups, uint32_t levels, uint32_t waves, const uint8_t *valid,
                          const uint32_t *offsets, const uint8_t *tables, void *out,
                          uint32_t T_total, bool symbols, int32_t *status, hipStream_t stream);
+size_t decode_lds_bytes(uint32_t levels, uint32_t waves);
 hipError_t launch_encode(const Desc &d, const uint8_t *tables, const uint16_t *kv, uint32_t T,
                          const ChunkInfo *dev_chunks, uint32_t n_chunks, uint8_t *records,
                          uint64_t *row_sums, uint32_t *flags, uint32_t *offsets, uint8_t *valid,
@@ -125,6 +126,8 @@ kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc
     if (c.n_tokens < 1 || c.n_tokens > d.chunk) return KVC_ERR_SHAPE;
     if (mode != 2 && (uint64_t)c.first_token + c.n_tokens > T_total) return KVC_ERR_SHAPE;
     if (c.container_bytes < kHdrBytes + kRecBytes * S) return KVC_ERR_SHAPE;
+    // decode reads containers through 32-bit bounded buffer resources
+    if (c.container_bytes > 0xFFFFFFFFull) return KVC_ERR_SHAPE;
     info[k].cont = c.container;
     info[k].records = c.container + kHdrBytes;
     info[k].cont_bytes = c.container_bytes;
@@ -140,6 +143,40 @@ kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc
     for (uint32_t k = 1; k < n_chunks; ++k)
       if (ranges[k].first < ranges[k - 1].second) return KVC_ERR_SHAPE;
   }
+  // Decode groups (values / symbols): the chunk table is ordered by level so
+  // that the two chunks a wave decodes together mostly share an alphabet
+  // size, then split into near-equal groups of whole pairs, each decoded by
+  // one workgroup per (row, channel block) whose waves take at most
+  // kMaxRounds pairs each.  The index-only call keeps the caller's order.
+  std::vector<DecodeGroup> groups;
+  uint32_t levels = 1, waves = 1;
+  if (mode != 2 && n_chunks) {
+    std::stable_sort(info.begin(), info.end(),
+                     [](const ChunkInfo &a, const ChunkInfo &b) { return a.level < b.level; });
+    constexpr uint32_t kMaxRounds = 4;
+    uint32_t all_levels = 0;
+    for (const ChunkInfo &c : info) all_levels |= 1u << c.level;
+    const uint32_t lv_all = (uint32_t)__builtin_popcount(all_levels);
+    uint32_t wmax = 1;
+    for (uint32_t w = kDecodeMaxWaves; w >= 1; --w)
+      if (decode_lds_bytes(lv_all, w) <= kDecodeLdsBudget) {
+        wmax = w;
+        break;
+      }
+    const uint32_t pairs = (n_chunks + 1) / 2;
+    const uint32_t ng = (pairs + wmax * kMaxRounds - 1) / (wmax * kMaxRounds);
+    for (uint32_t gi = 0; gi < ng; ++gi) {
+      const uint32_t a = 2 * (uint32_t)((uint64_t)pairs * gi / ng);
+      const uint32_t b = std::min<uint32_t>(n_chunks, 2 * (uint32_t)((uint64_t)pairs * (gi + 1) / ng));
+      DecodeGroup g{};
+      g.start = a;
+      g.count = b - a;
+      for (uint32_t i = a; i < b; ++i) g.level |= 1u << info[i].level;
+      levels = std::max<uint32_t>(levels, (uint32_t)__builtin_popcount(g.level));
+      waves = std::max<uint32_t>(waves, std::min<uint32_t>(wmax, (g.count + 1) / 2));
+      groups.push_back(g);
+    }
+  }
   hipError_t e = launch_reset_status(dev_status, stream);
   if (e != hipSuccess || n_chunks == 0) return hip_status(e);
   uint8_t *base = static_cast<uint8_t *>(ws);
@@ -153,31 +190,10 @@ kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc
                    offs, base + w.valid, reinterpret_cast<uint64_t *>(base + w.payload),
                    static_cast<const uint8_t *>(tables), 1, dev_status, stream);
   if (e != hipSuccess || mode == 2) return hip_status(e);
-  // decode groups: the chunks in call order, split into near-equal groups of
-  // at most kGroupChunks; a group's workgroups stage the models of every level
-  // the group uses
-  std::vector<DecodeGroup> groups;
-  uint32_t max_levels = 1;
-  {
-    const uint32_t ng = (n_chunks + kGroupChunks - 1) / kGroupChunks;
-    for (uint32_t gi = 0; gi < ng; ++gi) {
-      const uint32_t a = (uint32_t)((uint64_t)n_chunks * gi / ng);
-      const uint32_t b = (uint32_t)((uint64_t)n_chunks * (gi + 1) / ng);
-      DecodeGroup g{};
-      g.level = 0;
-      g.count = b - a;
-      for (uint32_t i = a; i < b; ++i) {
-        g.chunk[i - a] = i;
-        g.level |= 1u << chunks[i].level;
-      }
-      max_levels = std::max<uint32_t>(max_levels, (uint32_t)__builtin_popcount(g.level));
-      groups.push_back(g);
-    }
-  }
   DecodeGroup *dgr = reinterpret_cast<DecodeGroup *>(base + w.groups);
   e = launch_load_groups(groups.data(), (uint32_t)groups.size(), dgr, stream);
   if (e != hipSuccess) return KVC_ERR_HIP;
-  e = launch_decode(d, dch, dgr, (uint32_t)groups.size(), max_levels, base + w.valid, offs,
+  e = launch_decode(d, dch, dgr, (uint32_t)groups.size(), levels, waves, base + w.valid, offs,
                     static_cast<const uint8_t *>(tables), out, T_total, mode == 1, dev_status,
                     stream);
   return hip_status(e);

@@ -50,15 +50,25 @@ struct ChunkBatch {
   ChunkInfo c[kMaxChunksPerBatch];
 };
 
-// A group of up to kGroupChunks chunks of one compression level, decoded by
-// one workgroup per (row, channel block).
-constexpr uint32_t kGroupChunks = 8;
+// A group of chunks decoded by one workgroup per (row, channel block): the
+// chunk table entries [start, start + count), which the host orders by level.
 struct DecodeGroup {
   uint32_t level;  // bit l set: the group holds chunks of level l
+  uint32_t start;
   uint32_t count;
-  uint32_t chunk[kGroupChunks];  // indices into the call's chunk table
+  uint32_t pad;
 };
-static_assert(sizeof(DecodeGroup) == 40, "DecodeGroup layout");
+static_assert(sizeof(DecodeGroup) == 16, "DecodeGroup layout");
+
+// Decode workgroups have at most this many waves; a wave takes the group's
+// chunks two at a time.
+constexpr uint32_t kDecodeMaxWaves = 8;
+// LDS per decode workgroup that still lets two of them share a CU.
+constexpr uint32_t kDecodeLdsBudget = 80u * 1024u;
+
+// Fourth dword of a raw buffer resource on gfx9-family GPUs (32-bit data
+// format, no swizzle): loads are bounds-checked against num_records bytes.
+constexpr int32_t kBufferWord3 = 0x00020000;
 
 struct GroupBatch {
   DecodeGroup g[kMaxChunksPerBatch];
