@@ -20,18 +20,21 @@
 //    and the search depth are wave-uniform, and the 64 results of a token are
 //    64 consecutive channels: one coalesced 128-byte store per stream,
 //    addressed from a wave-uniform base;
-//  * symbols are found by binary search of the cumulative tables: 8 steps
-//    for anchors, b steps for a b-bit delta alphabet, the two streams'
-//    probes interleaved;
+//  * a symbol is the largest k with r * cum[k] <= code, found by binary
+//    search with one 24-bit multiply per probe (no division): 8 steps for
+//    anchors, b steps for a b-bit delta alphabet, the two streams' probes
+//    interleaved;
+//  * the models are staged row-interleaved (entry i of lane l at u16 index
+//    64 i + l), so a probe is a constant offset from the lane's current row,
+//    the symbol index is a shift of the address, and only the two lanes of a
+//    dword can collide on an LDS bank;
 //  * stream bytes are staged per lane in a 16-byte LDS ring fed in 8-byte
-//    blocks: at every group boundary a lane whose ring has room stores the
-//    block it loaded earlier and issues the load of the next one, so
-//    global-memory latency is off the per-symbol path; a rare slow path
-//    refills a ring that runs low.  Loads go through a buffer resource
+//    blocks: a lane stores the block it loaded earlier only when its ring
+//    runs low (at most 8 bytes left at a group's anchor, fewer than 2 before
+//    any other token) and then issues the load of the next one, so a load has
+//    about a group of tokens to arrive.  Loads go through a buffer resource
 //    bounded by the container size, so the block after a stream's last byte
 //    may be loaded unconditionally (past the container end it reads as zero);
-//  * LDS rows use odd dword strides so that lanes reading the same entry
-//    index of their own tables hit different banks;
 //  * blocks are numbered so that the groups of one (row, channel block) run
 //    on the same XCD.
 #include "kvc_internal.h"
@@ -42,8 +45,9 @@ namespace {
 
 constexpr uint32_t kMaxWaves = kDecodeMaxWaves;  // waves per workgroup (host picks W <= this)
 constexpr uint32_t kSlots = 2;                   // streams per lane
-constexpr uint32_t kAStride = 129;  // dwords per staged anchor model (cum[0..256] + pad)
-constexpr uint32_t kDStride = 33;   // dwords per staged delta model (cum[0..63] + pad)
+constexpr uint32_t kARows = 258;    // staged anchor model rows: cum[0..256] + pad
+constexpr uint32_t kDRows = 66;     // staged delta model rows: cum[0..63] + 2 pads
+constexpr uint32_t kRowBytes = 2 * kWave;  // one u16 entry for each of the 64 lanes
 constexpr uint32_t kRing = 5;       // dwords per lane ring: 16 bytes + mirror of bytes 0..3
 constexpr uint32_t kXcds = 8;
 
@@ -51,133 +55,131 @@ constexpr uint32_t kXcds = 8;
 // every access compiles to a ds_* or global_* instruction (a generic "flat"
 // access counts against both wait counters).
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
-typedef __attribute__((address_space(3))) const uint16_t lds_cu16;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) const uint8_t lds_cu8;
 typedef __attribute__((address_space(1))) uint8_t gbyte;
 
-// t = floor(code / r) for r in [2^9, 2^17).  The float estimate is biased
-// down by 2^-5, more than its worst error for quotients below 2^16, so it is
-// t or t - 1 and one compare fixes it; it never exceeds the true quotient,
-// so q * r <= code cannot wrap.  A quotient >= 2^15 (a corrupt stream) is
-// always returned as >= 2^15.
-__device__ inline uint32_t quotient(uint32_t code, uint32_t r) {
-  const float fr = (float)r;
-  const float fc = (float)code;
-  const uint32_t q = (uint32_t)(int32_t)__builtin_fmaf(fc, __builtin_amdgcn_rcpf(fr), -0.03125f);
-  const uint32_t p = __umul24(q, r);  // q < 2^24, r < 2^17: exact in 32 bits
-  return q + (code - p >= r ? 1u : 0u);
+// Position of the highest set bit counted from the top (v_ffbh_u32): 0..31,
+// and all ones for 0, which only a corrupt stream can produce.
+__device__ inline uint32_t ffbh(uint32_t v) {
+  uint32_t r;
+  __asm__("v_ffbh_u32 %0, %1" : "=v"(r) : "v"(v));
+  return r;
+}
+
+// LDS byte address of a lane's entry `row` of a row-interleaved table.
+__device__ inline uint32_t lds_addr(const lds_u32 *table) {
+  return (uint32_t)(uintptr_t)table;
+}
+__device__ inline uint32_t lds_read_u16(uint32_t addr) {
+  return *(const lds_u16 *)(uintptr_t)addr;
 }
 
 struct Stream {
   uint32_t voff;        // byte offset of the stream in its container
   lds_u32 *ring;        // this lane's ring in LDS (16 bytes + 4 mirrored)
   uint32_t code, range;
-  uint32_t rpos;        // bytes consumed
-  uint32_t wpos;        // bytes written to the ring (a multiple of 8)
-  uint32_t b0, b1;      // the 8 bytes at wpos, loaded ahead (memory order)
+  uint32_t rposb;       // bits consumed (a multiple of 8)
+  uint32_t wposb;       // bits written to the ring (a multiple of 64)
+  uint32_t b0, b1;      // the 8 bytes at wposb / 8, loaded ahead (memory order)
   uint32_t n;
   uint32_t nbytes;
-  uint32_t tor;         // OR of every quotient: >= 2^15 flags a corrupt stream
+  int32_t tor;          // largest delta q seen (> M flags a corrupt stream)
   int32_t M;
+  uint32_t dbase;       // LDS byte address of this lane's delta row 0
+  uint32_t dbaseM;      // dbase + M rows: (addr - dbaseM) >> 7 is q = s - M
   float lo, sa, dl, ahat;
 
   __device__ inline void load_block(__amdgpu_buffer_rsrc_t src) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(src, voff + wpos, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(src, voff + (wposb >> 3), 0, 0);
     b0 = v[0];
     b1 = v[1];
   }
-  __device__ inline void write_block() {  // b0, b1 into the free ring half
-    const uint32_t h = (wpos >> 2) & 2;     // dword 0 or 2
+  // Store the block loaded earlier into the free half of the ring and load
+  // the next one.  Only the rings that run low do this, and as late as
+  // possible, so that a block has had about a group of tokens to arrive.
+  __device__ inline void write_block(__amdgpu_buffer_rsrc_t src) {
+    const uint32_t h = (wposb >> 5) & 2;  // dword 0 or 2
     ring[h] = b0;
     ring[h + 1] = b1;
     if (h == 0) ring[4] = b0;
-    wpos += 8;
+    wposb += 64;
+    load_block(src);
   }
-  // At a group boundary: store the block loaded earlier if its half of the
-  // ring is free, then load the block that follows the ring's contents.
-  __device__ inline void maintain(__amdgpu_buffer_rsrc_t src) {
-    if (wpos - rpos <= 8) {
-      write_block();
-      load_block(src);
-    }
+  // At a group's anchor: top the ring up if at most 8 bytes are left.
+  __device__ inline void refill(__amdgpu_buffer_rsrc_t src) {
+    if (wposb - rposb <= 64) write_block(src);
   }
-  // Make sure the next symbol's (at most 2) bytes are in the ring (rare).
+  // Before every token: the next symbol's (at most 2) bytes must be in the
+  // ring (rarely false).
   __device__ inline void ensure(__amdgpu_buffer_rsrc_t src) {
-    if (__builtin_expect(wpos - rpos < 2, 0)) {
-      write_block();
-      load_block(src);
-    }
+    if (__builtin_expect(wposb - rposb < 16, 0)) write_block(src);
   }
 };
 
 // One token of Q streams of a lane, in lockstep: range decode, dequantize.
-// kSteps binary-search steps cover symbol indices [0, 2^kSteps); entries past
-// a model's alphabet are >= 0x8000 and never taken for a valid target.  Writes the value to
-// store (binary16 bits, or the symbol) to v[q].
+// The symbol is the largest k with r * cum[k] <= code (the division-free form
+// of cum[k] <= floor(code / r)); kSteps binary-search steps cover indices
+// [0, 2^kSteps), and delta entries past an alphabet are staged as 2^15 so
+// that no product can wrap and a valid code never selects them.  Writes the
+// value to store (binary16 bits, or the symbol) to v[q].
 template <uint32_t Q, bool kSymbols, bool kAnchor, uint32_t kSteps>
-__device__ inline void step(Stream *st, lds_cu16 *ta, lds_cu16 *const *td,
-                            const __amdgpu_buffer_rsrc_t *src, uint32_t *v) {
+__device__ inline void step(Stream *st, uint32_t abase, uint32_t *v) {
+  uint32_t in[Q];
 #pragma unroll
-  for (uint32_t q = 0; q < Q; ++q) st[q].ensure(src[q]);
-  uint32_t r[Q], t[Q], s[Q], cs[Q], cn[Q];
+  for (uint32_t q = 0; q < Q; ++q) {
+    lds_cu8 *rb = (lds_cu8 *)st[q].ring + ((st[q].rposb >> 3) & 15);
+    in[q] = ((uint32_t)rb[0] << 8) | rb[1];  // the next two stream bytes
+  }
+  uint32_t r[Q], a[Q];
 #pragma unroll
   for (uint32_t q = 0; q < Q; ++q) {
     r[q] = st[q].range >> kPrec;
-    t[q] = quotient(st[q].code, r[q]);
-    st[q].tor |= t[q];
+    a[q] = kAnchor ? abase : st[q].dbase;
   }
-  // binary search of the cumulative table, the streams' probes interleaved
-  lds_cu16 *p[Q];
-#pragma unroll
-  for (uint32_t q = 0; q < Q; ++q) p[q] = kAnchor ? ta : td[q];
-  lds_cu16 *base[Q];
-#pragma unroll
-  for (uint32_t q = 0; q < Q; ++q) base[q] = p[q];
+  // binary search, the streams' probes interleaved
 #pragma unroll
   for (uint32_t sz = 1u << (kSteps - 1); sz; sz >>= 1) {
     uint32_t probe[Q];
 #pragma unroll
-    for (uint32_t q = 0; q < Q; ++q) probe[q] = p[q][sz];
+    for (uint32_t q = 0; q < Q; ++q) probe[q] = lds_read_u16(a[q] + sz * kRowBytes);
 #pragma unroll
     for (uint32_t q = 0; q < Q; ++q)
-      if (probe[q] <= t[q]) p[q] += sz;
-  }
-#pragma unroll
-  for (uint32_t q = 0; q < Q; ++q) {
-    s[q] = (uint32_t)(p[q] - base[q]);
-    cs[q] = p[q][0];
-    cn[q] = p[q][1];
-  }
-  uint32_t in[Q];
-#pragma unroll
-  for (uint32_t q = 0; q < Q; ++q) {
-    lds_cu8 *rb = (lds_cu8 *)st[q].ring + (st[q].rpos & 15);
-    in[q] = ((uint32_t)rb[0] << 8) | rb[1];  // the next two stream bytes
+      if (__umul24(r[q], probe[q]) <= st[q].code) a[q] += sz * kRowBytes;
   }
 #pragma unroll
   for (uint32_t q = 0; q < Q; ++q) {
     Stream &x = st[q];
-    // 24-bit multiplies: r < 2^17 and cumulative counts <= 2^16.  Every
-    // interval of the staged tables is nonempty (the profiler gives every
-    // symbol a nonzero frequency; pads increase), so range >= r >= 2^9 here
-    // and >= 2^24 after the shift: the count of leading zeros is defined.
-    x.code -= __umul24(r[q], cs[q]);
-    const uint32_t range = __umul24(r[q], cn[q] - cs[q]);
-    // whole bytes to shift in: 0, 1 or 2
-    const uint32_t lz = (uint32_t)__builtin_clz(range);
-    const uint32_t sh = lz & 24u;
+    const uint32_t cs = lds_read_u16(a[q]);
+    const uint32_t cn = lds_read_u16(a[q] + kRowBytes);
+    uint32_t sym;
+    int32_t qd = 0;
+    if constexpr (kAnchor) {
+      sym = (a[q] - abase) >> 7;
+      // a code at or past r * 2^15 has no symbol
+      if (x.code >= (r[q] << kPrec)) x.tor = 0x7FFFFFFF;
+    } else {
+      qd = (int32_t)(a[q] - x.dbaseM) >> 7;
+      sym = (uint32_t)(qd + x.M);
+      x.tor = qd > x.tor ? qd : x.tor;
+    }
+    // 24-bit multiplies: r < 2^17 and staged cumulative counts <= 2^15
+    x.code -= __umul24(r[q], cs);
+    const uint32_t range = __umul24(r[q], cn - cs);
+    // whole bytes to shift in: 0, 1 or 2 (range >= 2^9 for a valid stream)
+    const uint32_t sh = ffbh(range) & 24u;
     x.range = range << sh;
     x.code = (x.code << sh) | (in[q] >> ((16 - sh) & 31));
-    x.rpos += lz >> 3;
+    x.rposb += sh;
     if constexpr (kSymbols) {
-      v[q] = s[q];
+      v[q] = sym;
     } else {
       float y;
       if constexpr (kAnchor) {
-        x.ahat = __builtin_fmaf((float)s[q], x.sa, x.lo);
+        x.ahat = __builtin_fmaf((float)sym, x.sa, x.lo);
         y = x.ahat;
       } else {
-        y = __builtin_fmaf((float)((int32_t)s[q] - x.M), x.dl, x.ahat);
+        y = __builtin_fmaf((float)qd, x.dl, x.ahat);
       }
       v[q] = f2h(y);
     }
@@ -200,14 +202,15 @@ __device__ inline gbyte *uniform_ptr(gbyte *p) {
   return (gbyte *)(((uint64_t)hi << 32) | lo);
 }
 
-// The delta tokens of one group (tokens j+1 .. jend-1) of both streams.
+// The `count` delta tokens of one group, both streams.
 template <bool kSymbols, uint32_t kSteps>
-__device__ inline void delta_run(Stream *st, lds_cu16 *ta, lds_cu16 *const *td,
-                                 const __amdgpu_buffer_rsrc_t *src, gbyte **ob, uint64_t ld,
-                                 uint32_t lane, uint32_t count) {
+__device__ inline void delta_run(Stream *st, uint32_t abase, const __amdgpu_buffer_rsrc_t *src,
+                                 gbyte **ob, uint64_t ld, uint32_t lane, uint32_t count) {
   for (uint32_t i = 0; i < count; ++i) {
+    st[0].ensure(src[0]);
+    st[1].ensure(src[1]);
     uint32_t v[2];
-    step<2, kSymbols, false, kSteps>(st, ta, td, src, v);
+    step<2, kSymbols, false, kSteps>(st, abase, v);
     put<kSymbols>(ob[0], lane, v[0]);
     put<kSymbols>(ob[1], lane, v[1]);
     ob[0] += ld;
@@ -216,32 +219,31 @@ __device__ inline void delta_run(Stream *st, lds_cu16 *ta, lds_cu16 *const *td,
 }
 
 template <bool kSymbols>
-__device__ inline void delta_dispatch(uint32_t steps, Stream *st, lds_cu16 *ta,
-                                      lds_cu16 *const *td, const __amdgpu_buffer_rsrc_t *src,
-                                      gbyte **ob, uint64_t ld, uint32_t lane, uint32_t count) {
+__device__ inline void delta_dispatch(uint32_t steps, Stream *st, uint32_t abase,
+                                      const __amdgpu_buffer_rsrc_t *src, gbyte **ob, uint64_t ld,
+                                      uint32_t lane, uint32_t count) {
   switch (steps) {
-    case 2: delta_run<kSymbols, 2>(st, ta, td, src, ob, ld, lane, count); break;
-    case 3: delta_run<kSymbols, 3>(st, ta, td, src, ob, ld, lane, count); break;
-    case 4: delta_run<kSymbols, 4>(st, ta, td, src, ob, ld, lane, count); break;
-    case 5: delta_run<kSymbols, 5>(st, ta, td, src, ob, ld, lane, count); break;
-    default: delta_run<kSymbols, 6>(st, ta, td, src, ob, ld, lane, count); break;
+    case 2: delta_run<kSymbols, 2>(st, abase, src, ob, ld, lane, count); break;
+    case 3: delta_run<kSymbols, 3>(st, abase, src, ob, ld, lane, count); break;
+    case 4: delta_run<kSymbols, 4>(st, abase, src, ob, ld, lane, count); break;
+    case 5: delta_run<kSymbols, 5>(st, abase, src, ob, ld, lane, count); break;
+    default: delta_run<kSymbols, 6>(st, abase, src, ob, ld, lane, count); break;
   }
 }
 
 template <bool kSymbols>
-__device__ inline void single_step(uint32_t steps, bool anchor, Stream *st, lds_cu16 *ta,
-                                   lds_cu16 *const *td, const __amdgpu_buffer_rsrc_t *src,
+__device__ inline void single_step(uint32_t steps, bool anchor, Stream *st, uint32_t abase,
                                    uint32_t *v) {
   if (anchor) {
-    step<1, kSymbols, true, 8>(st, ta, td, src, v);
+    step<1, kSymbols, true, 8>(st, abase, v);
     return;
   }
   switch (steps) {
-    case 2: step<1, kSymbols, false, 2>(st, ta, td, src, v); break;
-    case 3: step<1, kSymbols, false, 3>(st, ta, td, src, v); break;
-    case 4: step<1, kSymbols, false, 4>(st, ta, td, src, v); break;
-    case 5: step<1, kSymbols, false, 5>(st, ta, td, src, v); break;
-    default: step<1, kSymbols, false, 6>(st, ta, td, src, v); break;
+    case 2: step<1, kSymbols, false, 2>(st, abase, v); break;
+    case 3: step<1, kSymbols, false, 3>(st, abase, v); break;
+    case 4: step<1, kSymbols, false, 4>(st, abase, v); break;
+    case 5: step<1, kSymbols, false, 5>(st, abase, v); break;
+    default: step<1, kSymbols, false, 6>(st, abase, v); break;
   }
 }
 
@@ -272,18 +274,25 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
 
   extern __shared__ uint32_t lds_raw[];
   lds_u32 *lds = (lds_u32 *)lds_raw;
-  lds_u32 *sA = lds;                                // [64][kAStride] anchor cum
-  lds_u32 *sD = sA + kWave * kAStride;              // [levels used][64][kDStride] delta cum
-  lds_u32 *sR = sD + nlev_used * kWave * kDStride;  // [waves][kSlots][64][kRing] rings
+  lds_u32 *sA = lds;                                    // [kARows][64] u16 anchor cum
+  lds_u32 *sD = sA + kARows * kWave / 2;                // [levels used][kDRows][64] u16 delta cum
+  lds_u32 *sR = sD + nlev_used * kDRows * kWave / 2;    // [waves][kSlots][64][kRing] rings
+  lds_u16 *hA = (lds_u16 *)sA;
+  lds_u16 *hD = (lds_u16 *)sD;
 
-  // ---- stage the 64 channels' anchor models and the used levels' delta models
+  // ---- stage the 64 channels' anchor models and the used levels' delta
+  // models, row-interleaved: entry i of lane l at u16 index i * 64 + l, so
+  // lanes reading their own tables hit different banks unless two lanes of a
+  // pair read different rows of the same parity.
   const uint32_t tid = threadIdx.x;
   {
     const uint32_t *gA = reinterpret_cast<const uint32_t *>(tables + kTablesHdr) +
                          (uint64_t)m0 * (kAnchorStride / 2);
-    for (uint32_t i = tid; i < nv * kAStride; i += blockDim.x) {
-      const uint32_t mm = i / kAStride, w = i % kAStride;
-      sA[i] = gA[(uint64_t)mm * (kAnchorStride / 2) + w];
+    for (uint32_t i = tid; i < nv * (kARows / 2); i += blockDim.x) {
+      const uint32_t w = i / nv, l = i % nv;
+      const uint32_t v = gA[(uint64_t)l * (kAnchorStride / 2) + w];
+      hA[(2 * w) * kWave + l] = (uint16_t)v;
+      hA[(2 * w + 1) * kWave + l] = (uint16_t)(v >> 16);
     }
     uint32_t slot = 0;
     for (uint32_t lv = 0; lv < d.nlev; ++lv) {
@@ -291,18 +300,15 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
       const uint32_t *gD = reinterpret_cast<const uint32_t *>(
                                tables + kTablesHdr + (uint64_t)S * kAnchorStride * 2) +
                            ((uint64_t)lv * S + m0) * (kDeltaStride / 2);
-      lds_u32 *dst = sD + slot * kWave * kDStride;
-      for (uint32_t i = tid; i < nv * kDStride; i += blockDim.x) {
-        const uint32_t mm = i / kDStride, w = i % kDStride;
+      lds_u16 *dst = hD + slot * kDRows * kWave;
+      for (uint32_t i = tid; i < nv * (kDRows / 2); i += blockDim.x) {
+        const uint32_t w = i / nv, l = i % nv;
         const uint32_t v =
-            w < kDeltaStride / 2 ? gD[(uint64_t)mm * (kDeltaStride / 2) + w] : 0xFFFFFFFFu;
-        // entries past cum[A] (0xFFFF in the blob) become 0x8000 + index:
-        // above any valid target and strictly increasing, so even a corrupt
-        // stream's search never yields an empty interval
-        uint32_t lo16 = v & 0xFFFFu, hi16 = v >> 16;
-        lo16 = lo16 == 0xFFFFu ? 0x8000u + 2 * w : lo16;
-        hi16 = hi16 == 0xFFFFu ? 0x8001u + 2 * w : hi16;
-        dst[i] = lo16 | (hi16 << 16);
+            w < kDeltaStride / 2 ? gD[(uint64_t)l * (kDeltaStride / 2) + w] : 0xFFFFFFFFu;
+        // entries past cum[A] (0xFFFF pads) become 2^15 = cum[A]
+        const uint32_t e0 = v & 0xFFFFu, e1 = v >> 16;
+        dst[(2 * w) * kWave + l] = (uint16_t)(e0 == 0xFFFFu ? kTot : e0);
+        dst[(2 * w + 1) * kWave + l] = (uint16_t)(e1 == 0xFFFFu ? kTot : e1);
       }
       ++slot;
     }
@@ -312,7 +318,7 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   if (lane >= nv) return;
 
-  lds_cu16 *ta = (lds_cu16 *)(sA + lane * kAStride);
+  const uint32_t abase = lds_addr(sA) + 2 * lane;
   const uint32_t third = third_of(row >> 1, d.L);
   const uint32_t esz = kSymbols ? 1u : 2u;
   const uint64_t ld = (uint64_t)d.C * esz;
@@ -320,7 +326,6 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
   const uint32_t npairs = (gp.count + 1) / 2;
 
   for (uint32_t pair = wave; pair < npairs; pair += n_waves) {
-    lds_cu16 *td[kSlots];
     Stream st[kSlots];
     gbyte *ob[kSlots];  // wave-uniform output row of the current token
     __amdgpu_buffer_rsrc_t src[kSlots];
@@ -334,17 +339,21 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
       active[q] = idx < gp.count && valid[k];
       s.n = 0;
       s.tor = 0;
+      s.M = 0;
       s.ring = sR + ((wave * kSlots + q) * kWave + lane) * kRing;
       ob[q] = (gbyte *)out;
-      td[q] = (lds_cu16 *)(sD + lane * kDStride);
+      s.dbase = lds_addr(sD) + 2 * lane;
+      s.dbaseM = s.dbase;
       src[q] = __builtin_amdgcn_make_buffer_rsrc((void *)ci[k].cont, (short)0, 0, kBufferWord3);
       if (!active[q]) continue;
       const ChunkInfo c = ci[k];
       const uint32_t lslot = __builtin_popcount(level_mask & ((1u << c.level) - 1u));
-      td[q] = (lds_cu16 *)(sD + (lslot * kWave + lane) * kDStride);
+      s.dbase = lds_addr(sD) + lslot * kDRows * kRowBytes + 2 * lane;
       const uint32_t b = d.bits[c.level][third];
       steps = b > steps ? b : steps;
       s.M = (1 << (b - 1)) - 1;
+      s.dbaseM = s.dbase + (uint32_t)s.M * kRowBytes;
+      s.tor = -s.M;
       const uint32_t *rec = reinterpret_cast<const uint32_t *>(c.records + (uint64_t)m * kRecBytes);
       s.lo = __builtin_bit_cast(float, rec[0]);
       s.sa = __builtin_bit_cast(float, rec[1]);
@@ -364,32 +373,33 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
       s.ring[2] = v[2];
       s.ring[3] = v[3];
       s.ring[4] = v[0];
-      s.wpos = 16;
+      s.wposb = 128;
       s.load_block(src[q]);
       s.code = bswap32(v[0]);
-      s.rpos = 4;
+      s.rposb = 32;
       s.range = 0xFFFFFFFFu;
     }
     steps = __builtin_amdgcn_readfirstlane(steps);
 
     // Both streams live: one lockstep step per token, so the two dependency
-    // chains interleave; only the rare ring refills branch.
+    // chains interleave; only the ring refills branch.
     const uint32_t nmin = st[0].n < st[1].n ? st[0].n : st[1].n;
     const uint32_t nmax = st[0].n > st[1].n ? st[0].n : st[1].n;
     uint32_t j = 0;
     while (j < nmin) {
-      st[0].maintain(src[0]);
-      st[1].maintain(src[1]);
+      // after a refill at least 8 bytes are buffered: no check for the anchor
+      st[0].refill(src[0]);
+      st[1].refill(src[1]);
       {
         uint32_t v[2];
-        step<2, kSymbols, true, 8>(st, ta, td, src, v);
+        step<2, kSymbols, true, 8>(st, abase, v);
         put<kSymbols>(ob[0], lane, v[0]);
         put<kSymbols>(ob[1], lane, v[1]);
         ob[0] += ld;
         ob[1] += ld;
       }
       const uint32_t jend = j + d.G < nmin ? j + d.G : nmin;
-      delta_dispatch<kSymbols>(steps, st, ta, td, src, ob, ld, lane, jend - j - 1);
+      delta_dispatch<kSymbols>(steps, st, abase, src, ob, ld, lane, jend - j - 1);
       j = jend;
     }
     // Tail: one stream left (odd chunk count, or a shorter last chunk).
@@ -400,9 +410,12 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
 #pragma unroll
       for (uint32_t q = 0; q < kSlots; ++q) {
         if (j < st[q].n) {
-          if (anchor) st[q].maintain(src[q]);
+          if (anchor)
+            st[q].refill(src[q]);
+          else
+            st[q].ensure(src[q]);
           uint32_t v;
-          single_step<kSymbols>(steps, anchor, &st[q], ta, &td[q], &src[q], &v);
+          single_step<kSymbols>(steps, anchor, &st[q], abase, &v);
           put<kSymbols>(ob[q], lane, v);
           ob[q] += ld;
         }
@@ -410,14 +423,14 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
     }
 #pragma unroll
     for (uint32_t q = 0; q < kSlots; ++q)
-      if (active[q] && ((st[q].tor >> kPrec) != 0 || st[q].rpos != st[q].nbytes))
+      if (active[q] && (st[q].tor > st[q].M || st[q].rposb != 8 * st[q].nbytes))
         set_status(status, KVC_ERR_CORRUPT_STREAM);
   }
 }
 
 size_t decode_lds_bytes(uint32_t levels, uint32_t waves) {
-  return sizeof(uint32_t) * ((size_t)kWave * kAStride + (size_t)levels * kWave * kDStride +
-                             (size_t)waves * kSlots * kWave * kRing);
+  return (size_t)kARows * kRowBytes + (size_t)levels * kDRows * kRowBytes +
+         sizeof(uint32_t) * (size_t)waves * kSlots * kWave * kRing;
 }
 
 hipError_t launch_decode(const Desc &d, const ChunkInfo *dev_chunks, const DecodeGroup *groups,
