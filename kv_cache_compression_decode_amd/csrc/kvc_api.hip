@@ -21,11 +21,13 @@ hipError_t launch_decode(const Desc &d, const ChunkInfo *dev_chunks, const Decod
                          uint32_t T_total, bool symbols, int32_t *status, hipStream_t stream);
 size_t decode_lds_bytes(uint32_t levels, uint32_t waves);
 hipError_t launch_encode(const Desc &d, const uint8_t *tables, const uint16_t *kv, uint32_t T,
-                         const ChunkInfo *dev_chunks, uint32_t n_chunks, uint8_t *records,
-                         uint64_t *row_sums, uint32_t *flags, uint32_t *offsets, uint8_t *valid,
-                         uint64_t *payload, uint64_t *chunk_off_ws, uint32_t *fits, uint8_t *out,
-                         uint64_t out_cap, uint64_t *chunk_off_out, int32_t *status,
-                         hipStream_t stream);
+                         const ChunkInfo *dev_chunks, uint32_t n_chunks,
+                         const DecodeGroup *groups, uint32_t n_groups, uint32_t levels,
+                         uint32_t waves, uint8_t *records, uint64_t *row_sums, uint32_t *flags,
+                         uint32_t *offsets, uint8_t *valid, uint64_t *payload,
+                         uint64_t *chunk_off_ws, uint32_t *fits, uint8_t *out, uint64_t out_cap,
+                         uint64_t *chunk_off_out, int32_t *status, hipStream_t stream);
+size_t encode_lds_bytes(uint32_t levels);
 hipError_t launch_profile(const Desc &d, const uint16_t *kv, uint32_t T, uint8_t *tables,
                           uint32_t *counts, uint64_t *model_hash, uint64_t *row_hash,
                           int32_t *status, hipStream_t stream);
@@ -319,8 +321,33 @@ kvc_status kvc_encode(const kvc_codec_desc *dd, const void *tables, const uint16
   ChunkInfo *dch = reinterpret_cast<ChunkInfo *>(base + w.chunks);
   e = launch_load_chunks(info.data(), K, dch, reinterpret_cast<uint32_t *>(base + w.hdr), stream);
   if (e != hipSuccess) return KVC_ERR_HIP;
-  e = launch_encode(d, static_cast<const uint8_t *>(tables), kv_fp16, T, dch, K,
-                    base + w.records, reinterpret_cast<uint64_t *>(base + w.rows),
+  // Encode groups: contiguous chunk ranges, each encoded by one workgroup
+  // per (row, channel block) that stages the models of the levels it uses;
+  // its waves take the group's chunks in turn, at most kMaxRounds each.
+  std::vector<DecodeGroup> groups;
+  uint32_t levels = 1, waves = 1;
+  {
+    constexpr uint32_t kMaxRounds = 4;
+    const uint32_t per = kEncodeMaxWaves * kMaxRounds;
+    const uint32_t ng = (K + per - 1) / per;
+    for (uint32_t gi = 0; gi < ng; ++gi) {
+      const uint32_t a = (uint32_t)((uint64_t)K * gi / ng);
+      const uint32_t b = (uint32_t)((uint64_t)K * (gi + 1) / ng);
+      DecodeGroup g{};
+      g.start = a;
+      g.count = b - a;
+      for (uint32_t i = a; i < b; ++i) g.level |= 1u << chunk_levels[i];
+      levels = std::max<uint32_t>(levels, (uint32_t)__builtin_popcount(g.level));
+      waves = std::max<uint32_t>(waves, std::min<uint32_t>(kEncodeMaxWaves, g.count));
+      groups.push_back(g);
+    }
+  }
+  DecodeGroup *dgr = reinterpret_cast<DecodeGroup *>(base + w.groups);
+  e = launch_load_groups(groups.data(), (uint32_t)groups.size(), dgr, stream);
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  e = launch_encode(d, static_cast<const uint8_t *>(tables), kv_fp16, T, dch, K, dgr,
+                    (uint32_t)groups.size(), levels, waves, base + w.records,
+                    reinterpret_cast<uint64_t *>(base + w.rows),
                     reinterpret_cast<uint32_t *>(base + w.hdr),
                     reinterpret_cast<uint32_t *>(base + w.offsets), base + w.valid,
                     reinterpret_cast<uint64_t *>(base + w.payload),

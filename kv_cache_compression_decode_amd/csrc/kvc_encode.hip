@@ -5,8 +5,10 @@
 // anchor); layer-wise delta quantization (coarser for deeper thirds);
 // arithmetic coding with per channel-layer models.
 //
-// Kernels (one wavefront per (chunk, row, 64-channel block); lane = channel,
-// so every token's 64 inputs are one coalesced 128-byte load):
+// Kernels (a workgroup per (row, 64-channel block, group of chunks) stages
+// the 64 channels' models once; its waves take the group's chunks in turn;
+// lane = channel, so every token's 64 inputs are one coalesced 128-byte
+// load):
 //   k_encode_stats : per stream lo / sa / dl and the exact coded length
 //                    (the length depends only on the range evolution, so no
 //                    bytes are produced); records go to the workspace;
@@ -22,21 +24,47 @@ namespace kvc {
 
 namespace {
 
+constexpr uint32_t kXcds = 8;
+constexpr uint32_t kEA = 133;  // dwords per staged anchor model (cum[0..256] + pad; odd)
+constexpr uint32_t kED = 33;   // dwords per staged delta model (cum[0..63] + pad; odd)
+
+// The 64 channels' anchor models and the delta models of every level in
+// `level_mask`, one row per lane at odd dword strides (lanes indexing their
+// own rows hit different banks more often than not).
 __device__ inline void stage_tables(const Desc &d, const uint8_t *tables, uint32_t m0,
-                                    uint32_t nv, uint32_t level, uint16_t *sA, uint16_t *sD,
-                                    uint32_t lane) {
+                                    uint32_t nv, uint32_t level_mask, uint32_t *sA,
+                                    uint32_t *sD) {
   const uint32_t S = n_streams(d);
-  const uint4 *srcA =
-      reinterpret_cast<const uint4 *>(tables + kTablesHdr + (uint64_t)m0 * kAnchorStride * 2);
-  uint4 *dstA = reinterpret_cast<uint4 *>(sA);
-  const uint32_t nA = nv * (kAnchorStride * 2 / 16);
-  for (uint32_t i = lane; i < nA; i += kWave) dstA[i] = srcA[i];
-  const uint64_t delta_off = kTablesHdr + (uint64_t)S * kAnchorStride * 2;
-  const uint4 *srcD = reinterpret_cast<const uint4 *>(
-      tables + delta_off + ((uint64_t)level * S + m0) * kDeltaStride * 2);
-  uint4 *dstD = reinterpret_cast<uint4 *>(sD);
-  const uint32_t nD = nv * (kDeltaStride * 2 / 16);
-  for (uint32_t i = lane; i < nD; i += kWave) dstD[i] = srcD[i];
+  const uint32_t *gA = reinterpret_cast<const uint32_t *>(tables + kTablesHdr) +
+                       (uint64_t)m0 * (kAnchorStride / 2);
+  for (uint32_t i = threadIdx.x; i < nv * (kAnchorStride / 2); i += blockDim.x) {
+    const uint32_t l = i / (kAnchorStride / 2), w = i % (kAnchorStride / 2);
+    if (w < kEA) sA[l * kEA + w] = gA[i];
+  }
+  uint32_t slot = 0;
+  for (uint32_t lv = 0; lv < d.nlev; ++lv) {
+    if (!((level_mask >> lv) & 1u)) continue;
+    const uint32_t *gD = reinterpret_cast<const uint32_t *>(
+                             tables + kTablesHdr + (uint64_t)S * kAnchorStride * 2) +
+                         ((uint64_t)lv * S + m0) * (kDeltaStride / 2);
+    uint32_t *dst = sD + slot * kWave * kED;
+    for (uint32_t i = threadIdx.x; i < nv * (kDeltaStride / 2); i += blockDim.x) {
+      const uint32_t l = i / (kDeltaStride / 2), w = i % (kDeltaStride / 2);
+      dst[l * kED + w] = gD[i];
+    }
+    ++slot;
+  }
+}
+
+// Which (unit, group) a block owns: the groups of one (row, channel block)
+// on the same XCD.
+struct EncodeBlock {
+  uint32_t unit, grp;
+};
+__device__ inline EncodeBlock encode_block(uint32_t n_groups) {
+  const uint32_t id = blockIdx.x;
+  const uint32_t local = id / kXcds;
+  return {(local / n_groups) * kXcds + id % kXcds, local % n_groups};
 }
 
 // Little-endian byte sink into 4-byte words, bounded by `cap` bytes.
@@ -114,69 +142,80 @@ struct RangeEncoder {
 }  // namespace
 
 // Statistics and exact coded length of every stream.
-__global__ __launch_bounds__(64) void k_encode_stats(Desc d, const ChunkInfo *__restrict__ ci,
-                                                     const uint8_t *__restrict__ tables,
-                                                     const uint16_t *__restrict__ kv, uint32_t T,
-                                                     uint8_t *__restrict__ records,
-                                                     int32_t *status) {
-  const uint32_t cb = blockIdx.x, row = blockIdx.y, k = blockIdx.z;
-  __shared__ uint16_t sA[kWave * kAnchorStride];
-  __shared__ uint16_t sD[kWave * kDeltaStride];
-  const uint32_t lane = threadIdx.x;
+__global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_stats(
+    Desc d, const ChunkInfo *__restrict__ ci, const DecodeGroup *__restrict__ groups,
+    uint32_t n_groups, uint32_t n_units, const uint8_t *__restrict__ tables,
+    const uint16_t *__restrict__ kv, uint32_t T, uint8_t *__restrict__ records, int32_t *status) {
+  const EncodeBlock eb = encode_block(n_groups);
+  if (eb.unit >= n_units) return;
+  const uint32_t ncb = (d.C + kWave - 1) / kWave;
+  const uint32_t row = eb.unit / ncb, cb = eb.unit % ncb;
+  const DecodeGroup gp = groups[eb.grp];
+  extern __shared__ uint32_t lds_raw[];
+  uint32_t *sA = lds_raw;
+  uint32_t *sD = sA + kWave * kEA;
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const uint32_t n_waves = blockDim.x / kWave;
   const uint32_t S = n_streams(d);
   const uint32_t c0 = cb * kWave;
   const uint32_t nv = d.C - c0 < kWave ? d.C - c0 : kWave;
   const uint32_t m0 = row * d.C + c0;
-  const ChunkInfo c = ci[k];
-  const uint32_t level = c.level;
-  const uint32_t b = d.bits[level][third_of(row >> 1, d.L)];
-  const int32_t M = (1 << (b - 1)) - 1;
-  stage_tables(d, tables, m0, nv, level, sA, sD, lane);
+  stage_tables(d, tables, m0, nv, gp.level, sA, sD);
   __syncthreads();
   if (lane >= nv) return;
   const uint32_t m = m0 + lane;
-  const uint16_t *ta = sA + lane * kAnchorStride;
-  const uint16_t *td = sD + lane * kDeltaStride;
-
+  const uint16_t *ta = reinterpret_cast<const uint16_t *>(sA + lane * kEA);
+  const uint32_t third = third_of(row >> 1, d.L);
   const uint64_t ld = d.C;
-  const uint16_t *x = kv + ((uint64_t)row * T + c.first_token) * ld + c0 + lane;
-  const uint32_t n = c.n_tokens;
-  float lo, sa, maxabs;
-  if (!stream_stats(x, ld, n, d.G, lo, sa, maxabs)) set_status(status, KVC_ERR_NONFINITE);
-  const float dl = maxabs / (float)M;
 
-  // coded length = 4 + number of renormalisation shifts
-  uint32_t range = 0xFFFFFFFFu;
-  uint32_t shifts = 0;
-  float ahat = 0.0f;
-  uint32_t g = 0;
-  for (uint32_t j = 0; j < n; ++j) {
-    const float v = h2f(x[(uint64_t)j * ld]);
-    uint32_t f;
-    if (g == 0) {
-      const uint32_t qa = quant_anchor(v, lo, sa);
-      ahat = __builtin_fmaf((float)qa, sa, lo);
-      f = (uint32_t)ta[qa + 1] - ta[qa];
-    } else {
-      const uint32_t s = (uint32_t)(quant_delta(v - ahat, dl, M) + M);
-      f = (uint32_t)td[s + 1] - td[s];
+  for (uint32_t i = wave; i < gp.count; i += n_waves) {
+    const uint32_t k = gp.start + i;
+    const ChunkInfo c = ci[k];
+    const uint32_t level = c.level;
+    const uint32_t lslot = __builtin_popcount(gp.level & ((1u << level) - 1u));
+    const uint16_t *td = reinterpret_cast<const uint16_t *>(sD + (lslot * kWave + lane) * kED);
+    const uint32_t b = d.bits[level][third];
+    const int32_t M = (1 << (b - 1)) - 1;
+    const uint16_t *x = kv + ((uint64_t)row * T + c.first_token) * ld + c0 + lane;
+    const uint32_t n = c.n_tokens;
+    float lo, sa, maxabs;
+    if (!stream_stats(x, ld, n, d.G, lo, sa, maxabs)) set_status(status, KVC_ERR_NONFINITE);
+    const float dl = maxabs / (float)M;
+
+    // coded length = 4 + number of renormalisation shifts
+    uint32_t range = 0xFFFFFFFFu;
+    uint32_t shifts = 0;
+    float ahat = 0.0f;
+    uint32_t g = 0;
+    for (uint32_t j = 0; j < n; ++j) {
+      const float v = h2f(x[(uint64_t)j * ld]);
+      uint32_t f;
+      if (g == 0) {
+        const uint32_t qa = quant_anchor(v, lo, sa);
+        ahat = __builtin_fmaf((float)qa, sa, lo);
+        f = (uint32_t)ta[qa + 1] - ta[qa];
+      } else {
+        const uint32_t s = (uint32_t)(quant_delta(v - ahat, dl, M) + M);
+        f = (uint32_t)td[s + 1] - td[s];
+      }
+      g = g + 1 == d.G ? 0 : g + 1;
+      if (f == 0 || f > kTot) {  // damaged tables
+        set_status(status, KVC_ERR_CORRUPT_STREAM);
+        f = 1;
+      }
+      range = (range >> kPrec) * f;
+      while (range < (1u << 24)) {
+        range <<= 8;
+        ++shifts;
+      }
     }
-    g = g + 1 == d.G ? 0 : g + 1;
-    if (f == 0 || f > kTot) {  // damaged tables
-      set_status(status, KVC_ERR_CORRUPT_STREAM);
-      f = 1;
-    }
-    range = (range >> kPrec) * f;
-    while (range < (1u << 24)) {
-      range <<= 8;
-      ++shifts;
-    }
+    uint32_t *rec = reinterpret_cast<uint32_t *>(records + ((uint64_t)k * S + m) * kRecBytes);
+    rec[0] = __builtin_bit_cast(uint32_t, lo);
+    rec[1] = __builtin_bit_cast(uint32_t, sa);
+    rec[2] = __builtin_bit_cast(uint32_t, dl);
+    rec[3] = 4u + shifts;
   }
-  uint32_t *rec = reinterpret_cast<uint32_t *>(records + ((uint64_t)k * S + m) * kRecBytes);
-  rec[0] = __builtin_bit_cast(uint32_t, lo);
-  rec[1] = __builtin_bit_cast(uint32_t, sa);
-  rec[2] = __builtin_bit_cast(uint32_t, dl);
-  rec[3] = 4u + shifts;
 }
 
 // Container start offsets (one thread; chunk counts are small).
@@ -200,85 +239,101 @@ __global__ void k_encode_layout(Desc d, uint32_t n_chunks, const uint64_t *__res
   if (!ok) set_status(status, KVC_ERR_CAPACITY);
 }
 
-__global__ __launch_bounds__(64) void k_encode_emit(
-    Desc d, const ChunkInfo *__restrict__ ci, const uint8_t *__restrict__ tables,
+__global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
+    Desc d, const ChunkInfo *__restrict__ ci, const DecodeGroup *__restrict__ groups,
+    uint32_t n_groups, uint32_t n_units, const uint8_t *__restrict__ tables,
     const uint16_t *__restrict__ kv, uint32_t T, const uint8_t *__restrict__ records,
     const uint32_t *__restrict__ offsets, const uint64_t *__restrict__ chunk_off,
     const uint32_t *__restrict__ fits, uint8_t *__restrict__ out, int32_t *status) {
   if (*fits == 0) return;
-  const uint32_t cb = blockIdx.x, row = blockIdx.y, k = blockIdx.z;
-  __shared__ uint16_t sA[kWave * kAnchorStride];
-  __shared__ uint16_t sD[kWave * kDeltaStride];
-  const uint32_t lane = threadIdx.x;
+  const EncodeBlock eb = encode_block(n_groups);
+  if (eb.unit >= n_units) return;
+  const uint32_t ncb = (d.C + kWave - 1) / kWave;
+  const uint32_t row = eb.unit / ncb, cb = eb.unit % ncb;
+  const DecodeGroup gp = groups[eb.grp];
+  extern __shared__ uint32_t lds_raw[];
+  uint32_t *sA = lds_raw;
+  uint32_t *sD = sA + kWave * kEA;
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const uint32_t n_waves = blockDim.x / kWave;
   const uint32_t S = n_streams(d);
   const uint32_t c0 = cb * kWave;
   const uint32_t nv = d.C - c0 < kWave ? d.C - c0 : kWave;
   const uint32_t m0 = row * d.C + c0;
-  const ChunkInfo c = ci[k];
-  const uint32_t level = c.level;
-  const uint32_t b = d.bits[level][third_of(row >> 1, d.L)];
-  const int32_t M = (1 << (b - 1)) - 1;
-  stage_tables(d, tables, m0, nv, level, sA, sD, lane);
+  stage_tables(d, tables, m0, nv, gp.level, sA, sD);
   __syncthreads();
   if (lane >= nv) return;
   const uint32_t m = m0 + lane;
-  const uint16_t *ta = sA + lane * kAnchorStride;
-  const uint16_t *td = sD + lane * kDeltaStride;
-
-  const uint32_t *rin = reinterpret_cast<const uint32_t *>(records + ((uint64_t)k * S + m) * kRecBytes);
-  const float lo = __builtin_bit_cast(float, rin[0]);
-  const float sa = __builtin_bit_cast(float, rin[1]);
-  const float dl = __builtin_bit_cast(float, rin[2]);
-  const uint32_t nbytes = rin[3];
-
-  uint8_t *cont = out + chunk_off[k];
-  uint32_t *rout = reinterpret_cast<uint32_t *>(cont + kHdrBytes + (uint64_t)m * kRecBytes);
-  rout[0] = rin[0];
-  rout[1] = rin[1];
-  rout[2] = rin[2];
-  rout[3] = nbytes;
-
-  ByteSink sink;
-  sink.wp = reinterpret_cast<uint32_t *>(cont + kHdrBytes + (uint64_t)kRecBytes * S +
-                                         offsets[(uint64_t)k * S + m]);
-  sink.acc = 0;
-  sink.nacc = 0;
-  sink.count = 0;
-  sink.cap = nbytes;
-  sink.overflow = false;
-  RangeEncoder enc;
-  enc.low = 0;
-  enc.range = 0xFFFFFFFFu;
-  enc.cache = 0;
-  enc.nff = 0;
-  enc.have_cache = false;
-  enc.bad = false;
-
+  const uint16_t *ta = reinterpret_cast<const uint16_t *>(sA + lane * kEA);
+  const uint32_t third = third_of(row >> 1, d.L);
   const uint64_t ld = d.C;
-  const uint16_t *x = kv + ((uint64_t)row * T + c.first_token) * ld + c0 + lane;
-  const uint32_t n = c.n_tokens;
-  float ahat = 0.0f;
-  uint32_t g = 0;
-  for (uint32_t j = 0; j < n; ++j) {
-    const float v = h2f(x[(uint64_t)j * ld]);
-    uint32_t cs, f;
-    if (g == 0) {
-      const uint32_t qa = quant_anchor(v, lo, sa);
-      ahat = __builtin_fmaf((float)qa, sa, lo);
-      cs = ta[qa];
-      f = (uint32_t)ta[qa + 1] - cs;
-    } else {
-      const uint32_t s = (uint32_t)(quant_delta(v - ahat, dl, M) + M);
-      cs = td[s];
-      f = (uint32_t)td[s + 1] - cs;
+
+  for (uint32_t i = wave; i < gp.count; i += n_waves) {
+    const uint32_t k = gp.start + i;
+    const ChunkInfo c = ci[k];
+    const uint32_t level = c.level;
+    const uint32_t lslot = __builtin_popcount(gp.level & ((1u << level) - 1u));
+    const uint16_t *td = reinterpret_cast<const uint16_t *>(sD + (lslot * kWave + lane) * kED);
+    const uint32_t b = d.bits[level][third];
+    const int32_t M = (1 << (b - 1)) - 1;
+
+    const uint32_t *rin =
+        reinterpret_cast<const uint32_t *>(records + ((uint64_t)k * S + m) * kRecBytes);
+    const float lo = __builtin_bit_cast(float, rin[0]);
+    const float sa = __builtin_bit_cast(float, rin[1]);
+    const float dl = __builtin_bit_cast(float, rin[2]);
+    const uint32_t nbytes = rin[3];
+
+    uint8_t *cont = out + chunk_off[k];
+    uint32_t *rout = reinterpret_cast<uint32_t *>(cont + kHdrBytes + (uint64_t)m * kRecBytes);
+    rout[0] = rin[0];
+    rout[1] = rin[1];
+    rout[2] = rin[2];
+    rout[3] = nbytes;
+
+    ByteSink sink;
+    sink.wp = reinterpret_cast<uint32_t *>(cont + kHdrBytes + (uint64_t)kRecBytes * S +
+                                           offsets[(uint64_t)k * S + m]);
+    sink.acc = 0;
+    sink.nacc = 0;
+    sink.count = 0;
+    sink.cap = nbytes;
+    sink.overflow = false;
+    RangeEncoder enc;
+    enc.low = 0;
+    enc.range = 0xFFFFFFFFu;
+    enc.cache = 0;
+    enc.nff = 0;
+    enc.have_cache = false;
+    enc.bad = false;
+
+    const uint16_t *x = kv + ((uint64_t)row * T + c.first_token) * ld + c0 + lane;
+    const uint32_t n = c.n_tokens;
+    float ahat = 0.0f;
+    uint32_t g = 0;
+    for (uint32_t j = 0; j < n; ++j) {
+      const float v = h2f(x[(uint64_t)j * ld]);
+      uint32_t cs, f;
+      if (g == 0) {
+        const uint32_t qa = quant_anchor(v, lo, sa);
+        ahat = __builtin_fmaf((float)qa, sa, lo);
+        cs = ta[qa];
+        f = (uint32_t)ta[qa + 1] - cs;
+      } else {
+        const uint32_t s = (uint32_t)(quant_delta(v - ahat, dl, M) + M);
+        cs = td[s];
+        f = (uint32_t)td[s + 1] - cs;
+      }
+      g = g + 1 == d.G ? 0 : g + 1;
+      if (f == 0 || f > kTot) f = 1;  // damaged tables: already reported by the stats pass
+      enc.encode(cs, f, sink);
     }
-    g = g + 1 == d.G ? 0 : g + 1;
-    if (f == 0 || f > kTot) f = 1;  // damaged tables: already reported by the stats pass
-    enc.encode(cs, f, sink);
+    enc.finish(sink);
+    sink.flush();
+    if (enc.bad || sink.overflow || sink.count != nbytes)
+      set_status(status, KVC_ERR_CORRUPT_STREAM);
   }
-  enc.finish(sink);
-  sink.flush();
-  if (enc.bad || sink.overflow || sink.count != nbytes) set_status(status, KVC_ERR_CORRUPT_STREAM);
 }
 
 __global__ void k_encode_header(Desc d, const ChunkInfo *__restrict__ ci, uint32_t n_chunks,
@@ -316,24 +371,34 @@ hipError_t launch_index(const Desc &d, const ChunkInfo *dev_chunks, uint32_t n_c
                         uint64_t *payload, const uint8_t *tables, int check_header_flag,
                         int32_t *status, hipStream_t stream);
 
+size_t encode_lds_bytes(uint32_t levels) {
+  return sizeof(uint32_t) * ((size_t)kWave * kEA + (size_t)levels * kWave * kED);
+}
+
 // Stream-ordered encode sequence; dev_chunks already holds the chunk table
-// (records pointing into the workspace record array).
+// (records pointing into the workspace record array), `groups` the chunk
+// groups (contiguous ranges of it) and their level masks.
 hipError_t launch_encode(const Desc &d, const uint8_t *tables, const uint16_t *kv, uint32_t T,
-                         const ChunkInfo *dev_chunks, uint32_t n_chunks, uint8_t *records,
-                         uint64_t *row_sums, uint32_t *flags, uint32_t *offsets, uint8_t *valid,
-                         uint64_t *payload, uint64_t *chunk_off_ws, uint32_t *fits, uint8_t *out,
-                         uint64_t out_cap, uint64_t *chunk_off_out, int32_t *status,
-                         hipStream_t stream) {
-  const dim3 grid((d.C + kWave - 1) / kWave, 2u * d.L, n_chunks);
-  hipLaunchKernelGGL(k_encode_stats, grid, dim3(kWave), 0, stream, d, dev_chunks, tables, kv, T,
-                     records, status);
+                         const ChunkInfo *dev_chunks, uint32_t n_chunks,
+                         const DecodeGroup *groups, uint32_t n_groups, uint32_t levels,
+                         uint32_t waves, uint8_t *records, uint64_t *row_sums, uint32_t *flags,
+                         uint32_t *offsets, uint8_t *valid, uint64_t *payload,
+                         uint64_t *chunk_off_ws, uint32_t *fits, uint8_t *out, uint64_t out_cap,
+                         uint64_t *chunk_off_out, int32_t *status, hipStream_t stream) {
+  const uint32_t ncb = (d.C + kWave - 1) / kWave;
+  const uint32_t n_units = 2u * d.L * ncb;
+  const uint64_t blocks = (uint64_t)((n_units + kXcds - 1) / kXcds) * kXcds * n_groups;
+  const size_t lds = encode_lds_bytes(levels);
+  hipLaunchKernelGGL(k_encode_stats, dim3((uint32_t)blocks), dim3(waves * kWave), lds, stream, d,
+                     dev_chunks, groups, n_groups, n_units, tables, kv, T, records, status);
   hipError_t e = launch_index(d, dev_chunks, n_chunks, row_sums, flags, offsets, valid, payload,
                               tables, 0, status, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_encode_layout, dim3(1), dim3(64), 0, stream, d, n_chunks, payload,
                      chunk_off_ws, chunk_off_out, out_cap, fits, status);
-  hipLaunchKernelGGL(k_encode_emit, grid, dim3(kWave), 0, stream, d, dev_chunks, tables, kv, T,
-                     records, offsets, chunk_off_ws, fits, out, status);
+  hipLaunchKernelGGL(k_encode_emit, dim3((uint32_t)blocks), dim3(waves * kWave), lds, stream, d,
+                     dev_chunks, groups, n_groups, n_units, tables, kv, T, records, offsets,
+                     chunk_off_ws, fits, out, status);
   hipLaunchKernelGGL(k_encode_header, dim3(1), dim3(256), 0, stream, d, dev_chunks, n_chunks,
                      tables, payload, chunk_off_ws, fits, out);
   return hipGetLastError();

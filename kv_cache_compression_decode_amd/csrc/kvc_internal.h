@@ -63,6 +63,8 @@ static_assert(sizeof(DecodeGroup) == 16, "DecodeGroup layout");
 // Decode workgroups have at most this many waves; a wave takes the group's
 // chunks two at a time.
 constexpr uint32_t kDecodeMaxWaves = 8;
+// Encode workgroups have at most this many waves (one chunk each at a time).
+constexpr uint32_t kEncodeMaxWaves = 8;
 // LDS per decode workgroup that still lets two of them share a CU.
 constexpr uint32_t kDecodeLdsBudget = 80u * 1024u;
 
