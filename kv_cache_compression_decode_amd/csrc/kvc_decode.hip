@@ -81,6 +81,7 @@ struct Stream {
   uint32_t code, range;
   uint32_t rposb;       // bits consumed (a multiple of 8)
   uint32_t wposb;       // bits written to the ring (a multiple of 64)
+  uint32_t wlimb;       // wposb - 16: past it fewer than 2 bytes are buffered
   uint32_t b0, b1;      // the 8 bytes at wposb / 8, loaded ahead (memory order)
   uint32_t n;
   uint32_t nbytes;
@@ -88,7 +89,7 @@ struct Stream {
   int32_t M;
   uint32_t dbase;       // LDS byte address of this lane's delta row 0
   uint32_t dbaseM;      // dbase + M rows: (addr - dbaseM) >> 7 is q = s - M
-  float lo, sa, dl, ahat;
+  float lo, sa7, dl7, ahat;  // sa7 = sa / 128, dl7 = dl / 128 (exact)
 
   __device__ inline void load_block(__amdgpu_buffer_rsrc_t src) {
     const auto v = __builtin_amdgcn_raw_buffer_load_b64(src, voff + (wposb >> 3), 0, 0);
@@ -104,6 +105,7 @@ struct Stream {
     ring[h + 1] = b1;
     if (h == 0) ring[4] = b0;
     wposb += 64;
+    wlimb += 64;
     load_block(src);
   }
   // At a group's anchor: top the ring up if at most 8 bytes are left.
@@ -113,9 +115,14 @@ struct Stream {
   // Before every token: the next symbol's (at most 2) bytes must be in the
   // ring (rarely false).
   __device__ inline void ensure(__amdgpu_buffer_rsrc_t src) {
-    if (__builtin_expect(wposb - rposb < 16, 0)) write_block(src);
+    if (__builtin_expect(rposb > wlimb, 0)) write_block(src);
   }
 };
+
+// Keeps the instruction scheduler from moving code across this point, so that
+// the LDS reads of a lane's streams are issued back to back and waited for
+// together rather than one after the other.
+#define PAIR_BARRIER() __builtin_amdgcn_sched_barrier(0)
 
 // One token of Q streams of a lane, in lockstep: range decode, dequantize.
 // The symbol is the largest k with r * cum[k] <= code (the division-free form
@@ -143,25 +150,31 @@ __device__ inline void step(Stream *st, uint32_t abase, uint32_t *v) {
     uint32_t probe[Q];
 #pragma unroll
     for (uint32_t q = 0; q < Q; ++q) probe[q] = lds_read_u16(a[q] + sz * kRowBytes);
+    PAIR_BARRIER();
 #pragma unroll
     for (uint32_t q = 0; q < Q; ++q)
       if (__umul24(r[q], probe[q]) <= st[q].code) a[q] += sz * kRowBytes;
+    PAIR_BARRIER();
   }
+  uint32_t csv[Q], cnv[Q];
+#pragma unroll
+  for (uint32_t q = 0; q < Q; ++q) {
+    csv[q] = lds_read_u16(a[q]);
+    cnv[q] = lds_read_u16(a[q] + kRowBytes);
+  }
+  PAIR_BARRIER();
 #pragma unroll
   for (uint32_t q = 0; q < Q; ++q) {
     Stream &x = st[q];
-    const uint32_t cs = lds_read_u16(a[q]);
-    const uint32_t cn = lds_read_u16(a[q] + kRowBytes);
-    uint32_t sym;
-    int32_t qd = 0;
+    const uint32_t cs = csv[q], cn = cnv[q];
+    int32_t xq;  // 128 (symbol - M) for deltas, 128 symbol for anchors
     if constexpr (kAnchor) {
-      sym = (a[q] - abase) >> 7;
+      xq = (int32_t)(a[q] - abase);
       // a code at or past r * 2^15 has no symbol
       if (x.code >= (r[q] << kPrec)) x.tor = 0x7FFFFFFF;
     } else {
-      qd = (int32_t)(a[q] - x.dbaseM) >> 7;
-      sym = (uint32_t)(qd + x.M);
-      x.tor = qd > x.tor ? qd : x.tor;
+      xq = (int32_t)(a[q] - x.dbaseM);
+      x.tor = xq > x.tor ? xq : x.tor;
     }
     // 24-bit multiplies: r < 2^17 and staged cumulative counts <= 2^15
     x.code -= __umul24(r[q], cs);
@@ -169,17 +182,23 @@ __device__ inline void step(Stream *st, uint32_t abase, uint32_t *v) {
     // whole bytes to shift in: 0, 1 or 2 (range >= 2^9 for a valid stream)
     const uint32_t sh = ffbh(range) & 24u;
     x.range = range << sh;
-    x.code = (x.code << sh) | (in[q] >> ((16 - sh) & 31));
+    // code << sh with the next sh / 8 stream bytes below it, as one byte
+    // permute whose selector is a window sliding over the byte indices
+    // 07 06 05 04 (code, most significant first) 01 00 (the next two bytes)
+    const uint32_t sel = __builtin_amdgcn_alignbit(0x706u, 0x05040100u, (16 - sh) & 31);
+    x.code = __builtin_amdgcn_perm(x.code, in[q], sel);
     x.rposb += sh;
     if constexpr (kSymbols) {
-      v[q] = sym;
+      v[q] = kAnchor ? (uint32_t)xq >> 7 : (uint32_t)((xq >> 7) + x.M);
     } else {
       float y;
+      // 128 q is exact in binary32 and (128 q)(dl / 128) = q dl exactly, so
+      // this is the single rounding of fma(q, dl, ahat)
       if constexpr (kAnchor) {
-        x.ahat = __builtin_fmaf((float)sym, x.sa, x.lo);
+        x.ahat = __builtin_fmaf((float)xq, x.sa7, x.lo);
         y = x.ahat;
       } else {
-        y = __builtin_fmaf((float)qd, x.dl, x.ahat);
+        y = __builtin_fmaf((float)xq, x.dl7, x.ahat);
       }
       v[q] = f2h(y);
     }
@@ -353,11 +372,14 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
       steps = b > steps ? b : steps;
       s.M = (1 << (b - 1)) - 1;
       s.dbaseM = s.dbase + (uint32_t)s.M * kRowBytes;
-      s.tor = -s.M;
+      s.tor = -(int32_t)(s.M * kRowBytes);
       const uint32_t *rec = reinterpret_cast<const uint32_t *>(c.records + (uint64_t)m * kRecBytes);
       s.lo = __builtin_bit_cast(float, rec[0]);
-      s.sa = __builtin_bit_cast(float, rec[1]);
-      s.dl = __builtin_bit_cast(float, rec[2]);
+      // sa / 128 and dl / 128 are exact: sa is 0 or at least 2^-24 / 255 (a
+      // binary16 difference), dl is 0 or above 2^-70 (a difference of a
+      // binary16 value and an anchor on a 2^-55 grid), far from subnormals
+      s.sa7 = __builtin_bit_cast(float, rec[1]) * 0.0078125f;
+      s.dl7 = __builtin_bit_cast(float, rec[2]) * 0.0078125f;
       s.nbytes = rec[3];
       s.voff = (uint32_t)(kHdrBytes + (uint64_t)kRecBytes * S) + offsets[(uint64_t)k * S + m];
       s.n = c.n_tokens;
@@ -374,6 +396,7 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
       s.ring[3] = v[3];
       s.ring[4] = v[0];
       s.wposb = 128;
+      s.wlimb = 128 - 16;
       s.load_block(src[q]);
       s.code = bswap32(v[0]);
       s.rposb = 32;
@@ -423,7 +446,8 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
     }
 #pragma unroll
     for (uint32_t q = 0; q < kSlots; ++q)
-      if (active[q] && (st[q].tor > st[q].M || st[q].rposb != 8 * st[q].nbytes))
+      if (active[q] &&
+          (st[q].tor > (int32_t)(st[q].M * kRowBytes) || st[q].rposb != 8 * st[q].nbytes))
         set_status(status, KVC_ERR_CORRUPT_STREAM);
   }
 }
