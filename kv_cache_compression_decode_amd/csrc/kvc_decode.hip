@@ -210,7 +210,10 @@ __device__ inline void put(gbyte *base, uint32_t lane, uint32_t v) {
   if constexpr (kSymbols)
     base[lane] = (uint8_t)v;
   else
-    ((__attribute__((address_space(1))) uint16_t *)base)[lane] = (uint16_t)v;
+    // streaming store: the kernel never reads its output back, so the rows
+    // should not displace the stream blocks the lanes are still reading
+    __builtin_nontemporal_store((uint16_t)v,
+                                &((__attribute__((address_space(1))) uint16_t *)base)[lane]);
 }
 
 // Wave-uniform 64-bit pointer (kept in scalar registers).
