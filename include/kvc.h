@@ -132,8 +132,16 @@ uint64_t kvc_encode_ws_bytes(const kvc_codec_desc *d, uint32_t T);
  * container; containers are written back to back into `out` (device,
  * out_cap bytes) and chunk_offsets_out (device, n_chunks + 1 u64) receives
  * each container's start offset and, last, the total size.
+ * Each container's payload holds, per unit of up to 64 consecutive streams
+ * of one (layer, K/V) row, the streams' 8-byte blocks in the order in which
+ * the decoder's 64 lanes ask for them while decoding (so that one wave's
+ * requests are consecutive bytes); a stream's block padding is zero.
  * Device errors: KVC_ERR_NONFINITE, KVC_ERR_CAPACITY (out_cap too small; the
- * offsets are still written, `out` is not).
+ * offsets are still written, `out` is not), KVC_ERR_UNIMPLEMENTED (the
+ * decoder would ask for more than 16 of one stream's blocks before the
+ * encoder has written them, the size of the encoder's per-lane block queue:
+ * only reachable when a pending carry holds back a run of about 90 0xFF
+ * bytes).
  */
 kvc_status kvc_encode(const kvc_codec_desc *d, const void *tables, const uint16_t *kv_fp16,
                       uint32_t T, const uint8_t *chunk_levels, uint8_t *out, uint64_t out_cap,
@@ -163,8 +171,9 @@ kvc_status kvc_decode(const kvc_codec_desc *d, const void *tables, const kvc_chu
  * The bitstream index alone: validates the containers' headers against the
  * tables and writes offsets_out (device, [n_chunks][2LC] u32): each stream's
  * byte offset from the start of its container's payload (exclusive prefix
- * sum of the 4-byte-padded stream lengths).  Used by kvc_decode; exported for
- * inspection and tests.
+ * sum of the stream lengths rounded up to 8-byte blocks; a unit's blocks
+ * start at the offset of its first stream).  Used by kvc_decode; exported
+ * for inspection and tests.
  */
 kvc_status kvc_decode_index(const kvc_codec_desc *d, const void *tables,
                             const kvc_chunk_ref *chunks, uint32_t n_chunks, uint32_t *offsets_out,

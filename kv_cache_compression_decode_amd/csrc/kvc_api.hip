@@ -95,7 +95,7 @@ WsLayout ws_layout(const Desc &d, uint32_t K, bool encode) {
 
 uint64_t container_bound_n(const Desc &d, uint32_t n) {
   const uint64_t S = n_streams(d);
-  return kHdrBytes + kRecBytes * S + S * pad4(4ull + 2ull * n);
+  return kHdrBytes + kRecBytes * S + S * pad8(4ull + 2ull * n);
 }
 
 kvc_status hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
@@ -299,7 +299,7 @@ kvc_status kvc_encode(const kvc_codec_desc *dd, const void *tables, const uint16
   const uint32_t K = (uint32_t)K64;
   const uint64_t S = n_streams(d);
   // every stream offset inside a chunk's payload is a u32
-  if (S * pad4(4ull + 2ull * d.chunk) > 0xFFFFFFFFull) return KVC_ERR_SHAPE;
+  if (S * pad8(4ull + 2ull * d.chunk) > 0xFFFFFFFFull) return KVC_ERR_SHAPE;
   const WsLayout w = ws_layout(d, K, true);
   if (ws_bytes < w.total) return KVC_ERR_CAPACITY;
   uint8_t *base = static_cast<uint8_t *>(ws);

@@ -31,10 +31,16 @@
 //  * stream bytes are staged per lane in a 16-byte LDS ring fed in 8-byte
 //    blocks: a lane stores the block it loaded earlier only when its ring
 //    runs low (at most 8 bytes left at a group's anchor, fewer than 2 before
-//    any other token) and then issues the load of the next one, so a load has
-//    about a group of tokens to arrive.  Loads go through a buffer resource
-//    bounded by the container size, so the block after a stream's last byte
-//    may be loaded unconditionally (past the container end it reads as zero);
+//    any other token) and then asks for its next one, so a load has about a
+//    group of tokens to arrive;
+//  * the container holds each unit's blocks in exactly that order of
+//    requests (lanes in order within a step), so the wave keeps one
+//    wave-uniform count of the unit's blocks handed out, a lane's block is
+//    that count plus the requesting lanes below it, and a wave's loads walk
+//    its unit's payload front to back: each payload byte is fetched from HBM
+//    about once.  Loads go through a buffer resource bounded by the
+//    container size, so a load for a lane that has no block left is
+//    harmless (past the container end it reads as zero);
 //  * blocks are numbered so that the groups of one (row, channel block) run
 //    on the same XCD.
 #include "kvc_internal.h"
@@ -75,49 +81,72 @@ __device__ inline uint32_t lds_read_u16(uint32_t addr) {
   return *(const lds_u16 *)(uintptr_t)addr;
 }
 
+// A stream slot's container (all wave-uniform): its bounds-checked buffer
+// resource, the byte offset of this unit's payload in it, and how many of the
+// unit's payload blocks the wave has asked for so far.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct Source {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t ubase;
+  uint32_t cnt;
+};
+
 struct Stream {
-  uint32_t voff;        // byte offset of the stream in its container
   lds_u32 *ring;        // this lane's ring in LDS (16 bytes + 4 mirrored)
   uint32_t code, range;
   uint32_t rposb;       // bits consumed (a multiple of 8)
-  uint32_t wposb;       // bits written to the ring (a multiple of 64)
-  uint32_t wlimb;       // wposb - 16: past it fewer than 2 bytes are buffered
-  uint32_t b0, b1;      // the 8 bytes at wposb / 8, loaded ahead (memory order)
+  uint32_t wlimb;       // bits written to the ring (a multiple of 64), less
+                        // 16: past it fewer than 2 bytes are buffered
+  u32x2 held;           // the stream's next 8-byte block, loaded ahead (one
+                        // aligned register pair, the load's own destination)
+  uint32_t rem;         // the stream's blocks the lane has not asked for
+  uint32_t hpos;        // payload block number of the held block
   uint32_t n;
-  uint32_t nbytes;
   int32_t tor;          // largest delta q seen (> M flags a corrupt stream)
   int32_t M;
   uint32_t dbase;       // LDS byte address of this lane's delta row 0
   uint32_t dbaseM;      // dbase + M rows: (addr - dbaseM) >> 7 is q = s - M
   float lo, sa7, dl7, ahat;  // sa7 = sa / 128, dl7 = dl / 128 (exact)
 
-  __device__ inline void load_block(__amdgpu_buffer_rsrc_t src) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(src, voff + (wposb >> 3), 0, 0);
-    b0 = v[0];
-    b1 = v[1];
-  }
-  // Store the block loaded earlier into the free half of the ring and load
-  // the next one.  Only the rings that run low do this, and as late as
-  // possible, so that a block has had about a group of tokens to arrive.
-  __device__ inline void write_block(__amdgpu_buffer_rsrc_t src) {
-    const uint32_t h = (wposb >> 5) & 2;  // dword 0 or 2
-    ring[h] = b0;
-    ring[h + 1] = b1;
-    if (h == 0) ring[4] = b0;
-    wposb += 64;
+  // The held block into the free half of the ring.
+  __device__ inline void put_block() {
+    const uint32_t h = ((wlimb + 16) >> 5) & 2;  // dword 0 or 2
+    ring[h] = held[0];
+    ring[h + 1] = held[1];
+    if (h == 0) ring[4] = held[0];
     wlimb += 64;
-    load_block(src);
-  }
-  // At a group's anchor: top the ring up if at most 8 bytes are left.
-  __device__ inline void refill(__amdgpu_buffer_rsrc_t src) {
-    if (wposb - rposb <= 64) write_block(src);
-  }
-  // Before every token: the next symbol's (at most 2) bytes must be in the
-  // ring (rarely false).
-  __device__ inline void ensure(__amdgpu_buffer_rsrc_t src) {
-    if (__builtin_expect(rposb > wlimb, 0)) write_block(src);
   }
 };
+
+// The reading rule that fixes the payload's block order: the lanes with
+// `need` store their held block into the ring and ask for their next block,
+// if the stream has one; the unit's requests take consecutive payload blocks
+// in lane order.  Only rings that run low do this, as late as possible, so a
+// block has about a group of tokens to arrive before it is stored.
+//
+// Once any lane of the wave needs a block, every lane loads one: a lane that
+// stores its block takes the next (a lane whose stream has none left loads
+// some other block, or zeros past the container end, and never uses it), the
+// others load their held block again.  No lane keeps its old register value
+// across the branch, so nothing has to wait for the load before the block is
+// stored, a group later.
+__device__ inline void advance(Stream &s, Source &src, bool need) {
+  if (__builtin_amdgcn_ballot_w64(need) == 0) return;
+  const bool req = need && s.rem != 0;
+  const uint64_t mask = __builtin_amdgcn_ballot_w64(req);
+  if (need) s.put_block();
+  const uint32_t pos = src.cnt + lanes_below(mask);
+  s.hpos = need ? pos : s.hpos;
+  s.held = __builtin_amdgcn_raw_buffer_load_b64(src.rsrc, src.ubase + s.hpos * kBlock, 0, 0);
+  s.rem -= req ? 1u : 0u;
+  src.cnt += (uint32_t)__builtin_popcountll(mask);
+}
+// At a group's anchor: a ring with at most 8 bytes left takes its block.
+__device__ inline void refill(Stream &s, Source &src) { advance(s, src, s.rposb + 48 >= s.wlimb); }
+// Before every other token: a ring with fewer than 2 bytes left takes its
+// block (rare).
+__device__ inline void ensure(Stream &s, Source &src) { advance(s, src, s.rposb > s.wlimb); }
 
 // Keeps the instruction scheduler from moving code across this point, so that
 // the LDS reads of a lane's streams are issued back to back and waited for
@@ -226,11 +255,11 @@ __device__ inline gbyte *uniform_ptr(gbyte *p) {
 
 // The `count` delta tokens of one group, both streams.
 template <bool kSymbols, uint32_t kSteps>
-__device__ inline void delta_run(Stream *st, uint32_t abase, const __amdgpu_buffer_rsrc_t *src,
+__device__ inline void delta_run(Stream *st, uint32_t abase, Source *src,
                                  gbyte **ob, uint64_t ld, uint32_t lane, uint32_t count) {
   for (uint32_t i = 0; i < count; ++i) {
-    st[0].ensure(src[0]);
-    st[1].ensure(src[1]);
+    ensure(st[0], src[0]);
+    ensure(st[1], src[1]);
     uint32_t v[2];
     step<2, kSymbols, false, kSteps>(st, abase, v);
     put<kSymbols>(ob[0], lane, v[0]);
@@ -241,9 +270,8 @@ __device__ inline void delta_run(Stream *st, uint32_t abase, const __amdgpu_buff
 }
 
 template <bool kSymbols>
-__device__ inline void delta_dispatch(uint32_t steps, Stream *st, uint32_t abase,
-                                      const __amdgpu_buffer_rsrc_t *src, gbyte **ob, uint64_t ld,
-                                      uint32_t lane, uint32_t count) {
+__device__ inline void delta_dispatch(uint32_t steps, Stream *st, uint32_t abase, Source *src,
+                                      gbyte **ob, uint64_t ld, uint32_t lane, uint32_t count) {
   switch (steps) {
     case 2: delta_run<kSymbols, 2>(st, abase, src, ob, ld, lane, count); break;
     case 3: delta_run<kSymbols, 3>(st, abase, src, ob, ld, lane, count); break;
@@ -350,7 +378,7 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
   for (uint32_t pair = wave; pair < npairs; pair += n_waves) {
     Stream st[kSlots];
     gbyte *ob[kSlots];  // wave-uniform output row of the current token
-    __amdgpu_buffer_rsrc_t src[kSlots];
+    Source src[kSlots];
     uint32_t steps = 2;
     bool active[kSlots];
 #pragma unroll
@@ -366,7 +394,11 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
       ob[q] = (gbyte *)out;
       s.dbase = lds_addr(sD) + 2 * lane;
       s.dbaseM = s.dbase;
-      src[q] = __builtin_amdgcn_make_buffer_rsrc((void *)ci[k].cont, (short)0, 0, kBufferWord3);
+      s.rem = 0;
+      s.hpos = 0;
+      src[q].rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)ci[k].cont, (short)0, 0, kBufferWord3);
+      src[q].ubase = 0;
+      src[q].cnt = 0;
       if (!active[q]) continue;
       const ChunkInfo c = ci[k];
       const uint32_t lslot = __builtin_popcount(level_mask & ((1u << c.level) - 1u));
@@ -383,25 +415,39 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
       // binary16 value and an anchor on a 2^-55 grid), far from subnormals
       s.sa7 = __builtin_bit_cast(float, rec[1]) * 0.0078125f;
       s.dl7 = __builtin_bit_cast(float, rec[2]) * 0.0078125f;
-      s.nbytes = rec[3];
-      s.voff = (uint32_t)(kHdrBytes + (uint64_t)kRecBytes * S) + offsets[(uint64_t)k * S + m];
+      const uint32_t nblk = (uint32_t)(pad8(rec[3]) / kBlock);
       s.n = c.n_tokens;
-      // containers are below 2^32 bytes (checked on the host)
-      src[q] = __builtin_amdgcn_make_buffer_rsrc((void *)c.cont, (short)0,
-                                                 (int)(uint32_t)c.cont_bytes, kBufferWord3);
+      // containers are below 2^32 bytes (checked on the host); this unit's
+      // payload starts at its first stream's block offset
+      src[q].rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)c.cont, (short)0,
+                                                      (int)(uint32_t)c.cont_bytes, kBufferWord3);
+      src[q].ubase = (uint32_t)(kHdrBytes + (uint64_t)kRecBytes * S) + offsets[(uint64_t)k * S + m0];
       ob[q] = uniform_ptr((gbyte *)out + (((uint64_t)row * T_total + c.first_token) * d.C + c0) * esz);
       s.ahat = 0.0f;
-      // prime the ring with 16 bytes and start loading the next 8
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(src[q], s.voff, 0, 0);
-      s.ring[0] = v[0];
-      s.ring[1] = v[1];
-      s.ring[2] = v[2];
-      s.ring[3] = v[3];
-      s.ring[4] = v[0];
-      s.wposb = 128;
+      // start of the reading rule: every lane asks for its blocks 0, 1 and 2
+      // (block outer, lane inner); 0 and 1 fill the ring, 2 is held.  A lane
+      // without the block loads some other block and never uses it.
+      uint32_t blk[3][2];
+#pragma unroll
+      for (uint32_t b = 0; b < 3; ++b) {
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(b < nblk);
+        const uint32_t pos = src[q].cnt + lanes_below(mask);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(src[q].rsrc, src[q].ubase + pos * kBlock, 0, 0);
+        blk[b][0] = v[0];
+        blk[b][1] = v[1];
+        if (b == 2) s.hpos = pos;
+        src[q].cnt += (uint32_t)__builtin_popcountll(mask);
+      }
+      s.rem = nblk < 3 ? 0u : nblk - 3;
+      s.ring[0] = blk[0][0];
+      s.ring[1] = blk[0][1];
+      s.ring[2] = blk[1][0];
+      s.ring[3] = blk[1][1];
+      s.ring[4] = blk[0][0];
+      s.held[0] = blk[2][0];
+      s.held[1] = blk[2][1];
       s.wlimb = 128 - 16;
-      s.load_block(src[q]);
-      s.code = bswap32(v[0]);
+      s.code = bswap32(blk[0][0]);
       s.rposb = 32;
       s.range = 0xFFFFFFFFu;
     }
@@ -414,8 +460,8 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
     uint32_t j = 0;
     while (j < nmin) {
       // after a refill at least 8 bytes are buffered: no check for the anchor
-      st[0].refill(src[0]);
-      st[1].refill(src[1]);
+      refill(st[0], src[0]);
+      refill(st[1], src[1]);
       {
         uint32_t v[2];
         step<2, kSymbols, true, 8>(st, abase, v);
@@ -437,9 +483,9 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
       for (uint32_t q = 0; q < kSlots; ++q) {
         if (j < st[q].n) {
           if (anchor)
-            st[q].refill(src[q]);
+            refill(st[q], src[q]);
           else
-            st[q].ensure(src[q]);
+            ensure(st[q], src[q]);
           uint32_t v;
           single_step<kSymbols>(steps, anchor, &st[q], abase, &v);
           put<kSymbols>(ob[q], lane, v);
@@ -447,11 +493,16 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
         }
       }
     }
+    // a valid stream ends exactly at its last byte, with every block asked for
 #pragma unroll
-    for (uint32_t q = 0; q < kSlots; ++q)
-      if (active[q] &&
-          (st[q].tor > (int32_t)(st[q].M * kRowBytes) || st[q].rposb != 8 * st[q].nbytes))
+    for (uint32_t q = 0; q < kSlots; ++q) {
+      if (!active[q]) continue;
+      const uint32_t k = gp.start + 2 * pair + q;
+      const uint32_t nbytes =
+          reinterpret_cast<const uint32_t *>(ci[k].records + (uint64_t)m * kRecBytes)[3];
+      if (st[q].tor > (int32_t)(st[q].M * kRowBytes) || st[q].rposb != 8 * nbytes || st[q].rem != 0)
         set_status(status, KVC_ERR_CORRUPT_STREAM);
+    }
   }
 }
 

@@ -67,26 +67,57 @@ __device__ inline EncodeBlock encode_block(uint32_t n_groups) {
   return {(local / n_groups) * kXcds + id % kXcds, local % n_groups};
 }
 
-// Little-endian byte sink into 4-byte words, bounded by `cap` bytes.
-struct ByteSink {
-  uint32_t *wp;
-  uint32_t acc, nacc, count, cap;
-  bool overflow;
+// Entries of the per-lane queue of payload blocks asked for (by the reading
+// rule) but not yet written.  The queue holds the blocks between the last
+// byte written and the reader's position: about 5, plus one per 8 bytes the
+// range coder still holds back for a pending carry.
+constexpr uint32_t kQueue = 16;
+
+// Byte sink writing a stream's bytes, little-endian, in 8-byte blocks to the
+// payload blocks the reading rule gave them (queued in block order); at most
+// `cap` bytes.
+struct BlockSink {
+  uint8_t *pay;      // the unit's payload
+  uint32_t *queue;   // this lane's kQueue payload block numbers (LDS)
+  uint32_t cnt;      // blocks of the unit handed out so far (wave-uniform)
+  uint32_t head, tail;
+  uint32_t w0, w1, nacc, count, cap;
+  bool overflow;     // more bytes than cap, or no block to write to
+  bool window;       // the queue ran full
+  __device__ inline void push(uint32_t blk) {
+    if (tail - head >= kQueue) {
+      window = true;
+      return;
+    }
+    queue[tail % kQueue] = blk;
+    ++tail;
+  }
+  __device__ inline void emit() {
+    const uint32_t blk = head == tail ? cnt : queue[head % kQueue];
+    if (blk >= cnt) {
+      overflow = true;  // no block asked for: never write past those handed out
+    } else {
+      uint32_t *dst = reinterpret_cast<uint32_t *>(pay + (uint64_t)blk * kBlock);
+      ++head;
+      dst[0] = w0;
+      dst[1] = w1;
+    }
+    w0 = w1 = nacc = 0;
+  }
   __device__ inline void put(uint32_t b) {
     if (count >= cap) {
       overflow = true;
       return;
     }
-    acc |= (b & 0xFFu) << (8 * nacc);
+    if (nacc < 4)
+      w0 |= (b & 0xFFu) << (8 * nacc);
+    else
+      w1 |= (b & 0xFFu) << (8 * (nacc - 4));
     ++count;
-    if (++nacc == 4) {
-      *wp++ = acc;
-      acc = 0;
-      nacc = 0;
-    }
+    if (++nacc == kBlock) emit();
   }
   __device__ inline void flush() {
-    if (nacc) *wp = acc;  // the rest of the word is zero padding
+    if (nacc) emit();  // the rest of the block is zero padding
   }
 };
 
@@ -99,7 +130,7 @@ struct RangeEncoder {
   bool have_cache;
   bool bad;
 
-  __device__ inline void shift_low(ByteSink &out) {
+  __device__ inline void shift_low(BlockSink &out) {
     const uint32_t top = (uint32_t)(low >> 24);  // 9 bits: carry in bit 8
     if (top != 0xFFu) {
       const uint32_t carry = top >> 8;
@@ -120,17 +151,21 @@ struct RangeEncoder {
     low = (low & 0x00FFFFFFull) << 8;
   }
 
-  __device__ inline void encode(uint32_t cum, uint32_t f, ByteSink &out) {
+  // Encodes one symbol; returns the bytes the decoder shifts in for it.
+  __device__ inline uint32_t encode(uint32_t cum, uint32_t f, BlockSink &out) {
     const uint32_t r = range >> kPrec;
     low += (uint64_t)r * cum;
     range = r * f;
+    uint32_t k = 0;
     while (range < (1u << 24)) {
       shift_low(out);
       range <<= 8;
+      ++k;
     }
+    return k;
   }
 
-  __device__ inline void finish(ByteSink &out) {
+  __device__ inline void finish(BlockSink &out) {
     for (int i = 0; i < 4; ++i) shift_low(out);
     if (have_cache) {
       out.put(cache);
@@ -254,6 +289,8 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
   extern __shared__ uint32_t lds_raw[];
   uint32_t *sA = lds_raw;
   uint32_t *sD = sA + kWave * kEA;
+  // after the models: each lane's queue of payload block numbers
+  uint32_t *queues = reinterpret_cast<uint32_t *>(sD + __builtin_popcount(gp.level) * kWave * kED);
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const uint32_t n_waves = blockDim.x / kWave;
@@ -292,14 +329,18 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
     rout[2] = rin[2];
     rout[3] = nbytes;
 
-    ByteSink sink;
-    sink.wp = reinterpret_cast<uint32_t *>(cont + kHdrBytes + (uint64_t)kRecBytes * S +
-                                           offsets[(uint64_t)k * S + m]);
-    sink.acc = 0;
-    sink.nacc = 0;
+    const uint32_t nblk = (uint32_t)(pad8(nbytes) / kBlock);
+    BlockSink sink;
+    // this unit's payload starts at its first stream's block offset
+    sink.pay = cont + kHdrBytes + (uint64_t)kRecBytes * S + offsets[(uint64_t)k * S + m0];
+    sink.queue = queues + (wave * kWave + lane) * kQueue;
+    sink.cnt = 0;
+    sink.head = sink.tail = 0;
+    sink.w0 = sink.w1 = sink.nacc = 0;
     sink.count = 0;
     sink.cap = nbytes;
     sink.overflow = false;
+    sink.window = false;
     RangeEncoder enc;
     enc.low = 0;
     enc.range = 0xFFFFFFFFu;
@@ -308,11 +349,43 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
     enc.have_cache = false;
     enc.bad = false;
 
+    // The decoder's reading rule, run alongside: R bytes consumed by the
+    // decoder, W bytes it holds, q its next block to ask for; the unit's
+    // requests take consecutive payload blocks in lane order (cnt is
+    // wave-uniform).  Start: blocks 0, 1, 2 of every lane.
+    uint32_t cnt = 0, R = 4, W = 16, q = 0;
+#pragma unroll
+    for (uint32_t blk = 0; blk < 3; ++blk) {
+      const bool req = blk < nblk;
+      const uint64_t mask = __builtin_amdgcn_ballot_w64(req);
+      if (req) {
+        sink.push(cnt + lanes_below(mask));
+        ++q;
+      }
+      cnt += (uint32_t)__builtin_popcountll(mask);
+    }
+    sink.cnt = cnt;
+
     const uint16_t *x = kv + ((uint64_t)row * T + c.first_token) * ld + c0 + lane;
     const uint32_t n = c.n_tokens;
     float ahat = 0.0f;
     uint32_t g = 0;
     for (uint32_t j = 0; j < n; ++j) {
+      // before token j: a reader ring with at most 8 bytes (anchor) or fewer
+      // than 2 bytes (other tokens) takes its next block and asks for one
+      {
+        const uint32_t ahead = W - R;
+        const bool need = g == 0 ? ahead <= 8u : ahead < 2u;
+        const bool req = need && q < nblk;
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(req);
+        if (req) {
+          sink.push(cnt + lanes_below(mask));
+          ++q;
+        }
+        if (need) W += kBlock;
+        cnt += (uint32_t)__builtin_popcountll(mask);
+        sink.cnt = cnt;
+      }
       const float v = h2f(x[(uint64_t)j * ld]);
       uint32_t cs, f;
       if (g == 0) {
@@ -327,12 +400,17 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
       }
       g = g + 1 == d.G ? 0 : g + 1;
       if (f == 0 || f > kTot) f = 1;  // damaged tables: already reported by the stats pass
-      enc.encode(cs, f, sink);
+      R += enc.encode(cs, f, sink);
     }
     enc.finish(sink);
     sink.flush();
-    if (enc.bad || sink.overflow || sink.count != nbytes)
+    if (sink.window) {
+      // a run of pending carry bytes longer than the block queue
+      set_status(status, KVC_ERR_UNIMPLEMENTED);
+    } else if (enc.bad || sink.overflow || sink.count != nbytes || q != nblk ||
+               sink.head != sink.tail) {
       set_status(status, KVC_ERR_CORRUPT_STREAM);
+    }
   }
 }
 
@@ -389,6 +467,7 @@ hipError_t launch_encode(const Desc &d, const uint8_t *tables, const uint16_t *k
   const uint32_t n_units = 2u * d.L * ncb;
   const uint64_t blocks = (uint64_t)((n_units + kXcds - 1) / kXcds) * kXcds * n_groups;
   const size_t lds = encode_lds_bytes(levels);
+  const size_t lds_emit = lds + sizeof(uint32_t) * (size_t)waves * kWave * kQueue;
   hipLaunchKernelGGL(k_encode_stats, dim3((uint32_t)blocks), dim3(waves * kWave), lds, stream, d,
                      dev_chunks, groups, n_groups, n_units, tables, kv, T, records, status);
   hipError_t e = launch_index(d, dev_chunks, n_chunks, row_sums, flags, offsets, valid, payload,
@@ -396,7 +475,7 @@ hipError_t launch_encode(const Desc &d, const uint8_t *tables, const uint16_t *k
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_encode_layout, dim3(1), dim3(64), 0, stream, d, n_chunks, payload,
                      chunk_off_ws, chunk_off_out, out_cap, fits, status);
-  hipLaunchKernelGGL(k_encode_emit, dim3((uint32_t)blocks), dim3(waves * kWave), lds, stream, d,
+  hipLaunchKernelGGL(k_encode_emit, dim3((uint32_t)blocks), dim3(waves * kWave), lds_emit, stream, d,
                      dev_chunks, groups, n_groups, n_units, tables, kv, T, records, offsets,
                      chunk_off_ws, fits, out, status);
   hipLaunchKernelGGL(k_encode_header, dim3(1), dim3(256), 0, stream, d, dev_chunks, n_chunks,

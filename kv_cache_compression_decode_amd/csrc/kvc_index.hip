@@ -1,6 +1,7 @@
-// Bitstream index: every (chunk, layer, K/V, channel) stream's payload
-// offset, as the exclusive prefix sum of the 4-byte-padded stream lengths in
-// (layer, K/V, channel) order, plus container header validation.
+// Bitstream index: every (chunk, layer, K/V, channel) stream's block offset,
+// the exclusive prefix sum of the stream lengths rounded up to whole 8-byte
+// blocks in (layer, K/V, channel) order (a unit's payload starts at its
+// first stream's offset), plus container header validation.
 //
 // Two launches over a (row = layer*2 + kv, chunk) grid:
 //   k_index_rows : per row, the sum of padded lengths (u64); the row-0 block
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(256) void k_index_rows(Desc d, const ChunkInfo *__r
   for (uint32_t ch = threadIdx.x; ch < d.C; ch += blockDim.x) {
     const uint32_t nb = ld_u32(rec + (uint64_t)ch * kRecBytes + 12);
     short_stream = short_stream || nb < 4u;
-    acc += pad4(nb);
+    acc += pad8(nb);
   }
   // block reduction
   __shared__ uint64_t red[256];
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(256) void k_index_scan(Desc d, const ChunkInfo *__r
   uint32_t *out = offsets + (uint64_t)k * S + (uint64_t)row * d.C;
   for (uint32_t t0 = 0; t0 < d.C; t0 += blockDim.x) {
     const uint32_t ch = t0 + threadIdx.x;
-    const uint64_t v = ch < d.C ? pad4(ld_u32(rec + (uint64_t)ch * kRecBytes + 12)) : 0;
+    const uint64_t v = ch < d.C ? pad8(ld_u32(rec + (uint64_t)ch * kRecBytes + 12)) : 0;
     const uint64_t incl = block_scan_incl(v, tmp);
     if (ch < d.C) out[ch] = (uint32_t)(running + incl - v);
     // the tile's total is the last thread's inclusive value

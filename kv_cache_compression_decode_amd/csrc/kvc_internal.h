@@ -3,9 +3,10 @@
 // Layouts (little-endian, all written and read only by this library and by
 // whoever follows the same published format):
 //   container  : 64-byte header, 2LC records of 16 bytes {f32 lo, f32 sa,
-//                f32 dl, u32 nbytes}, then the payload: the streams'
-//                bytes in (layer, K/V, channel) order, each zero-padded to a
-//                multiple of 4 bytes.
+//                f32 dl, u32 nbytes}, then the payload: per unit (one
+//                (layer, K/V) row and up to 64 consecutive channels), in
+//                unit order, the unit's streams' 8-byte blocks in the order
+//                the decoder's reading rule asks for them (kvc_decode.hip).
 //   tables blob: 128-byte header, anchor cumulative frequencies
 //                [2LC][ANCHOR_STRIDE] u16, delta cumulative frequencies
 //                [n_levels][2LC][DELTA_STRIDE] u16.
@@ -31,7 +32,8 @@ constexpr uint32_t kMaxChunksPerBatch = 64;
 
 constexpr uint32_t kContainerMagic = 0x3143564Bu;  // "KVC1"
 constexpr uint32_t kTablesMagic = 0x5443564Bu;     // "KVCT"
-constexpr uint32_t kFormatVersion = 1;
+constexpr uint32_t kFormatVersion = 2;  // containers: block-interleaved unit payloads
+constexpr uint32_t kTablesVersion = 1;
 
 // Per-chunk description kept in the workspace.
 struct ChunkInfo {
@@ -84,7 +86,11 @@ struct Desc {
 
 __host__ __device__ inline uint32_t third_of(uint32_t l, uint32_t L) { return (3u * l) / L; }
 __host__ __device__ inline uint32_t n_streams(const Desc &d) { return 2u * d.L * d.C; }
-__host__ __device__ inline uint64_t pad4(uint64_t v) { return (v + 3u) & ~uint64_t(3); }
+// Payload blocks: a stream's bytes are cut into 8-byte blocks (the last one
+// zero-padded); a unit (one row, up to 64 consecutive channels) stores its
+// streams' blocks in the order its reader asks for them.
+constexpr uint32_t kBlock = 8;
+__host__ __device__ inline uint64_t pad8(uint64_t v) { return (v + 7u) & ~uint64_t(7); }
 
 // 64-bit FNV-1a (Fowler / Noll / Vo), published offset basis and prime.
 constexpr uint64_t kFnvOffset = 0xcbf29ce484222325ull;
@@ -103,6 +109,12 @@ __host__ __device__ inline uint64_t fnv_u32(uint64_t h, uint32_t v) {
 __host__ __device__ inline uint64_t fnv_u64(uint64_t h, uint64_t v) {
   h = fnv_u32(h, (uint32_t)v);
   return fnv_u32(h, (uint32_t)(v >> 32));
+}
+
+// Rank of this lane among the set lanes of `mask` below it.
+__device__ inline uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
 // Record the first device-side error of a call.

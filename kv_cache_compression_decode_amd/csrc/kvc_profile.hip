@@ -159,7 +159,7 @@ __global__ void k_profile_final(Desc d, const uint64_t *__restrict__ row_hash,
   const uint64_t S = n_streams(d);
   uint32_t *w = reinterpret_cast<uint32_t *>(tables);
   w[0] = kTablesMagic;
-  w[1] = kFormatVersion;
+  w[1] = kTablesVersion;
   w[2] = d.L;
   w[3] = d.C;
   w[4] = d.G;

@@ -126,6 +126,10 @@ def _load():
     lib.orc_stream_offsets.argtypes = [vp, vp, u64, vp]
     lib.orc_decode_chunk.argtypes = [vp, vp, vp, u64, vp, u64, u32, u32, u32, vp, u32]
     lib.orc_decode_streams.argtypes = [vp, vp, vp, u64, vp, u64, vp, u32, vp, vp]
+    lib.orc_unit_order.argtypes = [vp, vp, vp, u64, vp, u64, u32, vp, u64, vp]
+    lib.orc_block_order_trace.argtypes = [u32, u32, u32, vp, vp, vp, u64]
+    lib.orc_block_order_trace.restype = i64
+    lib.orc_rc_shifts.argtypes = [vp, u64, u32, u32, vp, u32, vp, u32, vp]
     lib.orc_f2h_array.argtypes = [vp, vp, u64]
     lib.orc_h2f_array.argtypes = [vp, vp, u64]
     lib.orc_f2h_patterns.argtypes = [u32, u64, vp]
@@ -242,6 +246,34 @@ def rc_decode(data: bytes, n: int, fA: Sequence[int], fD: Optional[Sequence[int]
     return sym[:n]
 
 
+def rc_shifts(data: bytes, n: int, fA: Sequence[int], fD: Optional[Sequence[int]] = None,
+              group: int = 1) -> np.ndarray:
+    """Bytes shifted in by each decoded symbol (0..2): the decoder's
+    consumption trace that the reference reader of reading R17 follows."""
+    buf = np.frombuffer(data, np.uint8).copy() if len(data) else np.zeros(1, np.uint8)
+    a = np.ascontiguousarray(fA, np.uint32)
+    d = np.ascontiguousarray(fA if fD is None else fD, np.uint32)
+    k = np.zeros(max(n, 1), np.uint8)
+    st = _load().orc_rc_shifts(_p(buf), len(data), n, group, _p(a), len(a), _p(d), len(d), _p(k))
+    if st:
+        raise OracleError(st, "rc_shifts")
+    return k[:n]
+
+
+def block_order_trace(nblk: Sequence[int], shifts: np.ndarray, group: int) -> np.ndarray:
+    """Reading R17 on an explicit trace: slot order (lane << 16 | block) of a
+    unit whose lanes have nblk[l] blocks and shift counts shifts[l][j]."""
+    nb = np.ascontiguousarray(nblk, np.uint32)
+    k = np.ascontiguousarray(shifts, np.uint8)
+    nv, n = k.shape
+    cap = int(nb.sum()) + 1
+    order = np.zeros(cap, np.uint32)
+    r = _load().orc_block_order_trace(nv, n, group, _p(nb), _p(k), _p(order), cap)
+    if r < 0:
+        raise OracleError(int(r), "block_order_trace")
+    return order[:r]
+
+
 # -------------------------------------------------------------- the codec
 @dataclasses.dataclass
 class Tables:
@@ -341,6 +373,33 @@ def decode_streams(desc: Desc, tables: Tables, container: np.ndarray, ids: Seque
     if st:
         raise OracleError(st, "decode_streams")
     return vals, syms
+
+
+def unit_order(desc: Desc, tables: Tables, container: np.ndarray, unit: int):
+    """Slot order of one unit's payload (lane << 16 | block per slot), as the
+    reference reader of reading R17 reads it, and the unit's lane count."""
+    cap = 64 * (4 + 2 * desc.chunk_tokens) // 8 + 64
+    order = np.zeros(cap, np.uint32)
+    nv = np.zeros(1, np.uint32)
+    st = _load().orc_unit_order(_p(desc.words()), _p(tables.fA), _p(tables.fD),
+                                tables.profile_id, _p(container), len(container), unit,
+                                _p(order), cap, _p(nv))
+    if st:
+        raise OracleError(st, "unit_order")
+    m0, n_lanes = unit_streams(desc, unit)
+    nb = records(desc, container)["nbytes"][m0:m0 + n_lanes].astype(np.int64)
+    return order[:int(((nb + 7) // 8).sum())], int(nv[0])
+
+
+def n_units(desc: Desc) -> int:
+    return 2 * desc.n_layers * ((desc.n_channels + 63) // 64)
+
+
+def unit_streams(desc: Desc, unit: int) -> Tuple[int, int]:
+    """First stream and stream count of a unit (reading R6)."""
+    ncb = (desc.n_channels + 63) // 64
+    row, cb = divmod(unit, ncb)
+    return row * desc.n_channels + 64 * cb, min(64, desc.n_channels - 64 * cb)
 
 
 # ------------------------------------------------------ container parsing

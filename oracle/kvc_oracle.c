@@ -33,8 +33,12 @@
  *      emitted bytes and a 4-byte flush.
  *   R5 model normalisation: floor of 1 count per symbol, the remainder to the
  *      most frequent symbol (lowest index on ties).
- *   R6 container: 64-byte header, 16-byte record per stream, payload of the
- *      streams in (layer, K/V, channel) order, each padded to 4 bytes.
+ *   R6 container: 64-byte header, 16-byte record per stream, then the
+ *      payload of the units (a unit: one (layer, K/V) row and a block of up
+ *      to 64 consecutive channels) in (layer, K/V, channel block) order.
+ *   R17 a unit's payload holds its streams' bytes cut into 8-byte blocks (the
+ *      last one zero-padded), in the order in which the reference reader
+ *      (unit_reader below) asks for them.
  * Arithmetic: IEEE-754 binary32 with round-to-nearest-even, correctly
  * rounded division, true fused multiply-add, no flush-to-zero, no
  * contraction (build with -ffp-contract=off).
@@ -336,39 +340,76 @@ int64_t orc_rc_encode(const int32_t *sym, uint32_t n, uint32_t G, const uint32_t
 
 /* Decode n symbols from exactly nbytes bytes; any inconsistency is
  * reported as a corrupt stream. */
+/* The decoder as a state machine, one symbol per step (the reference reader
+ * of R17 interleaves the steps of several streams). */
+typedef struct {
+  uint32_t code, range;
+  uint64_t pos; /* bytes consumed */
+} rc_dec;
+
+static int rc_dec_init(rc_dec *d, const uint8_t *in, uint64_t nbytes) {
+  if (nbytes < 4) return ORC_ERR_CORRUPT;
+  d->code = ((uint32_t)in[0] << 24) | ((uint32_t)in[1] << 16) | ((uint32_t)in[2] << 8) |
+            (uint32_t)in[3];
+  d->range = 0xFFFFFFFFu;
+  d->pos = 4;
+  return ORC_OK;
+}
+
+static int rc_dec_step(rc_dec *d, const uint8_t *in, uint64_t nbytes, const uint32_t *f,
+                       uint32_t A, int32_t *sym) {
+  const uint32_t r = d->range >> PREC;
+  const uint32_t t = d->code / r;
+  if (t >= TOT) return ORC_ERR_CORRUPT;
+  /* linear search for the symbol whose interval holds t */
+  uint32_t s = 0, c = 0;
+  while (s < A && c + f[s] <= t) {
+    c += f[s];
+    ++s;
+  }
+  if (s >= A) return ORC_ERR_CORRUPT;
+  d->code -= r * c;
+  d->range = r * f[s];
+  *sym = (int32_t)s;
+  while (d->range < (1u << 24)) {
+    if (d->pos >= nbytes) return ORC_ERR_CORRUPT;
+    d->code = (d->code << 8) | in[d->pos++];
+    d->range <<= 8;
+  }
+  return ORC_OK;
+}
+
 int orc_rc_decode(const uint8_t *in, uint64_t nbytes, uint32_t n, uint32_t G,
                   const uint32_t *fA, uint32_t AA, const uint32_t *fD, uint32_t AD,
                   int32_t *sym) {
-  if (nbytes < 4) return ORC_ERR_CORRUPT;
-  uint32_t code = ((uint32_t)in[0] << 24) | ((uint32_t)in[1] << 16) | ((uint32_t)in[2] << 8) |
-                  (uint32_t)in[3];
-  uint32_t range = 0xFFFFFFFFu;
-  uint64_t pos = 4;
+  rc_dec d;
+  int st = rc_dec_init(&d, in, nbytes);
+  if (st) return st;
   for (uint32_t j = 0; j < n; ++j) {
     const int anchor = (j % G) == 0;
-    const uint32_t *f = anchor ? fA : fD;
-    const uint32_t A = anchor ? AA : AD;
-    const uint32_t r = range >> PREC;
-    const uint32_t t = code / r;
-    if (t >= TOT) return ORC_ERR_CORRUPT;
-    /* linear search for the symbol whose interval holds t */
-    uint32_t s = 0, c = 0;
-    while (s < A && c + f[s] <= t) {
-      c += f[s];
-      ++s;
-    }
-    if (s >= A) return ORC_ERR_CORRUPT;
-    code -= r * c;
-    range = r * f[s];
-    sym[j] = (int32_t)s;
-    while (range < (1u << 24)) {
-      if (pos >= nbytes) return ORC_ERR_CORRUPT;
-      code = (code << 8) | in[pos++];
-      range <<= 8;
-    }
+    st = rc_dec_step(&d, in, nbytes, anchor ? fA : fD, anchor ? AA : AD, &sym[j]);
+    if (st) return st;
   }
-  if (pos != nbytes) return ORC_ERR_CORRUPT;
+  if (d.pos != nbytes) return ORC_ERR_CORRUPT;
   return ORC_OK;
+}
+
+/* Bytes shifted in by each symbol of a stream (k[j] in 0..2), for checks of
+ * the reference reader; same arguments as orc_rc_decode. */
+int orc_rc_shifts(const uint8_t *in, uint64_t nbytes, uint32_t n, uint32_t G, const uint32_t *fA,
+                  uint32_t AA, const uint32_t *fD, uint32_t AD, uint8_t *k) {
+  rc_dec d;
+  int st = rc_dec_init(&d, in, nbytes);
+  if (st) return st;
+  for (uint32_t j = 0; j < n; ++j) {
+    const int anchor = (j % G) == 0;
+    const uint64_t before = d.pos;
+    int32_t s;
+    st = rc_dec_step(&d, in, nbytes, anchor ? fA : fD, anchor ? AA : AD, &s);
+    if (st) return st;
+    k[j] = (uint8_t)(d.pos - before);
+  }
+  return d.pos == nbytes ? ORC_OK : ORC_ERR_CORRUPT;
 }
 
 /* ---------------------------------------------------------- tables / ids */
@@ -520,19 +561,131 @@ static float get_f32(const uint8_t *b) {
   memcpy(&f, &u, 4);
   return f;
 }
-static uint64_t pad4(uint64_t v) { return (v + 3u) & ~(uint64_t)3u; }
+static uint64_t pad8(uint64_t v) { return (v + 7u) & ~(uint64_t)7u; }
 
 /* the container's upper size bound for n tokens: each symbol emits at most
- * two bytes, plus the 4-byte flush */
+ * two bytes, plus the 4-byte flush, rounded up to whole 8-byte blocks */
 uint64_t orc_container_bound(const uint32_t *pw, uint32_t n) {
   params p;
   if (read_params(pw, &p)) return 0;
   return HDR_BYTES + (uint64_t)REC_BYTES * n_streams(&p) +
-         (uint64_t)n_streams(&p) * pad4(4u + 2u * (uint64_t)n);
+         (uint64_t)n_streams(&p) * pad8(4u + 2u * (uint64_t)n);
 }
 
 static void widen_freqs(const uint16_t *src, uint32_t A, uint32_t *dst) {
   for (uint32_t s = 0; s < A; ++s) dst[s] = src[s];
+}
+
+/* ------------------------------------------------------------ units (R6) */
+#define UNIT_LANES 64u
+#define BLOCK 8u
+
+static uint32_t n_units(const params *p) {
+  return 2u * p->L * ((p->C + UNIT_LANES - 1) / UNIT_LANES);
+}
+/* first stream and stream count of unit u */
+static void unit_span(const params *p, uint32_t u, uint32_t *m0, uint32_t *nv) {
+  const uint32_t ncb = (p->C + UNIT_LANES - 1) / UNIT_LANES;
+  const uint32_t row = u / ncb, cb = u % ncb;
+  *m0 = row * p->C + cb * UNIT_LANES;
+  *nv = (p->C - cb * UNIT_LANES < UNIT_LANES) ? p->C - cb * UNIT_LANES : UNIT_LANES;
+}
+
+/*
+ * R17: the reference reader of one unit, which fixes the order of the unit's
+ * 8-byte blocks in the payload.  Every lane l (stream m0 + l) decodes its
+ * stream; R is the number of bytes its decoder has consumed, W the number of
+ * bytes it holds ready (the "delivered" blocks), q the next block it has not
+ * asked for.  A request hands out the next payload slot, lanes in increasing
+ * order within a step:
+ *   - start: every lane asks for its blocks 0, 1 and 2 (block index outer,
+ *     lane inner); W = 16, R = 4;
+ *   - before token j, every lane for which
+ *       j % G == 0 ? W - R <= 8 : W - R < 2
+ *     takes its next block (W += 8) and asks for block q (q += 1), if its
+ *     stream has a block q;
+ *   - then every lane decodes symbol j (R grows by the bytes it shifts in).
+ * A lane never reads a byte it does not hold (W - R >= 2 before a token, a
+ * symbol shifts in at most 2 bytes), and never holds more than 16 bytes
+ * ahead (W - R <= 16).
+ * Encode mode (`streams` given): copies each requested block from the
+ * stream's contiguous bytes (zero-padded to whole blocks) into `slots_out`.
+ * Decode mode (`slots_in` given): gathers each requested block from the
+ * payload into the lane's buffer and decodes from it.  Both decode every
+ * symbol (into sym [nv][n] when given) and return ORC_ERR_CORRUPT if a
+ * stream does not decode to exactly its nbytes.  `order` (optional) receives
+ * lane << 16 | block for every slot.
+ */
+static int unit_reader(const params *p, const uint16_t *fA, const uint16_t *fD, uint32_t level,
+                       uint32_t m0, uint32_t nv, uint32_t n, const uint32_t *nb,
+                       const uint8_t *const *streams, const uint8_t *slots_in, uint64_t n_slots,
+                       uint8_t *slots_out, int32_t *sym, uint32_t *order) {
+  const uint32_t S = n_streams(p);
+  uint32_t nblk[UNIT_LANES], q[UNIT_LANES], W[UNIT_LANES];
+  uint8_t *own[UNIT_LANES];
+  const uint8_t *buf[UNIT_LANES];
+  rc_dec dec[UNIT_LANES];
+  uint32_t fa[UNIT_LANES][ANCHOR_ALPHA], fd[UNIT_LANES][MAX_DELTA_ALPHA];
+  uint32_t A[UNIT_LANES];
+  int err = ORC_OK;
+  for (uint32_t l = 0; l < nv; ++l) {
+    const uint32_t m = m0 + l;
+    const uint32_t b = p->bits[level][third_of(m / (2 * p->C), p->L)];
+    nblk[l] = (uint32_t)(pad8(nb[l]) / BLOCK);
+    q[l] = 0;
+    W[l] = 16;
+    A[l] = delta_alpha(b);
+    widen_freqs(fA + (size_t)m * ANCHOR_ALPHA, ANCHOR_ALPHA, fa[l]);
+    widen_freqs(fD + ((size_t)level * S + m) * MAX_DELTA_ALPHA, A[l], fd[l]);
+    own[l] = NULL;
+    if (streams) {
+      buf[l] = streams[l];
+    } else {
+      own[l] = (uint8_t *)calloc((size_t)nblk[l] + 1, BLOCK);
+      buf[l] = own[l];
+    }
+  }
+  uint64_t next = 0;
+#define REQUEST(l)                                                                     \
+  do {                                                                                 \
+    if (q[l] < nblk[l]) {                                                              \
+      const uint64_t slot = next++;                                                    \
+      if (slot >= n_slots) {                                                           \
+        err = ORC_ERR_CORRUPT;                                                         \
+      } else if (streams) {                                                            \
+        memcpy(slots_out + slot * BLOCK, buf[l] + (size_t)q[l] * BLOCK, BLOCK);        \
+      } else {                                                                         \
+        memcpy(own[l] + (size_t)q[l] * BLOCK, slots_in + slot * BLOCK, BLOCK);         \
+      }                                                                                \
+      if (order && slot < n_slots) order[slot] = (l << 16) | q[l];                     \
+      ++q[l];                                                                          \
+    }                                                                                  \
+  } while (0)
+  for (uint32_t blk = 0; blk < 3; ++blk)
+    for (uint32_t l = 0; l < nv; ++l) REQUEST(l);
+  for (uint32_t l = 0; l < nv && !err; ++l) err = rc_dec_init(&dec[l], buf[l], nb[l]);
+  for (uint32_t j = 0; j < n && !err; ++j) {
+    const int anchor = (j % p->G) == 0;
+    for (uint32_t l = 0; l < nv; ++l) {
+      const uint64_t ahead = W[l] - dec[l].pos; /* R <= W always */
+      if (anchor ? ahead <= 8 : ahead < 2) {
+        W[l] += BLOCK;
+        REQUEST(l);
+      }
+    }
+    for (uint32_t l = 0; l < nv && !err; ++l) {
+      int32_t s;
+      err = anchor ? rc_dec_step(&dec[l], buf[l], nb[l], fa[l], ANCHOR_ALPHA, &s)
+                   : rc_dec_step(&dec[l], buf[l], nb[l], fd[l], A[l], &s);
+      if (sym) sym[(size_t)l * n + j] = s;
+    }
+  }
+#undef REQUEST
+  for (uint32_t l = 0; l < nv && !err; ++l)
+    if (dec[l].pos != nb[l]) err = ORC_ERR_CORRUPT;
+  if (!err && next != n_slots) err = ORC_ERR_CORRUPT; /* every block asked for once */
+  for (uint32_t l = 0; l < nv; ++l) free(own[l]);
+  return err;
 }
 
 /*
@@ -551,7 +704,7 @@ int64_t orc_encode_chunk(const uint32_t *pw, const uint16_t *fA, const uint16_t 
   if (t0 >= T) return ORC_ERR_SHAPE;
   const uint32_t n = (uint32_t)((T - t0 < p.chunk) ? T - t0 : p.chunk);
   const uint32_t S = n_streams(&p);
-  const uint64_t slot = pad4(4u + 2u * (uint64_t)n);
+  const uint64_t slot = pad8(4u + 2u * (uint64_t)n);
   uint8_t *scratch = (uint8_t *)calloc((size_t)S, (size_t)slot);
   float *side = (float *)malloc(sizeof(float) * 3u * S);
   uint32_t *nb = (uint32_t *)malloc(sizeof(uint32_t) * S);
@@ -562,6 +715,7 @@ int64_t orc_encode_chunk(const uint32_t *pw, const uint16_t *fA, const uint16_t 
     return ORC_ERR_CAPACITY;
   }
   int err = ORC_OK;
+  /* every stream's bytes, contiguous */
 #pragma omp parallel for schedule(dynamic, 16)
   for (long mm = 0; mm < (long)S; ++mm) {
     const uint32_t m = (uint32_t)mm;
@@ -596,7 +750,7 @@ int64_t orc_encode_chunk(const uint32_t *pw, const uint16_t *fA, const uint16_t 
     return err;
   }
   uint64_t payload = 0;
-  for (uint32_t m = 0; m < S; ++m) payload += pad4(nb[m]);
+  for (uint32_t m = 0; m < S; ++m) payload += pad8(nb[m]);
   const uint64_t total = HDR_BYTES + (uint64_t)REC_BYTES * S + payload;
   if (total > cap) {
     free(scratch);
@@ -607,7 +761,7 @@ int64_t orc_encode_chunk(const uint32_t *pw, const uint16_t *fA, const uint16_t 
   memset(out, 0, (size_t)total);
   /* header */
   memcpy(out, "KVC1", 4);
-  put_u16(out + 4, 1);
+  put_u16(out + 4, 2);
   out[6] = (uint8_t)level;
   out[7] = (uint8_t)p.abits;
   put_u16(out + 8, (uint16_t)p.G);
@@ -621,21 +775,44 @@ int64_t orc_encode_chunk(const uint32_t *pw, const uint16_t *fA, const uint16_t 
   put_u64(out + 40, payload);
   put_u32(out + 48, p.chunk);
   put_u32(out + 52, S);
-  /* records and payload */
-  uint64_t off = HDR_BYTES + (uint64_t)REC_BYTES * S;
+  /* records */
   for (uint32_t m = 0; m < S; ++m) {
     uint8_t *rec = out + HDR_BYTES + (size_t)REC_BYTES * m;
     put_f32(rec, side[3 * m]);
     put_f32(rec + 4, side[3 * m + 1]);
     put_f32(rec + 8, side[3 * m + 2]);
     put_u32(rec + 12, nb[m]);
-    memcpy(out + off, scratch + (size_t)m * slot, nb[m]);
-    off += pad4(nb[m]);
   }
+  /* payload: each unit's blocks in the reference reader's order (R17) */
+  uint64_t *uoff = (uint64_t *)malloc(sizeof(uint64_t) * (n_units(&p) + 1));
+  uoff[0] = 0;
+  for (uint32_t u = 0; u < n_units(&p); ++u) {
+    uint32_t m0, nv;
+    unit_span(&p, u, &m0, &nv);
+    uint64_t sz = 0;
+    for (uint32_t l = 0; l < nv; ++l) sz += pad8(nb[m0 + l]);
+    uoff[u + 1] = uoff[u] + sz;
+  }
+  uint8_t *pay = out + HDR_BYTES + (size_t)REC_BYTES * S;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (long uu = 0; uu < (long)n_units(&p); ++uu) {
+    const uint32_t u = (uint32_t)uu;
+    uint32_t m0, nv;
+    unit_span(&p, u, &m0, &nv);
+    const uint8_t *streams[UNIT_LANES];
+    for (uint32_t l = 0; l < nv; ++l) streams[l] = scratch + (size_t)(m0 + l) * slot;
+    const int e = unit_reader(&p, fA, fD, level, m0, nv, n, nb + m0, streams, NULL,
+                              (uoff[u + 1] - uoff[u]) / BLOCK, pay + uoff[u], NULL, NULL);
+    if (e) {
+#pragma omp critical
+      err = e;
+    }
+  }
+  free(uoff);
   free(scratch);
   free(side);
   free(nb);
-  return (int64_t)total;
+  return err ? err : (int64_t)total;
 }
 
 /* ------------------------------------------------------ decode */
@@ -648,7 +825,7 @@ static int check_header(const params *p, uint64_t profile_id, const uint8_t *c, 
                         chunk_hdr *h) {
   const uint32_t S = n_streams(p);
   if (nbytes < HDR_BYTES + (uint64_t)REC_BYTES * S) return ORC_ERR_CORRUPT;
-  if (memcmp(c, "KVC1", 4) != 0 || get_u16(c + 4) != 1) return ORC_ERR_CORRUPT;
+  if (memcmp(c, "KVC1", 4) != 0 || get_u16(c + 4) != 2) return ORC_ERR_CORRUPT;
   h->level = c[6];
   h->n = get_u32(c + 24);
   h->payload = get_u64(c + 40);
@@ -663,13 +840,14 @@ static int check_header(const params *p, uint64_t profile_id, const uint8_t *c, 
   if (get_u64(c + 32) != profile_id) return ORC_ERR_PROFILE;
   if (HDR_BYTES + (uint64_t)REC_BYTES * S + h->payload != nbytes) return ORC_ERR_CORRUPT;
   uint64_t sum = 0;
-  for (uint32_t m = 0; m < S; ++m) sum += pad4(get_u32(c + HDR_BYTES + (size_t)REC_BYTES * m + 12));
+  for (uint32_t m = 0; m < S; ++m) sum += pad8(get_u32(c + HDR_BYTES + (size_t)REC_BYTES * m + 12));
   if (sum != h->payload) return ORC_ERR_CORRUPT;
   return ORC_OK;
 }
 
-/* Per-stream payload offsets of a container (relative to the payload
- * start): the exclusive prefix sum of the padded stream lengths. */
+/* Per-stream block offsets of a container (relative to the payload start):
+ * the exclusive prefix sum of the streams' lengths rounded up to whole
+ * 8-byte blocks.  A unit's payload starts at its first stream's offset. */
 int orc_stream_offsets(const uint32_t *pw, const uint8_t *c, uint64_t nbytes, uint32_t *offs) {
   params p;
   int st = read_params(pw, &p);
@@ -679,27 +857,36 @@ int orc_stream_offsets(const uint32_t *pw, const uint8_t *c, uint64_t nbytes, ui
   uint64_t acc = 0;
   for (uint32_t m = 0; m < S; ++m) {
     offs[m] = (uint32_t)acc;
-    acc += pad4(get_u32(c + HDR_BYTES + (size_t)REC_BYTES * m + 12));
+    acc += pad8(get_u32(c + HDR_BYTES + (size_t)REC_BYTES * m + 12));
   }
   return ORC_OK;
 }
 
-static int decode_one(const params *p, const uint16_t *fA, const uint16_t *fD, const uint8_t *c,
-                      const chunk_hdr *h, uint32_t m, uint64_t off, int32_t *sym, uint16_t *vals) {
+/* Run the reference reader over unit u of a checked container: symbols
+ * [nv][n], and optionally each lane's contiguous stream bytes (`bytes`,
+ * nv pointers of pad8(nbytes) bytes) and the slot order. */
+static int read_unit(const params *p, const uint16_t *fA, const uint16_t *fD, const uint8_t *c,
+                     const chunk_hdr *h, const uint32_t *offs, uint32_t u, int32_t *sym,
+                     uint32_t *order) {
   const uint32_t S = n_streams(p);
+  uint32_t m0, nv, nb[UNIT_LANES];
+  unit_span(p, u, &m0, &nv);
+  uint64_t sz = 0;
+  for (uint32_t l = 0; l < nv; ++l) {
+    nb[l] = get_u32(c + HDR_BYTES + (size_t)REC_BYTES * (m0 + l) + 12);
+    sz += pad8(nb[l]);
+  }
+  const uint8_t *pay = c + HDR_BYTES + (size_t)REC_BYTES * S + offs[m0];
+  return unit_reader(p, fA, fD, h->level, m0, nv, h->n, nb, NULL, pay, sz / BLOCK, NULL, sym,
+                     order);
+}
+
+static void dequantize_lane(const params *p, const uint8_t *c, const chunk_hdr *h, uint32_t m,
+                            const int32_t *sym, uint16_t *vals) {
   const uint32_t l = m / (2 * p->C);
   const uint32_t b = p->bits[h->level][third_of(l, p->L)];
   const uint8_t *rec = c + HDR_BYTES + (size_t)REC_BYTES * m;
-  const float lo = get_f32(rec), sa = get_f32(rec + 4), dl = get_f32(rec + 8);
-  const uint32_t nb = get_u32(rec + 12);
-  uint32_t fa[ANCHOR_ALPHA], fd[MAX_DELTA_ALPHA];
-  widen_freqs(fA + (size_t)m * ANCHOR_ALPHA, ANCHOR_ALPHA, fa);
-  widen_freqs(fD + ((size_t)h->level * S + m) * MAX_DELTA_ALPHA, delta_alpha(b), fd);
-  const uint8_t *payload = c + HDR_BYTES + (size_t)REC_BYTES * S;
-  int st = orc_rc_decode(payload + off, nb, h->n, p->G, fa, ANCHOR_ALPHA, fd, delta_alpha(b), sym);
-  if (st) return st;
-  orc_dequantize(sym, h->n, p->G, b, lo, sa, dl, vals);
-  return ORC_OK;
+  orc_dequantize(sym, h->n, p->G, b, get_f32(rec), get_f32(rec + 4), get_f32(rec + 8), vals);
 }
 
 /*
@@ -722,19 +909,25 @@ int orc_decode_chunk(const uint32_t *pw, const uint16_t *fA, const uint16_t *fD,
   uint32_t *offs = (uint32_t *)malloc(sizeof(uint32_t) * S);
   orc_stream_offsets(pw, c, nbytes, offs);
   int err = ORC_OK;
-#pragma omp parallel for schedule(dynamic, 16)
-  for (long mm = 0; mm < (long)S; ++mm) {
-    const uint32_t m = (uint32_t)mm;
-    int32_t *sym = (int32_t *)malloc(sizeof(int32_t) * h.n);
+#pragma omp parallel for schedule(dynamic, 4)
+  for (long uu = 0; uu < (long)n_units(&p); ++uu) {
+    const uint32_t u = (uint32_t)uu;
+    uint32_t m0, nv;
+    unit_span(&p, u, &m0, &nv);
+    int32_t *sym = (int32_t *)malloc(sizeof(int32_t) * (size_t)nv * h.n);
     uint16_t *vals = (uint16_t *)malloc(sizeof(uint16_t) * h.n);
-    const int e = decode_one(&p, fA, fD, c, &h, m, offs[m], sym, vals);
+    const int e = read_unit(&p, fA, fD, c, &h, offs, u, sym, NULL);
     if (e) {
 #pragma omp critical
       err = e;
     } else {
-      const uint32_t row = m / p.C, ch = m % p.C;
-      uint16_t *dst = out + (size_t)row * T_total * p.C;
-      for (uint32_t j = 0; j < h.n; ++j) dst[(size_t)(first_token + j) * p.C + ch] = vals[j];
+      for (uint32_t l = 0; l < nv; ++l) {
+        const uint32_t m = m0 + l;
+        dequantize_lane(&p, c, &h, m, sym + (size_t)l * h.n, vals);
+        const uint32_t row = m / p.C, ch = m % p.C;
+        uint16_t *dst = out + (size_t)row * T_total * p.C;
+        for (uint32_t j = 0; j < h.n; ++j) dst[(size_t)(first_token + j) * p.C + ch] = vals[j];
+      }
     }
     free(sym);
     free(vals);
@@ -744,7 +937,8 @@ int orc_decode_chunk(const uint32_t *pw, const uint16_t *fA, const uint16_t *fD,
 }
 
 /* Decode selected streams of one container: values [count][n] (binary16)
- * and symbols [count][n]; for checks at sizes too large to decode whole. */
+ * and symbols [count][n]; for checks at sizes too large to decode whole
+ * (each stream's whole unit is read). */
 int orc_decode_streams(const uint32_t *pw, const uint16_t *fA, const uint16_t *fD,
                        uint64_t profile_id, const uint8_t *c, uint64_t nbytes,
                        const uint32_t *ids, uint32_t count, uint16_t *vals, int32_t *syms) {
@@ -755,19 +949,99 @@ int orc_decode_streams(const uint32_t *pw, const uint16_t *fA, const uint16_t *f
   st = check_header(&p, profile_id, c, nbytes, &h);
   if (st) return st;
   const uint32_t S = n_streams(&p);
+  const uint32_t ncb = (p.C + UNIT_LANES - 1) / UNIT_LANES;
   uint32_t *offs = (uint32_t *)malloc(sizeof(uint32_t) * S);
+  int32_t *usym = (int32_t *)malloc(sizeof(int32_t) * (size_t)UNIT_LANES * h.n);
   orc_stream_offsets(pw, c, nbytes, offs);
   int err = ORC_OK;
+  uint32_t last = 0xFFFFFFFFu; /* the unit whose symbols usym holds */
   for (uint32_t i = 0; i < count && !err; ++i) {
     if (ids[i] >= S) {
       err = ORC_ERR_ARG;
       break;
     }
-    err = decode_one(&p, fA, fD, c, &h, ids[i], offs[ids[i]], syms + (size_t)i * h.n,
-                     vals + (size_t)i * h.n);
+    const uint32_t m = ids[i];
+    const uint32_t u = (m / p.C) * ncb + (m % p.C) / UNIT_LANES;
+    uint32_t m0, nv;
+    unit_span(&p, u, &m0, &nv);
+    if (u != last) {
+      err = read_unit(&p, fA, fD, c, &h, offs, u, usym, NULL);
+      if (err) break;
+      last = u;
+    }
+    memcpy(syms + (size_t)i * h.n, usym + (size_t)(m - m0) * h.n, sizeof(int32_t) * h.n);
+    dequantize_lane(&p, c, &h, m, syms + (size_t)i * h.n, vals + (size_t)i * h.n);
   }
+  free(usym);
   free(offs);
   return err;
+}
+
+/* For checks of the payload layout: the slot order of unit u (lane << 16 |
+ * block per slot; n_slots = the unit's payload bytes / 8) and the unit's
+ * number of lanes. */
+int orc_unit_order(const uint32_t *pw, const uint16_t *fA, const uint16_t *fD,
+                   uint64_t profile_id, const uint8_t *c, uint64_t nbytes, uint32_t u,
+                   uint32_t *order, uint64_t order_cap, uint32_t *nv_out) {
+  params p;
+  int st = read_params(pw, &p);
+  if (st) return st;
+  chunk_hdr h;
+  st = check_header(&p, profile_id, c, nbytes, &h);
+  if (st) return st;
+  if (u >= n_units(&p)) return ORC_ERR_ARG;
+  const uint32_t S = n_streams(&p);
+  uint32_t m0, nv;
+  unit_span(&p, u, &m0, &nv);
+  uint64_t sz = 0;
+  for (uint32_t l = 0; l < nv; ++l) sz += pad8(get_u32(c + HDR_BYTES + (size_t)REC_BYTES * (m0 + l) + 12));
+  if (sz / BLOCK > order_cap) return ORC_ERR_CAPACITY;
+  uint32_t *offs = (uint32_t *)malloc(sizeof(uint32_t) * S);
+  orc_stream_offsets(pw, c, nbytes, offs);
+  int32_t *sym = (int32_t *)malloc(sizeof(int32_t) * (size_t)nv * h.n);
+  st = read_unit(&p, fA, fD, c, &h, offs, u, sym, order);
+  free(sym);
+  free(offs);
+  *nv_out = nv;
+  return st;
+}
+
+/* The reference reader on an explicit trace, for worked examples: nv lanes
+ * with nblk[l] blocks each and per-token shift counts k[l][j] (bytes shifted
+ * in by symbol j); writes the slot order (lane << 16 | block) and returns
+ * the number of slots, or a negative error.  Mirrors unit_reader's request
+ * rule without decoding. */
+int64_t orc_block_order_trace(uint32_t nv, uint32_t n, uint32_t G, const uint32_t *nblk,
+                              const uint8_t *k, uint32_t *order, uint64_t cap) {
+  if (nv > UNIT_LANES) return ORC_ERR_ARG;
+  uint32_t q[UNIT_LANES], W[UNIT_LANES], R[UNIT_LANES];
+  uint64_t next = 0;
+  for (uint32_t l = 0; l < nv; ++l) {
+    q[l] = 0;
+    W[l] = 16;
+    R[l] = 4;
+  }
+  for (uint32_t blk = 0; blk < 3; ++blk)
+    for (uint32_t l = 0; l < nv; ++l)
+      if (q[l] < nblk[l]) {
+        if (next >= cap) return ORC_ERR_CAPACITY;
+        order[next++] = (l << 16) | q[l]++;
+      }
+  for (uint32_t j = 0; j < n; ++j) {
+    const int anchor = (j % G) == 0;
+    for (uint32_t l = 0; l < nv; ++l) {
+      const uint32_t ahead = W[l] - R[l];
+      if (anchor ? ahead <= 8 : ahead < 2) {
+        W[l] += BLOCK;
+        if (q[l] < nblk[l]) {
+          if (next >= cap) return ORC_ERR_CAPACITY;
+          order[next++] = (l << 16) | q[l]++;
+        }
+      }
+    }
+    for (uint32_t l = 0; l < nv; ++l) R[l] += k[(size_t)l * n + j];
+  }
+  return (int64_t)next;
 }
 
 /* Thread count for the parallel loops (streams are independent, so the

@@ -55,9 +55,9 @@ def test_size_queries(L):
     d = kvc.make_desc(80, 1024, delta_bits=((6, 5, 4), (5, 4, 3), (4, 3, 2)))
     S = 2 * 80 * 1024
     assert L.kvc_tables_bytes(ctypes.byref(d)) == 128 + S * 528 + 3 * S * 128
-    assert L.kvc_container_bound(ctypes.byref(d), 1500) == 64 + 16 * S + S * 3004
-    assert L.kvc_encode_bound(ctypes.byref(d), 16000) == 10 * (64 + 16 * S + S * 3004) + (
-        64 + 16 * S + S * 2004)
+    assert L.kvc_container_bound(ctypes.byref(d), 1500) == 64 + 16 * S + S * 3008
+    assert L.kvc_encode_bound(ctypes.byref(d), 16000) == 10 * (64 + 16 * S + S * 3008) + (
+        64 + 16 * S + S * 2008)
     assert L.kvc_decode_ws_bytes(ctypes.byref(d), 11) >= 11 * S * 4
     assert L.kvc_encode_ws_bytes(ctypes.byref(d), 16000) >= 11 * S * 20
 

@@ -114,7 +114,7 @@ def test_full_size_config(idx):
         assert hdr["n_tokens"] == enc.n_tokens[k] and hdr["first_token"] == 1500 * k
         assert hdr["profile_id"] == otb.profile_id
         nb = enc.container(k)[64:64 + 16 * S].view(torch.int32).view(S, 4)[:, 3].long()
-        assert int(((nb + 3) // 4 * 4).sum()) == hdr["payload_bytes"]
+        assert int(((nb + 7) // 8 * 8).sum()) == hdr["payload_bytes"]
         assert enc.offsets[k + 1] - enc.offsets[k] == 64 + 16 * S + hdr["payload_bytes"]
 
     print("[fullsize] half-step bound on every element", flush=True)
