@@ -10,9 +10,11 @@ from containers already resident in HBM into the preallocated binary16
 [L][2][T][C] KV cache.
 
 Printed: one JSON line with decoded-KV GB/s (binary16 bytes written per
-second), the HBM roofline of the decode kernel, the compression ratio, a
-bit-exactness check against the CPU oracle on a sample of chunks, the
-oracle's own decode rate on the host cores, and the encode rate.
+second), the HBM roofline of the decode kernel (also against a device copy
+measured in the same run, and beside its VALU issue rate), the compression
+ratio, a bit-exactness check against the CPU oracle on a sample of chunks,
+the oracle's own decode rate on the host cores, the encode rate, and SHA-256
+digests of the binary16 tensors.
 """
 from __future__ import annotations
 
@@ -27,6 +29,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+# VALU issue ceiling: 256 CUs x 4 SIMDs, one wave64 vector instruction per
+# SIMD every 4 cycles (16 lanes per cycle) at 2.4 GHz
+VALU_PEAK_WAVE_INSTS = 256 * 4 * 2.4e9 / 4
 COPY_CALIBRATION_BYTES = 1 << 30
 # rocprofv3 HBM counter summary of the decode kernel on this workload; its
 # traffic figure is reported only while the kernel sources still hash to the
@@ -51,8 +56,9 @@ def decode_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
-    """(bytes per decode launch, note) from the committed counter summary."""
+def counter_fields():
+    """(fields, note): the committed counter summary's `- key: value` lines,
+    or None while the decode kernel sources no longer hash to its value."""
     if not os.path.exists(COUNTERS_MD):
         return None, "no counter summary"
     fields = {}
@@ -61,14 +67,57 @@ def measured_traffic():
             if line.startswith("- ") and ": " in line:
                 k, v = line[2:].strip().split(": ", 1)
                 fields[k.strip("`")] = v.strip().strip("`")
+    if fields.get("decode_source_sha256") != decode_source_hash():
+        return None, "decode kernel changed since the counters were taken"
+    return fields, "rocprofv3 counters of this kernel source"
+
+
+def measured_traffic():
+    """(bytes per decode launch, note) from the committed counter summary."""
+    fields, note = counter_fields()
+    if fields is None:
+        return None, note
     try:
-        src = fields["decode_source_sha256"]
         traffic = int(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None, "counter summary unreadable"
-    if src != decode_source_hash():
-        return None, "decode kernel changed since the counters were taken"
     return traffic, f"rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a {COPY_CALIBRATION_BYTES}-byte copy"
+
+
+def measured_valu_insts():
+    """VALU wave-instructions per decode launch (rocprofv3 SQ_INSTS_VALU)
+    from the committed counter summary, or None."""
+    fields, _ = counter_fields()
+    try:
+        return int(fields["valu_insts_per_launch"]) if fields else None
+    except (KeyError, ValueError):
+        return None
+
+
+def sha256_of(a) -> str:
+    import hashlib
+
+    return hashlib.sha256(memoryview(a).cast("B")).hexdigest()
+
+
+def copy_rate(src, reps: int = 5) -> float:
+    """GB/s (bytes read + written) of a plain device-to-device copy of
+    `src`, measured with HIP events on the current stream."""
+    import torch
+
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ms = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        ms.append(a.elapsed_time(b))
+    del dst
+    nbytes = 2 * src.numel() * src.element_size()
+    return nbytes / (statistics.median(ms) * 1e-3) / 1e9
 
 
 def copy_calibration() -> int:
@@ -200,7 +249,13 @@ def main() -> int:
     # codec's own reconstruction (checked bit-exactly against the oracle below)
     decoded_ok = bool(torch.isfinite(out.view(torch.float16)).all().item())
 
+    # a plain device copy of the decoded tensor in the same run: the HBM rate
+    # this GPU actually sustains, as a second reference for the roofline
+    copy_gbs = copy_rate(out)
+    torch.cuda.synchronize()
+
     traffic, traffic_note = measured_traffic()
+    valu_insts = measured_valu_insts()
     value = fp16_bytes / (ms_per_step * 1e-3) / 1e9
     algo_bytes = fp16_bytes + container_bytes
     achieved = algo_bytes / (kernel_ms * 1e-3) / 1e9
@@ -240,12 +295,27 @@ def main() -> int:
             "kernel_ms": round(kernel_ms, 4),
             "index_ms": round(index_ms, 4),
             "algorithmic_bytes": algo_bytes,
+            "copy_GBps": round(copy_gbs, 1),
+            "frac_of_copy": round(achieved / copy_gbs, 4),
+        },
+        # the co-bound: the decode kernel's VALU instruction issue against the
+        # chip's ceiling (instruction count from rocprofv3 SQ_INSTS_VALU of
+        # this kernel source, rate from this run's kernel time)
+        "alu": {
+            "bound": "alu",
+            "unit": "wave64 VALU instructions/s",
+            "insts_per_launch": valu_insts,
+            "achieved": (round(valu_insts / (kernel_ms * 1e-3), -6) if valu_insts else None),
+            "peak": VALU_PEAK_WAVE_INSTS,
+            "frac": (round(valu_insts / (kernel_ms * 1e-3) / VALU_PEAK_WAVE_INSTS, 4)
+                     if valu_insts else None),
         },
         "encode": {
             "ms": round(statistics.median(enc_ms), 3),
             "fp16_GBps": round(fp16_bytes / (statistics.median(enc_ms) * 1e-3) / 1e9, 2),
         },
         "decoded_finite": decoded_ok,
+        "sha256": {"kv_fp16": sha256_of(kv), "profile_kv_fp16": sha256_of(kvp)},
     }
 
     # ---- CPU oracle: bit-exact check on a sample of chunks + its own rate
@@ -269,6 +339,8 @@ def main() -> int:
         hi = 1500 * ks[-1] + cfg.chunk_tokens(ks[-1])
         got = out[:, :, :hi].cpu().numpy().view(np.uint16)
         exact = exact and np.array_equal(got, oout[:, :, :hi])
+        if hi == cfg.n_tokens:
+            result["sha256"]["decoded_fp16"] = sha256_of(np.ascontiguousarray(got))
         sample_bytes = 2 * cfg.n_layers * cfg.n_channels * hi * 2
         result["bit_exact"] = bool(exact)
         result["cpu_baseline"] = {

@@ -24,15 +24,17 @@
 //    search with one 24-bit multiply per probe (no division): 8 steps for
 //    anchors, b steps for a b-bit delta alphabet, the two streams' probes
 //    interleaved;
-//  * the models are staged row-interleaved (entry i of lane l at u16 index
-//    64 i + l), so a probe is a constant offset from the lane's current row,
-//    the symbol index is a shift of the address, and only the two lanes of a
-//    dword can collide on an LDS bank;
-//  * stream bytes are staged per lane in a 16-byte LDS ring fed in 8-byte
-//    blocks: a lane stores the block it loaded earlier only when its ring
-//    runs low (at most 8 bytes left at a group's anchor, fewer than 2 before
-//    any other token) and then asks for its next one, so a load has about a
-//    group of tokens to arrive;
+//  * the models are staged row-interleaved (entry i of lane l in row i, a
+//    128-byte row per entry index), so a probe is a constant offset from the
+//    lane's current row and the symbol index is a shift of the address;
+//    within a row lanes 0..31 take the low halves of the 32 dwords and lanes
+//    32..63 the high halves, so a half-wave never collides on an LDS bank;
+//  * stream bytes are staged per lane in a 16-byte LDS ring (stored
+//    byte-reversed, so the next four bytes are one funnel shift of two
+//    aligned dwords) fed in 8-byte blocks: a lane stores the block it loaded
+//    earlier only when its ring runs low (at most 8 bytes left at a group's
+//    anchor, fewer than 2 before any other token) and then asks for its next
+//    one, so a load has about a group of tokens to arrive;
 //  * the container holds each unit's blocks in exactly that order of
 //    requests (lanes in order within a step), so the wave keeps one
 //    wave-uniform count of the unit's blocks handed out, a lane's block is
@@ -73,6 +75,18 @@ __device__ inline uint32_t ffbh(uint32_t v) {
   return r;
 }
 
+// A lane's u16 column in a row of a staged model table: lanes 0..31 take
+// the low halves of the row's first 32 dwords, lanes 32..63 the high halves.
+__device__ inline uint32_t lane_col(uint32_t lane) { return 2 * (lane & 31) + (lane >> 5); }
+
+// Bits 5..6 of a ring position: the first of the two ring dwords to read.
+// (As a plain shift-and-mask the compiler spends one more instruction.)
+__device__ inline uint32_t dword_of(uint32_t nrpos) {
+  uint32_t r;
+  __asm__("v_bfe_u32 %0, %1, 5, 2" : "=v"(r) : "v"(nrpos));
+  return r;
+}
+
 // LDS byte address of a lane's entry `row` of a row-interleaved table.
 __device__ inline uint32_t lds_addr(const lds_u32 *table) {
   return (uint32_t)(uintptr_t)table;
@@ -92,30 +106,38 @@ struct Source {
   uint32_t cnt;
 };
 
+// A lane's ring holds the stream's bytes in reverse: stream byte p sits at
+// ring byte 19 - p mod 16, and ring bytes 0..3 mirror bytes 16..19.  The four
+// bytes from p on are then the little-endian dword at ring byte -p mod 16,
+// most significant first, and that dword lies inside the two aligned dwords
+// at (-p mod 16) & 12: one paired LDS read and one funnel shift whose shift
+// count is the bit position itself.
 struct Stream {
-  lds_u32 *ring;        // this lane's ring in LDS (16 bytes + 4 mirrored)
+  lds_u32 *ring;        // this lane's ring in LDS (20 bytes)
   uint32_t code, range;
-  uint32_t rposb;       // bits consumed (a multiple of 8)
-  uint32_t wlimb;       // bits written to the ring (a multiple of 64), less
-                        // 16: past it fewer than 2 bytes are buffered
+  uint32_t nrpos;       // -(bits consumed) mod 2^32 (a multiple of 8)
+  uint32_t nwlim;       // -(bits written to the ring, less 16): past it fewer
+                        // than 2 bytes are buffered
   u32x2 held;           // the stream's next 8-byte block, loaded ahead (one
                         // aligned register pair, the load's own destination)
   uint32_t rem;         // the stream's blocks the lane has not asked for
   uint32_t hpos;        // payload block number of the held block
   uint32_t n;
-  int32_t tor;          // largest delta q seen (> M flags a corrupt stream)
   int32_t M;
   uint32_t dbase;       // LDS byte address of this lane's delta row 0
   uint32_t dbaseM;      // dbase + M rows: (addr - dbaseM) >> 7 is q = s - M
   float lo, sa7, dl7, ahat;  // sa7 = sa / 128, dl7 = dl / 128 (exact)
 
-  // The held block into the free half of the ring.
+  // The held block, byte-reversed, into the free half of the ring: its
+  // first stream byte is a multiple of 16 (dwords 4, 3 and the mirror 0) or
+  // 8 past one (dwords 2, 1).
   __device__ inline void put_block() {
-    const uint32_t h = ((wlimb + 16) >> 5) & 2;  // dword 0 or 2
-    ring[h] = held[0];
-    ring[h + 1] = held[1];
-    if (h == 0) ring[4] = held[0];
-    wlimb += 64;
+    const uint32_t h = ((16u - nwlim) >> 5) & 2;
+    const uint32_t lo = __builtin_bswap32(held[0]);
+    ring[4 - h] = lo;
+    ring[3 - h] = __builtin_bswap32(held[1]);
+    if (h == 0) ring[0] = lo;
+    nwlim -= 64;
   }
 };
 
@@ -143,10 +165,12 @@ __device__ inline void advance(Stream &s, Source &src, bool need) {
   src.cnt += (uint32_t)__builtin_popcountll(mask);
 }
 // At a group's anchor: a ring with at most 8 bytes left takes its block.
-__device__ inline void refill(Stream &s, Source &src) { advance(s, src, s.rposb + 48 >= s.wlimb); }
+__device__ inline void refill(Stream &s, Source &src) {
+  advance(s, src, (int32_t)(s.nrpos - s.nwlim) <= 48);
+}
 // Before every other token: a ring with fewer than 2 bytes left takes its
 // block (rare).
-__device__ inline void ensure(Stream &s, Source &src) { advance(s, src, s.rposb > s.wlimb); }
+__device__ inline void ensure(Stream &s, Source &src) { advance(s, src, s.nrpos < s.nwlim); }
 
 // Keeps the instruction scheduler from moving code across this point, so that
 // the LDS reads of a lane's streams are issued back to back and waited for
@@ -164,8 +188,9 @@ __device__ inline void step(Stream *st, uint32_t abase, uint32_t *v) {
   uint32_t in[Q];
 #pragma unroll
   for (uint32_t q = 0; q < Q; ++q) {
-    lds_cu8 *rb = (lds_cu8 *)st[q].ring + ((st[q].rposb >> 3) & 15);
-    in[q] = ((uint32_t)rb[0] << 8) | rb[1];  // the next two stream bytes
+    // the next four stream bytes, most significant first
+    const lds_u32 *rd = (const lds_u32 *)(uintptr_t)(lds_addr(st[q].ring) + (dword_of(st[q].nrpos) << 2));
+    in[q] = __builtin_amdgcn_alignbit(rd[1], rd[0], st[q].nrpos);
   }
   uint32_t r[Q], a[Q];
 #pragma unroll
@@ -197,26 +222,28 @@ __device__ inline void step(Stream *st, uint32_t abase, uint32_t *v) {
     Stream &x = st[q];
     const uint32_t cs = csv[q], cn = cnv[q];
     int32_t xq;  // 128 (symbol - M) for deltas, 128 symbol for anchors
+    // A code at or past r * 2^15 has no symbol.  For a delta the search
+    // then ends on a staged pad (2^15, as is cum[A]), so the interval is
+    // empty and the range becomes 0; an anchor's search cannot pass symbol
+    // 255, so the range is cleared explicitly.  A zero range stays zero
+    // (r = 0 from then on) and is reported at the end of the stream.
+    bool lost = false;
     if constexpr (kAnchor) {
       xq = (int32_t)(a[q] - abase);
-      // a code at or past r * 2^15 has no symbol
-      if (x.code >= (r[q] << kPrec)) x.tor = 0x7FFFFFFF;
+      lost = x.code >= (r[q] << kPrec);
     } else {
       xq = (int32_t)(a[q] - x.dbaseM);
-      x.tor = xq > x.tor ? xq : x.tor;
     }
     // 24-bit multiplies: r < 2^17 and staged cumulative counts <= 2^15
     x.code -= __umul24(r[q], cs);
-    const uint32_t range = __umul24(r[q], cn - cs);
+    uint32_t range = __umul24(r[q], cn - cs);
+    if constexpr (kAnchor) range = lost ? 0u : range;
     // whole bytes to shift in: 0, 1 or 2 (range >= 2^9 for a valid stream)
     const uint32_t sh = ffbh(range) & 24u;
     x.range = range << sh;
-    // code << sh with the next sh / 8 stream bytes below it, as one byte
-    // permute whose selector is a window sliding over the byte indices
-    // 07 06 05 04 (code, most significant first) 01 00 (the next two bytes)
-    const uint32_t sel = __builtin_amdgcn_alignbit(0x706u, 0x05040100u, (16 - sh) & 31);
-    x.code = __builtin_amdgcn_perm(x.code, in[q], sel);
-    x.rposb += sh;
+    // code << sh with the next sh / 8 stream bytes below it: one 64-bit shift
+    x.code = (uint32_t)((((uint64_t)x.code << 32) | in[q]) << sh >> 32);
+    x.nrpos -= sh;
     if constexpr (kSymbols) {
       v[q] = kAnchor ? (uint32_t)xq >> 7 : (uint32_t)((xq >> 7) + x.M);
     } else {
@@ -331,9 +358,9 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
   lds_u16 *hD = (lds_u16 *)sD;
 
   // ---- stage the 64 channels' anchor models and the used levels' delta
-  // models, row-interleaved: entry i of lane l at u16 index i * 64 + l, so
-  // lanes reading their own tables hit different banks unless two lanes of a
-  // pair read different rows of the same parity.
+  // models, row-interleaved: entry i of lane l at u16 index
+  // i * 64 + lane_col(l), so the 32 lanes of a half-wave always read 32
+  // different dwords of their rows, one per bank, whatever rows they are at.
   const uint32_t tid = threadIdx.x;
   {
     const uint32_t *gA = reinterpret_cast<const uint32_t *>(tables + kTablesHdr) +
@@ -341,8 +368,8 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
     for (uint32_t i = tid; i < nv * (kARows / 2); i += blockDim.x) {
       const uint32_t w = i / nv, l = i % nv;
       const uint32_t v = gA[(uint64_t)l * (kAnchorStride / 2) + w];
-      hA[(2 * w) * kWave + l] = (uint16_t)v;
-      hA[(2 * w + 1) * kWave + l] = (uint16_t)(v >> 16);
+      hA[(2 * w) * kWave + lane_col(l)] = (uint16_t)v;
+      hA[(2 * w + 1) * kWave + lane_col(l)] = (uint16_t)(v >> 16);
     }
     uint32_t slot = 0;
     for (uint32_t lv = 0; lv < d.nlev; ++lv) {
@@ -357,8 +384,8 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
             w < kDeltaStride / 2 ? gD[(uint64_t)l * (kDeltaStride / 2) + w] : 0xFFFFFFFFu;
         // entries past cum[A] (0xFFFF pads) become 2^15 = cum[A]
         const uint32_t e0 = v & 0xFFFFu, e1 = v >> 16;
-        dst[(2 * w) * kWave + l] = (uint16_t)(e0 == 0xFFFFu ? kTot : e0);
-        dst[(2 * w + 1) * kWave + l] = (uint16_t)(e1 == 0xFFFFu ? kTot : e1);
+        dst[(2 * w) * kWave + lane_col(l)] = (uint16_t)(e0 == 0xFFFFu ? kTot : e0);
+        dst[(2 * w + 1) * kWave + lane_col(l)] = (uint16_t)(e1 == 0xFFFFu ? kTot : e1);
       }
       ++slot;
     }
@@ -368,7 +395,7 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   if (lane >= nv) return;
 
-  const uint32_t abase = lds_addr(sA) + 2 * lane;
+  const uint32_t abase = lds_addr(sA) + 2 * lane_col(lane);
   const uint32_t third = third_of(row >> 1, d.L);
   const uint32_t esz = kSymbols ? 1u : 2u;
   const uint64_t ld = (uint64_t)d.C * esz;
@@ -388,11 +415,16 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
       const uint32_t k = gp.start + (idx < gp.count ? idx : 0u);
       active[q] = idx < gp.count && valid[k];
       s.n = 0;
-      s.tor = 0;
       s.M = 0;
-      s.ring = sR + ((wave * kSlots + q) * kWave + lane) * kRing;
+      {
+        // one register per ring address, so that a ring read is one
+        // bit-field extract and one shift-add
+        uint32_t ra = lds_addr(sR + ((wave * kSlots + q) * kWave + lane) * kRing);
+        __asm__ volatile("" : "+v"(ra));
+        s.ring = (lds_u32 *)(uintptr_t)ra;
+      }
       ob[q] = (gbyte *)out;
-      s.dbase = lds_addr(sD) + 2 * lane;
+      s.dbase = lds_addr(sD) + 2 * lane_col(lane);
       s.dbaseM = s.dbase;
       s.rem = 0;
       s.hpos = 0;
@@ -402,12 +434,11 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
       if (!active[q]) continue;
       const ChunkInfo c = ci[k];
       const uint32_t lslot = __builtin_popcount(level_mask & ((1u << c.level) - 1u));
-      s.dbase = lds_addr(sD) + lslot * kDRows * kRowBytes + 2 * lane;
+      s.dbase = lds_addr(sD) + lslot * kDRows * kRowBytes + 2 * lane_col(lane);
       const uint32_t b = d.bits[c.level][third];
       steps = b > steps ? b : steps;
       s.M = (1 << (b - 1)) - 1;
       s.dbaseM = s.dbase + (uint32_t)s.M * kRowBytes;
-      s.tor = -(int32_t)(s.M * kRowBytes);
       const uint32_t *rec = reinterpret_cast<const uint32_t *>(c.records + (uint64_t)m * kRecBytes);
       s.lo = __builtin_bit_cast(float, rec[0]);
       // sa / 128 and dl / 128 are exact: sa is 0 or at least 2^-24 / 255 (a
@@ -439,16 +470,16 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
         src[q].cnt += (uint32_t)__builtin_popcountll(mask);
       }
       s.rem = nblk < 3 ? 0u : nblk - 3;
-      s.ring[0] = blk[0][0];
-      s.ring[1] = blk[0][1];
-      s.ring[2] = blk[1][0];
-      s.ring[3] = blk[1][1];
-      s.ring[4] = blk[0][0];
+      s.ring[4] = __builtin_bswap32(blk[0][0]);
+      s.ring[3] = __builtin_bswap32(blk[0][1]);
+      s.ring[2] = __builtin_bswap32(blk[1][0]);
+      s.ring[1] = __builtin_bswap32(blk[1][1]);
+      s.ring[0] = __builtin_bswap32(blk[0][0]);
       s.held[0] = blk[2][0];
       s.held[1] = blk[2][1];
-      s.wlimb = 128 - 16;
+      s.nwlim = 0u - (128 - 16);
       s.code = bswap32(blk[0][0]);
-      s.rposb = 32;
+      s.nrpos = 0u - 32;
       s.range = 0xFFFFFFFFu;
     }
     steps = __builtin_amdgcn_readfirstlane(steps);
@@ -500,7 +531,7 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
       const uint32_t k = gp.start + 2 * pair + q;
       const uint32_t nbytes =
           reinterpret_cast<const uint32_t *>(ci[k].records + (uint64_t)m * kRecBytes)[3];
-      if (st[q].tor > (int32_t)(st[q].M * kRowBytes) || st[q].rposb != 8 * nbytes || st[q].rem != 0)
+      if (st[q].range == 0 || st[q].nrpos != 0u - 8 * nbytes || st[q].rem != 0)
         set_status(status, KVC_ERR_CORRUPT_STREAM);
     }
   }
