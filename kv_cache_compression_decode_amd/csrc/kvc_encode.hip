@@ -70,8 +70,11 @@ __device__ inline EncodeBlock encode_block(uint32_t n_groups) {
 // Entries of the per-lane queue of payload blocks asked for (by the reading
 // rule) but not yet written.  The queue holds the blocks between the last
 // byte written and the reader's position: about 5, plus one per 8 bytes the
-// range coder still holds back for a pending carry.
-constexpr uint32_t kQueue = 16;
+// range coder still holds back for a pending carry.  8 entries keep the
+// emit kernel's LDS (models + queues) small enough for two workgroups per
+// CU; a longer queue would be needed only by a run of some 25 pending 0xFF
+// bytes.
+constexpr uint32_t kQueue = 8;
 
 // Byte sink writing a stream's bytes, little-endian, in 8-byte blocks to the
 // payload blocks the reading rule gave them (queued in block order); at most
