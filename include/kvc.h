@@ -83,6 +83,17 @@ typedef struct {
   uint32_t reserved;        /* 0 */
 } kvc_chunk_ref;
 
+/* One encoded chunk still in host memory, for kvc_restore. */
+typedef struct {
+  const uint8_t *host_container; /* host pointer; pinned (hipHostMalloc) memory
+                                    lets the copy overlap the decode */
+  uint64_t container_bytes;      /* its size in bytes */
+  uint32_t first_token;          /* destination token offset in kv_out */
+  uint32_t n_tokens;             /* tokens in the chunk; must equal the header */
+  uint32_t level;                /* compression level; must equal the header */
+  uint32_t reserved;             /* 0 */
+} kvc_host_chunk;
+
 /* Library version (major * 10000 + minor * 100 + patch). */
 int kvc_version(void);
 
@@ -178,6 +189,42 @@ kvc_status kvc_decode(const kvc_codec_desc *d, const void *tables, const kvc_chu
 kvc_status kvc_decode_index(const kvc_codec_desc *d, const void *tables,
                             const kvc_chunk_ref *chunks, uint32_t n_chunks, uint32_t *offsets_out,
                             void *ws, uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream);
+
+/* --------------------------------------------------------- streamed restore */
+/*
+ * Device staging bytes kvc_restore needs for these chunks in batches of
+ * batch_chunks: three slots (fewer if there are fewer batches), each the
+ * largest batch's containers, each container rounded up to 256 bytes.  0 for
+ * an empty or invalid request.
+ */
+uint64_t kvc_restore_staging_bytes(const kvc_host_chunk *chunks, uint32_t n_chunks,
+                                   uint32_t batch_chunks);
+
+/*
+ * Restore a context from containers in host memory, with the transfer of
+ * one batch of chunks overlapping the decode of the one before (CacheGen
+ * page, 核心方法, implementation paragraph: chunk i is sent while chunk i-1
+ * is decoded).  chunks: host array of n_chunks, processed in order in
+ * batches of batch_chunks (>= 1).  Batch b is copied host-to-device on
+ * `copy` into staging slot b % 3 (device, staging_bytes >=
+ * kvc_restore_staging_bytes), then decoded on `compute` exactly as
+ * kvc_decode would decode those chunks (same kernels, same bits) into kv_out
+ * [L][2][T_total][C]; the copy into a slot waits for the decode that last
+ * read it, and the first copy waits for the work already queued on
+ * `compute`.  ws: workspace of kvc_decode_ws_bytes(d, min(batch_chunks,
+ * n_chunks)) bytes.  batch_done: NULL, or a host array of ceil(n_chunks /
+ * batch_chunks) caller-created events, event b recorded on `compute` once
+ * batch b is in kv_out.  All argument, range and size checks of every batch
+ * are made before anything is queued.  On return everything is queued;
+ * synchronizing `compute` waits for all of it.  `copy` and `compute` may be
+ * the same stream (no overlap).  Device errors: those of kvc_decode, the
+ * first one of any batch.
+ */
+kvc_status kvc_restore(const kvc_codec_desc *d, const void *tables, const kvc_host_chunk *chunks,
+                       uint32_t n_chunks, uint32_t batch_chunks, uint16_t *kv_out,
+                       uint32_t T_total, uint8_t *staging, uint64_t staging_bytes, void *ws,
+                       uint64_t ws_bytes, int32_t *dev_status, hipStream_t compute,
+                       hipStream_t copy, hipEvent_t *batch_done);
 
 /*
  * Debug form of kvc_decode: same kernels, but writes the decoded symbols

@@ -37,7 +37,7 @@ EXPORTED = (
     "kvc_version", "kvc_status_str", "kvc_validate_desc", "kvc_tables_bytes",
     "kvc_profile_ws_bytes", "kvc_profile", "kvc_container_bound", "kvc_encode_bound",
     "kvc_encode_ws_bytes", "kvc_encode", "kvc_decode_ws_bytes", "kvc_decode",
-    "kvc_decode_index", "kvc_decode_symbols",
+    "kvc_decode_index", "kvc_decode_symbols", "kvc_restore_staging_bytes", "kvc_restore",
 )
 
 
@@ -70,6 +70,18 @@ class ChunkRef(ctypes.Structure):
     """kvc_chunk_ref: one fetched chunk handed to the decoder."""
     _fields_ = [
         ("container", ctypes.c_void_p),
+        ("container_bytes", ctypes.c_uint64),
+        ("first_token", ctypes.c_uint32),
+        ("n_tokens", ctypes.c_uint32),
+        ("level", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+    ]
+
+
+class HostChunk(ctypes.Structure):
+    """kvc_host_chunk: one encoded chunk still in (pinned) host memory."""
+    _fields_ = [
+        ("host_container", ctypes.c_void_p),
         ("container_bytes", ctypes.c_uint64),
         ("first_token", ctypes.c_uint32),
         ("n_tokens", ctypes.c_uint32),
@@ -131,6 +143,10 @@ def lib():
     L.kvc_decode_symbols.restype = ctypes.c_int
     L.kvc_decode_index.argtypes = [dp, vp, vp, u32, vp, vp, u64, vp, vp]
     L.kvc_decode_index.restype = ctypes.c_int
+    L.kvc_restore_staging_bytes.argtypes = [vp, u32, u32]
+    L.kvc_restore_staging_bytes.restype = u64
+    L.kvc_restore.argtypes = [dp, vp, vp, u32, u32, vp, u32, vp, u64, vp, u64, vp, vp, vp, vp]
+    L.kvc_restore.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -347,3 +363,111 @@ def decode_index(desc: CodecDesc, tables: torch.Tensor, refs: Sequence[ChunkRef]
                                   wsp.status.data_ptr(), _stream(stream)), "kvc_decode_index")
     read_status(wsp.status, "kvc_decode_index")
     return offs
+
+
+# ------------------------------------------------------------ streamed restore
+def host_chunks(enc: Encoded, host_blob: torch.Tensor,
+                chunks: Optional[Sequence[int]] = None) -> List[HostChunk]:
+    """HostChunks for (a subset of) an Encoded context whose containers were
+    copied to `host_blob` (a CPU uint8 tensor laid out like enc.blob; pinned
+    memory lets the copies overlap the decode)."""
+    if host_blob.is_cuda or host_blob.dtype != torch.uint8 or not host_blob.is_contiguous():
+        raise ValueError("host_blob must be a contiguous CPU uint8 tensor")
+    ks = list(range(enc.n_chunks)) if chunks is None else list(chunks)
+    base = host_blob.data_ptr()
+    out = []
+    for k in ks:
+        c = HostChunk()
+        c.host_container = base + enc.offsets[k]
+        c.container_bytes = enc.offsets[k + 1] - enc.offsets[k]
+        c.first_token = k * enc.chunk_tokens
+        c.n_tokens = enc.n_tokens[k]
+        c.level = enc.levels[k]
+        c.reserved = 0
+        out.append(c)
+    return out
+
+
+def _host_array(chunks: Sequence[HostChunk]):
+    arr = (HostChunk * max(len(chunks), 1))()
+    for i, c in enumerate(chunks):
+        arr[i] = c
+    return arr
+
+
+def restore_staging_bytes(chunks: Sequence[HostChunk], batch: int) -> int:
+    return int(lib().kvc_restore_staging_bytes(_host_array(chunks), len(chunks), batch))
+
+
+class RestoreWorkspace:
+    """Device staging slots, decode workspace, status word and copy stream
+    of kvc_restore for these chunks in batches of `batch`."""
+
+    def __init__(self, desc: CodecDesc, chunks: Sequence[HostChunk], batch: int, device,
+                 min_staging_bytes: int = 0):
+        self.batch = batch
+        self.staging_bytes = max(restore_staging_bytes(chunks, batch), min_staging_bytes, 256)
+        self.staging = torch.empty(self.staging_bytes, dtype=torch.uint8, device=device)
+        per = max(1, min(batch, len(chunks)))
+        self.ws_bytes = int(lib().kvc_decode_ws_bytes(ctypes.byref(desc), per))
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+        self.status = _dev_status(device)
+        self.copy_stream = torch.cuda.Stream(device=device)
+
+
+class HipEvents:
+    """Raw HIP events (timing disabled) for kvc_restore's per-batch signal."""
+
+    def __init__(self, n: int):
+        try:
+            self._hip = ctypes.CDLL("libamdhip64.so")
+        except OSError:
+            self._hip = ctypes.CDLL("/opt/rocm/lib/libamdhip64.so")
+        self.handles = (ctypes.c_void_p * max(n, 1))()
+        self.n = n
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self._hip.hipEventCreateWithFlags(ctypes.byref(ev), ctypes.c_uint(2)) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.handles[i] = ev
+
+    def query(self, i: int) -> bool:
+        """True once event i has completed."""
+        return self._hip.hipEventQuery(ctypes.c_void_p(self.handles[i])) == 0
+
+    def synchronize(self, i: int) -> None:
+        if self._hip.hipEventSynchronize(ctypes.c_void_p(self.handles[i])) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+
+    def __del__(self):
+        for i in range(self.n):
+            if self.handles[i]:
+                self._hip.hipEventDestroy(ctypes.c_void_p(self.handles[i]))
+
+
+def restore_async(desc: CodecDesc, tables: torch.Tensor, chunks: Sequence[HostChunk],
+                  out: torch.Tensor, rws: RestoreWorkspace, stream=None,
+                  events: Optional[HipEvents] = None) -> None:
+    """Queue kvc_restore: batches of rws.batch chunks copied on rws.copy_stream
+    and decoded on `stream` (default: the current stream) into out."""
+    arr = _host_array(chunks)
+    ev = events.handles if events is not None else None
+    _check(lib().kvc_restore(ctypes.byref(desc), tables.data_ptr(), arr, len(chunks), rws.batch,
+                             _kv_ptr(out), out.shape[2], rws.staging.data_ptr(),
+                             rws.staging_bytes, rws.ws.data_ptr(), rws.ws_bytes,
+                             rws.status.data_ptr(), _stream(stream),
+                             ctypes.c_void_p(rws.copy_stream.cuda_stream), ev), "kvc_restore")
+
+
+def restore(desc: CodecDesc, tables: torch.Tensor, chunks: Sequence[HostChunk], T_total: int,
+            batch: int = 2, out: Optional[torch.Tensor] = None, stream=None,
+            rws: Optional[RestoreWorkspace] = None) -> torch.Tensor:
+    """Restore host-resident chunks into the KV cache [L][2][T_total][C]."""
+    dev = tables.device
+    if out is None:
+        out = torch.zeros((desc.n_layers, 2, T_total, desc.n_channels), dtype=torch.int16, device=dev)
+    if rws is None:
+        rws = RestoreWorkspace(desc, chunks, batch, dev)
+    restore_async(desc, tables, chunks, out, rws, stream)
+    read_status(rws.status, "kvc_restore")
+    return out

@@ -103,7 +103,7 @@ kvc_status hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_
 kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc_chunk_ref *chunks,
                          uint32_t n_chunks, void *out, uint32_t T_total, void *ws,
                          uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream, int mode,
-                         uint32_t *offsets_out) {
+                         uint32_t *offsets_out, bool reset_status = true) {
   // mode 0: values, 1: symbols, 2: index only
   if (!desc_ok(dd)) return KVC_ERR_INVALID_ARG;
   const Desc d = to_desc(dd);
@@ -179,7 +179,7 @@ kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc
       groups.push_back(g);
     }
   }
-  hipError_t e = launch_reset_status(dev_status, stream);
+  hipError_t e = reset_status ? launch_reset_status(dev_status, stream) : hipSuccess;
   if (e != hipSuccess || n_chunks == 0) return hip_status(e);
   uint8_t *base = static_cast<uint8_t *>(ws);
   ChunkInfo *dch = reinterpret_cast<ChunkInfo *>(base + w.chunks);
@@ -200,6 +200,39 @@ kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc
                     stream);
   return hip_status(e);
 }
+
+// Largest batch of a restore: the sum of its containers, each rounded up to
+// 256 bytes (the staging slot size).
+uint64_t restore_slot_bytes(const kvc_host_chunk *c, uint32_t n, uint32_t batch) {
+  uint64_t best = 0;
+  for (uint32_t b0 = 0; b0 < n; b0 += batch) {
+    uint64_t sum = 0;
+    for (uint32_t k = b0; k < n && k - b0 < batch; ++k) sum += align256(c[k].container_bytes);
+    best = std::max(best, sum);
+  }
+  return best;
+}
+
+// Staging slots of a restore: a batch's copy waits only for the decode of
+// the batch kRestoreSlots earlier, so copies run ahead of slow decodes.
+constexpr uint32_t kRestoreSlots = 3;
+
+// Events of one restore call, destroyed when the call returns (a recorded
+// event may be destroyed before it completes; the runtime releases it then).
+struct RestoreEvents {
+  hipEvent_t ev[2 * kRestoreSlots + 1] = {};
+  hipError_t create() {
+    for (hipEvent_t &e : ev) {
+      const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+      if (r != hipSuccess) return r;
+    }
+    return hipSuccess;
+  }
+  ~RestoreEvents() {
+    for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
+  }
+};
 
 }  // namespace
 
@@ -382,6 +415,87 @@ kvc_status kvc_decode_index(const kvc_codec_desc *d, const void *tables,
                             void *ws, uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream) {
   return decode_common(d, tables, chunks, n_chunks, nullptr, 0, ws, ws_bytes, dev_status, stream,
                        2, offsets_out);
+}
+
+uint64_t kvc_restore_staging_bytes(const kvc_host_chunk *chunks, uint32_t n_chunks,
+                                   uint32_t batch_chunks) {
+  if (!chunks || n_chunks == 0 || batch_chunks == 0) return 0;
+  const uint32_t nb = (n_chunks + batch_chunks - 1) / batch_chunks;
+  return restore_slot_bytes(chunks, n_chunks, batch_chunks) * std::min(nb, kRestoreSlots);
+}
+
+kvc_status kvc_restore(const kvc_codec_desc *dd, const void *tables, const kvc_host_chunk *chunks,
+                       uint32_t n_chunks, uint32_t batch_chunks, uint16_t *kv_out,
+                       uint32_t T_total, uint8_t *staging, uint64_t staging_bytes, void *ws,
+                       uint64_t ws_bytes, int32_t *dev_status, hipStream_t compute,
+                       hipStream_t copy, hipEvent_t *batch_done) {
+  // every check of every batch before anything is queued
+  if (!desc_ok(dd)) return KVC_ERR_INVALID_ARG;
+  const Desc d = to_desc(dd);
+  if (!tables || !aligned(tables, 16) || !dev_status || !aligned(dev_status, 4))
+    return KVC_ERR_INVALID_ARG;
+  if (batch_chunks == 0) return KVC_ERR_INVALID_ARG;
+  if (n_chunks > 65535) return KVC_ERR_SHAPE;
+  if (n_chunks == 0) return hip_status(launch_reset_status(dev_status, compute));
+  if (!chunks || !kv_out || !aligned(kv_out, 2) || !staging || !aligned(staging, 256))
+    return KVC_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 256)) return KVC_ERR_INVALID_ARG;
+  const uint64_t S = n_streams(d);
+  std::vector<std::pair<uint32_t, uint32_t>> ranges(n_chunks);
+  for (uint32_t k = 0; k < n_chunks; ++k) {
+    const kvc_host_chunk &c = chunks[k];
+    if (!c.host_container || c.level >= d.nlev || c.reserved != 0) return KVC_ERR_INVALID_ARG;
+    if (c.n_tokens < 1 || c.n_tokens > d.chunk) return KVC_ERR_SHAPE;
+    if ((uint64_t)c.first_token + c.n_tokens > T_total) return KVC_ERR_SHAPE;
+    if (c.container_bytes < kHdrBytes + kRecBytes * S) return KVC_ERR_SHAPE;
+    if (c.container_bytes > 0xFFFFFFFFull) return KVC_ERR_SHAPE;
+    ranges[k] = {c.first_token, c.first_token + c.n_tokens};
+  }
+  std::sort(ranges.begin(), ranges.end());
+  for (uint32_t k = 1; k < n_chunks; ++k)
+    if (ranges[k].first < ranges[k - 1].second) return KVC_ERR_SHAPE;
+  const uint32_t per = std::min(batch_chunks, n_chunks);
+  const uint32_t nb = (n_chunks + per - 1) / per;
+  const uint64_t slot = restore_slot_bytes(chunks, n_chunks, per);
+  if (staging_bytes < slot * std::min(nb, kRestoreSlots)) return KVC_ERR_CAPACITY;
+  if (ws_bytes < ws_layout(d, per, false).total) return KVC_ERR_CAPACITY;
+
+  RestoreEvents evs;  // per slot: copied, decoded; then the start
+  if (evs.create() != hipSuccess) return KVC_ERR_HIP;
+  hipEvent_t *copied = evs.ev, *decoded = evs.ev + kRestoreSlots;
+  hipEvent_t start = evs.ev[2 * kRestoreSlots];
+  hipError_t e = launch_reset_status(dev_status, compute);
+  // the staging slots may still be read by work queued earlier on compute
+  if (e == hipSuccess) e = hipEventRecord(start, compute);
+  if (e == hipSuccess) e = hipStreamWaitEvent(copy, start, 0);
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  std::vector<kvc_chunk_ref> refs;
+  for (uint32_t b = 0; b < nb; ++b) {
+    const uint32_t s = b % kRestoreSlots, k0 = b * per, k1 = std::min(n_chunks, k0 + per);
+    uint8_t *base = staging + (uint64_t)s * slot;
+    if (b >= kRestoreSlots && hipStreamWaitEvent(copy, decoded[s], 0) != hipSuccess)
+      return KVC_ERR_HIP;
+    refs.clear();
+    uint64_t off = 0;
+    for (uint32_t k = k0; k < k1; ++k) {
+      const kvc_host_chunk &c = chunks[k];
+      if (hipMemcpyAsync(base + off, c.host_container, c.container_bytes, hipMemcpyHostToDevice,
+                         copy) != hipSuccess)
+        return KVC_ERR_HIP;
+      refs.push_back({base + off, c.container_bytes, c.first_token, c.n_tokens, c.level, 0});
+      off += align256(c.container_bytes);
+    }
+    if (hipEventRecord(copied[s], copy) != hipSuccess ||
+        hipStreamWaitEvent(compute, copied[s], 0) != hipSuccess)
+      return KVC_ERR_HIP;
+    const kvc_status st = decode_common(dd, tables, refs.data(), (uint32_t)refs.size(), kv_out,
+                                        T_total, ws, ws_bytes, dev_status, compute, 0, nullptr,
+                                        /*reset_status=*/false);
+    if (st != KVC_OK) return st;
+    if (hipEventRecord(decoded[s], compute) != hipSuccess) return KVC_ERR_HIP;
+    if (batch_done && hipEventRecord(batch_done[b], compute) != hipSuccess) return KVC_ERR_HIP;
+  }
+  return KVC_OK;
 }
 
 }  // extern "C"

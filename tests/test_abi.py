@@ -119,3 +119,57 @@ def test_no_oracle_in_product():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "import oracle" not in text and "kvc_oracle" not in text, f
+
+
+def _host_chunks(sizes, first_tokens, n_tokens=10):
+    arr = (kvc.HostChunk * len(sizes))()
+    for i, (b, t0) in enumerate(zip(sizes, first_tokens)):
+        arr[i].host_container = 1 << 20
+        arr[i].container_bytes = b
+        arr[i].first_token = t0
+        arr[i].n_tokens = n_tokens
+        arr[i].level = 0
+    return arr
+
+
+def test_restore_staging_bytes(L):
+    """Three slots of the largest batch (fewer with fewer batches), each
+    container rounded up to 256 bytes; 0 for an empty request."""
+    sizes = [5000, 300, 7000, 256, 100]
+    arr = _host_chunks(sizes, [0, 10, 20, 30, 40])
+    r = lambda n: (n + 255) // 256 * 256
+    assert L.kvc_restore_staging_bytes(arr, 5, 2) == 3 * max(r(5000) + r(300), r(7000) + r(256), r(100))
+    assert L.kvc_restore_staging_bytes(arr, 5, 1) == 3 * r(7000)
+    assert L.kvc_restore_staging_bytes(arr, 5, 3) == 2 * max(r(5000) + r(300) + r(7000), r(256) + r(100))
+    assert L.kvc_restore_staging_bytes(arr, 5, 5) == sum(r(x) for x in sizes)
+    assert L.kvc_restore_staging_bytes(arr, 5, 9) == sum(r(x) for x in sizes)
+    assert L.kvc_restore_staging_bytes(arr, 0, 2) == 0
+    assert L.kvc_restore_staging_bytes(arr, 5, 0) == 0
+
+
+def test_restore_synchronous_errors(L):
+    """kvc_restore checks every batch before queueing anything: a bad batch
+    size, an overlap between chunks of different batches, a short staging
+    buffer or workspace are all returned at once."""
+    d = kvc.make_desc(2, 64)
+    S = d.n_streams
+    size = 64 + 16 * S + 4 * S
+    status = ctypes.c_int32()
+    p = ctypes.c_void_p(1 << 16)
+
+    def call(arr, n, batch, staging_bytes=1 << 30, ws_bytes=1 << 30, T=100):
+        return L.kvc_restore(ctypes.byref(d), p, arr, n, batch, p, T, p, staging_bytes, p,
+                             ws_bytes, ctypes.byref(status), None, None, None)
+
+    ok = _host_chunks([size] * 3, [0, 10, 20])
+    assert call(ok, 3, 0) == kvc.ERR_INVALID_ARG
+    # chunk 2 (second batch of 2) overlaps chunk 0 (first batch)
+    assert call(_host_chunks([size] * 3, [0, 10, 5]), 3, 2) == kvc.ERR_SHAPE
+    assert call(_host_chunks([size] * 3, [0, 10, 95]), 3, 2) == kvc.ERR_SHAPE  # past T
+    assert call(_host_chunks([16] * 3, [0, 10, 20]), 3, 2) == kvc.ERR_SHAPE  # no room for records
+    need = L.kvc_restore_staging_bytes(ok, 3, 2)
+    assert call(ok, 3, 2, staging_bytes=need - 1) == kvc.ERR_CAPACITY
+    assert call(ok, 3, 2, ws_bytes=16) == kvc.ERR_CAPACITY
+    bad = _host_chunks([size] * 3, [0, 10, 20])
+    bad[1].host_container = None
+    assert call(bad, 3, 2) == kvc.ERR_INVALID_ARG
