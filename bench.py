@@ -186,6 +186,57 @@ def measure_restore(kvc, d, tables, enc, cfg, ref_out, reps: int = 3) -> dict:
     return res
 
 
+def measure_controller(kvc, d, tables, kv_dev, cfg, n_traces: int = 500, slo_s: float = 1.0,
+                       sigma: float = 0.3) -> dict:
+    """The per-chunk level choice (kvc_plan_stream) on seeded bandwidth
+    traces, with this workload's real container sizes at every level (the
+    context encoded once per level).  Two links: median rate just enough for
+    all chunks at level 0, and at level 1, within the SLO.  The baselines are
+    the fixed levels, sent back to back (the same call with one level)."""
+    import numpy as np
+
+    import synth
+
+    sizes = []
+    for lv in range(d.n_levels):
+        e = kvc.encode(d, tables, kv_dev, [lv] * cfg.n_chunks)
+        sizes.append(np.diff(np.asarray(e.offsets, dtype=np.int64)))
+        del e
+    sizes = np.stack(sizes, axis=1)  # [chunk][level]
+    res = {"slo_s": slo_s, "traces": n_traces,
+           "link": f"log-normal pieces of 0.05-0.4 s, sigma {sigma} (seeded)",
+           "level_bytes_GB": [round(float(x) / 1e9, 4) for x in sizes.sum(axis=0)],
+           "scenarios": {}}
+    plan_s, plans = 0.0, 0
+    for ref in (0, 1):
+        median = float(sizes[:, ref].sum()) / slo_s
+        viol = np.zeros(d.n_levels + 1)
+        share = np.zeros(d.n_levels)
+        for i in range(n_traces):
+            trace = synth.bandwidth_trace(5000 + i, median, sigma=sigma)
+            a = time.perf_counter()
+            levels, finish = kvc.plan_stream(sizes, trace, slo_s, median)
+            plan_s += time.perf_counter() - a
+            plans += 1
+            viol[d.n_levels] += finish[-1] > slo_s
+            share += np.bincount(levels, minlength=d.n_levels)
+            for lv in range(d.n_levels):
+                _, f = kvc.plan_stream(sizes[:, lv:lv + 1], trace, slo_s, median)
+                viol[lv] += f[-1] > slo_s
+        share /= share.sum()
+        res["scenarios"][f"link_fits_level{ref}"] = {
+            "median_link_GBps": round(median / 1e9, 3),
+            "adaptive": {"violation_rate": round(viol[d.n_levels] / n_traces, 4),
+                         "level_share": [round(float(x), 4) for x in share],
+                         "mean_level": round(float((share * np.arange(d.n_levels)).sum()), 4)},
+            "fixed_violation_rate": {str(lv): round(viol[lv] / n_traces, 4)
+                                     for lv in range(d.n_levels)},
+        }
+    res["plan_us"] = round(plan_s / plans * 1e6, 2)
+    log(f"level controller: {res['scenarios']}")
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -304,6 +355,7 @@ def main() -> int:
     torch.cuda.synchronize()
 
     restore = measure_restore(kvc, d, tables, enc, cfg, out)
+    controller = measure_controller(kvc, d, tables, kv_dev, cfg)
 
     traffic, traffic_note = measured_traffic()
     valu_insts = measured_valu_insts()
@@ -378,6 +430,7 @@ def main() -> int:
         },
         "decoded_finite": decoded_ok,
         "restore": restore,
+        "level_controller": controller,
         "sha256": {"kv_fp16": sha256_of(kv), "profile_kv_fp16": sha256_of(kvp)},
     }
 

@@ -226,6 +226,41 @@ kvc_status kvc_restore(const kvc_codec_desc *d, const void *tables, const kvc_ho
                        uint64_t ws_bytes, int32_t *dev_status, hipStream_t compute,
                        hipStream_t copy, hipEvent_t *batch_done);
 
+/* ---------------------------------------------------- per-chunk level choice */
+/* One piece of a piecewise-constant bandwidth trace: from start_s (seconds,
+ * increasing; the first is 0) until the next piece's start (the last piece
+ * lasts forever) the link moves bytes_per_s (> 0) bytes per second. */
+typedef struct {
+  double start_s;
+  double bytes_per_s;
+} kvc_bw_piece;
+
+/*
+ * Per-chunk compression-level choice while streaming a context (CacheGen
+ * page, 核心方法, online streaming paragraph: each chunk's level is chosen
+ * from the previous chunk's measured throughput so that the remaining chunks
+ * fit the TTFT SLO at the best quality; 关键观察, assumption 1: the estimate
+ * lags by at most one chunk).  Host-only; simulates sending the chunks one
+ * after another over `trace`, from time 0:
+ *  - before chunk i the bandwidth estimate is init_bytes_per_s for i = 0,
+ *    else chunk i-1's bytes / its transfer time (kept as it was if that
+ *    time rounds to 0);
+ *  - chunk i takes the lowest level index l (levels are ordered from best
+ *    to worst quality) with  t + (sum over j >= i of chunk_bytes[j][l]) /
+ *    estimate <= slo_s;  if no level fits, the level with the fewest
+ *    remaining bytes (lowest index on a tie);
+ *  - the chunk's bytes then move through the trace's pieces from time t.
+ * chunk_bytes: host [n_chunks][n_levels] container sizes; levels_out: host
+ * [n_chunks]; finish_s_out: host [n_chunks], each chunk's arrival time.  All
+ * arithmetic is IEEE binary64 in the order written above.  Errors:
+ * KVC_ERR_INVALID_ARG (null pointer, n_levels not in 1..255, a rate or the
+ * estimate not positive and finite, pieces not starting at 0 or not
+ * increasing, slo_s not finite).
+ */
+kvc_status kvc_plan_stream(const uint64_t *chunk_bytes, uint32_t n_chunks, uint32_t n_levels,
+                           const kvc_bw_piece *trace, uint32_t n_pieces, double slo_s,
+                           double init_bytes_per_s, uint8_t *levels_out, double *finish_s_out);
+
 /*
  * Debug form of kvc_decode: same kernels, but writes the decoded symbols
  * (u8: anchor 0..255, delta q + M) to sym_out [L][2][T_total][C] instead of

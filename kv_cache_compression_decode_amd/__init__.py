@@ -38,6 +38,7 @@ EXPORTED = (
     "kvc_profile_ws_bytes", "kvc_profile", "kvc_container_bound", "kvc_encode_bound",
     "kvc_encode_ws_bytes", "kvc_encode", "kvc_decode_ws_bytes", "kvc_decode",
     "kvc_decode_index", "kvc_decode_symbols", "kvc_restore_staging_bytes", "kvc_restore",
+    "kvc_plan_stream",
 )
 
 
@@ -147,6 +148,8 @@ def lib():
     L.kvc_restore_staging_bytes.restype = u64
     L.kvc_restore.argtypes = [dp, vp, vp, u32, u32, vp, u32, vp, u64, vp, u64, vp, vp, vp, vp]
     L.kvc_restore.restype = ctypes.c_int
+    L.kvc_plan_stream.argtypes = [vp, u32, u32, vp, u32, ctypes.c_double, ctypes.c_double, vp, vp]
+    L.kvc_plan_stream.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -471,3 +474,32 @@ def restore(desc: CodecDesc, tables: torch.Tensor, chunks: Sequence[HostChunk], 
     restore_async(desc, tables, chunks, out, rws, stream)
     read_status(rws.status, "kvc_restore")
     return out
+
+
+# ------------------------------------------------------ per-chunk level choice
+class BwPiece(ctypes.Structure):
+    """kvc_bw_piece: from start_s on, the link moves bytes_per_s."""
+    _fields_ = [("start_s", ctypes.c_double), ("bytes_per_s", ctypes.c_double)]
+
+
+def plan_stream(chunk_bytes, trace: Sequence[Tuple[float, float]], slo_s: float,
+                init_bytes_per_s: float) -> Tuple[List[int], List[float]]:
+    """kvc_plan_stream: the level chosen for each chunk and its arrival time.
+    chunk_bytes: [n_chunks][n_levels] container sizes (best quality first);
+    trace: (start_s, bytes_per_s) pieces, the first at 0."""
+    import numpy as np
+
+    cb = np.ascontiguousarray(np.asarray(chunk_bytes, dtype=np.uint64))
+    if cb.ndim != 2:
+        raise ValueError("chunk_bytes must be [n_chunks][n_levels]")
+    n, L = cb.shape
+    tr = (BwPiece * max(len(trace), 1))()
+    for i, (t0, r) in enumerate(trace):
+        tr[i].start_s = float(t0)
+        tr[i].bytes_per_s = float(r)
+    levels = np.zeros(max(n, 1), dtype=np.uint8)
+    finish = np.zeros(max(n, 1), dtype=np.float64)
+    _check(lib().kvc_plan_stream(cb.ctypes.data, n, L, tr, len(trace), float(slo_s),
+                                 float(init_bytes_per_s), levels.ctypes.data,
+                                 finish.ctypes.data), "kvc_plan_stream")
+    return [int(x) for x in levels[:n]], [float(x) for x in finish[:n]]

@@ -232,3 +232,18 @@ def innovations(seed: int, m0: int, count: int, n_tokens: int) -> np.ndarray:
 
 def to_half_bits(v: float) -> int:
     return int(_load().kvs_to_half(float(v)))
+
+
+def bandwidth_trace(seed: int, median_bytes_per_s: float, sigma: float = 0.7,
+                    n_pieces: int = 128, min_s: float = 0.05,
+                    max_s: float = 0.4) -> List[tuple]:
+    """A seeded piecewise-constant link: pieces of U(min_s, max_s) seconds
+    at median * exp(sigma * N(0, 1)) bytes per second, the first at time 0
+    (the CacheGen page evaluates its streaming adaptation on random bandwidth
+    traces without describing them; this is a log-normal stand-in).
+    Returns [(start_s, bytes_per_s), ...]."""
+    rng = np.random.default_rng(seed)
+    durations = rng.uniform(min_s, max_s, n_pieces - 1)
+    starts = np.concatenate([[0.0], np.cumsum(durations)])
+    rates = median_bytes_per_s * np.exp(sigma * rng.standard_normal(n_pieces))
+    return [(float(a), float(b)) for a, b in zip(starts, rates)]
