@@ -237,6 +237,61 @@ def measure_controller(kvc, d, tables, kv_dev, cfg, n_traces: int = 500, slo_s: 
     return res
 
 
+def measure_multi(kvc, d, tables, kv_dev, cfg, n_req: int = 8, req_tokens: int = 2000,
+                  reps: int = 3) -> dict:
+    """Several requests at once: the context cut into n_req requests of
+    req_tokens tokens (two chunks each: 1,500 + 500), each encoded on its own
+    at levels (r mod 3, r+1 mod 3); decoded as one kvc_decode per request, and
+    as one kvc_decode_multi call for all their chunks, into per-request KV
+    caches.  Both must give the same bits."""
+    import torch
+
+    dev = tables.device
+    encs, outs_a, outs_b = [], [], []
+    for r in range(n_req):
+        kv_r = kv_dev[:, :, r * req_tokens:(r + 1) * req_tokens].contiguous()
+        n_ch = (req_tokens + cfg.chunk_tokens(0) - 1) // cfg.chunk_tokens(0)
+        encs.append(kvc.encode(d, tables, kv_r, [(r + i) % d.n_levels for i in range(n_ch)]))
+        del kv_r
+        outs_a.append(torch.zeros((cfg.n_layers, 2, req_tokens, cfg.n_channels),
+                                  dtype=torch.int16, device=dev))
+        outs_b.append(torch.zeros_like(outs_a[-1]))
+    refs = [kvc.chunk_refs(e) for e in encs]
+    wss = [kvc.DecodeWorkspace(d, len(rf), dev) for rf in refs]
+    chunks = [c for e, o in zip(encs, outs_b) for c in kvc.request_chunks(e, o)]
+    wsm = kvc.DecodeWorkspace(d, len(chunks), dev)
+
+    def one_by_one():
+        for rf, o, w in zip(refs, outs_a, wss):
+            kvc.decode_async(d, tables, rf, o, w)
+
+    def together():
+        kvc.decode_multi_async(d, tables, chunks, wsm)
+
+    res = {"requests": n_req, "tokens_per_request": req_tokens, "chunks": len(chunks)}
+    total = sum(o.numel() * 2 for o in outs_a)
+    for name, fn in (("per_request_calls", one_by_one), ("one_multi_call", together)):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        res[name] = {"ms": round(statistics.median(ms), 3),
+                     "decoded_GBps": round(total / (statistics.median(ms) * 1e-3) / 1e9, 2)}
+    for w in wss:
+        kvc.read_status(w.status, "kvc_decode")
+    kvc.read_status(wsm.status, "kvc_decode_multi")
+    res["same_bits"] = all(bool(torch.equal(x, y)) for x, y in zip(outs_a, outs_b))
+    res["speedup"] = round(res["per_request_calls"]["ms"] / res["one_multi_call"]["ms"], 3)
+    log(f"multi-request decode: {res}")
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -356,6 +411,7 @@ def main() -> int:
 
     restore = measure_restore(kvc, d, tables, enc, cfg, out)
     controller = measure_controller(kvc, d, tables, kv_dev, cfg)
+    multi = measure_multi(kvc, d, tables, kv_dev, cfg)
 
     traffic, traffic_note = measured_traffic()
     valu_insts = measured_valu_insts()
@@ -431,6 +487,7 @@ def main() -> int:
         "decoded_finite": decoded_ok,
         "restore": restore,
         "level_controller": controller,
+        "multi_request": multi,
         "sha256": {"kv_fp16": sha256_of(kv), "profile_kv_fp16": sha256_of(kvp)},
     }
 

@@ -83,6 +83,20 @@ typedef struct {
   uint32_t reserved;        /* 0 */
 } kvc_chunk_ref;
 
+/* One encoded chunk of one of several requests, for kvc_decode_multi: the
+ * fields of kvc_chunk_ref plus the request's own KV cache. */
+typedef struct {
+  const uint8_t *container; /* device pointer to the chunk's container */
+  uint64_t container_bytes; /* its size in bytes */
+  uint32_t first_token;     /* destination token offset in kv_out */
+  uint32_t n_tokens;        /* tokens in the chunk; must equal the header */
+  uint32_t level;           /* compression level; must equal the header */
+  uint32_t reserved;        /* 0 */
+  uint16_t *kv_out;         /* device: the request's KV cache [L][2][T_total][C] */
+  uint32_t T_total;         /* its token capacity */
+  uint32_t reserved2;       /* 0 */
+} kvc_request_chunk;
+
 /* One encoded chunk still in host memory, for kvc_restore. */
 typedef struct {
   const uint8_t *host_container; /* host pointer; pinned (hipHostMalloc) memory
@@ -189,6 +203,21 @@ kvc_status kvc_decode(const kvc_codec_desc *d, const void *tables, const kvc_chu
 kvc_status kvc_decode_index(const kvc_codec_desc *d, const void *tables,
                             const kvc_chunk_ref *chunks, uint32_t n_chunks, uint32_t *offsets_out,
                             void *ws, uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream);
+
+/*
+ * Decode chunks of several requests in one call (CacheGen page, 核心方法,
+ * online streaming paragraph: with concurrent requests the chunks are
+ * batched on the GPU).  Each chunk names its own KV cache; caches of one
+ * model share `tables`.  Chunks writing to the same kv_out must agree on
+ * T_total and have disjoint token ranges; different caches must not
+ * overlap in memory.  No padding: chunks of any lengths and positions mix
+ * freely.  Every chunk is decoded exactly as kvc_decode would (same kernels,
+ * same bits).  ws: kvc_decode_ws_bytes(d, n_chunks) bytes.
+ * Device errors: those of kvc_decode.
+ */
+kvc_status kvc_decode_multi(const kvc_codec_desc *d, const void *tables,
+                            const kvc_request_chunk *chunks, uint32_t n_chunks, void *ws,
+                            uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream);
 
 /* --------------------------------------------------------- streamed restore */
 /*

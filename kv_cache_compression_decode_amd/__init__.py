@@ -38,7 +38,7 @@ EXPORTED = (
     "kvc_profile_ws_bytes", "kvc_profile", "kvc_container_bound", "kvc_encode_bound",
     "kvc_encode_ws_bytes", "kvc_encode", "kvc_decode_ws_bytes", "kvc_decode",
     "kvc_decode_index", "kvc_decode_symbols", "kvc_restore_staging_bytes", "kvc_restore",
-    "kvc_plan_stream",
+    "kvc_plan_stream", "kvc_decode_multi",
 )
 
 
@@ -76,6 +76,22 @@ class ChunkRef(ctypes.Structure):
         ("n_tokens", ctypes.c_uint32),
         ("level", ctypes.c_uint32),
         ("reserved", ctypes.c_uint32),
+    ]
+
+
+class RequestChunk(ctypes.Structure):
+    """kvc_request_chunk: a chunk of one of several requests, with that
+    request's KV cache."""
+    _fields_ = [
+        ("container", ctypes.c_void_p),
+        ("container_bytes", ctypes.c_uint64),
+        ("first_token", ctypes.c_uint32),
+        ("n_tokens", ctypes.c_uint32),
+        ("level", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+        ("kv_out", ctypes.c_void_p),
+        ("T_total", ctypes.c_uint32),
+        ("reserved2", ctypes.c_uint32),
     ]
 
 
@@ -148,6 +164,8 @@ def lib():
     L.kvc_restore_staging_bytes.restype = u64
     L.kvc_restore.argtypes = [dp, vp, vp, u32, u32, vp, u32, vp, u64, vp, u64, vp, vp, vp, vp]
     L.kvc_restore.restype = ctypes.c_int
+    L.kvc_decode_multi.argtypes = [dp, vp, vp, u32, vp, u64, vp, vp]
+    L.kvc_decode_multi.restype = ctypes.c_int
     L.kvc_plan_stream.argtypes = [vp, u32, u32, vp, u32, ctypes.c_double, ctypes.c_double, vp, vp]
     L.kvc_plan_stream.restype = ctypes.c_int
     _lib = L
@@ -503,3 +521,46 @@ def plan_stream(chunk_bytes, trace: Sequence[Tuple[float, float]], slo_s: float,
                                  float(init_bytes_per_s), levels.ctypes.data,
                                  finish.ctypes.data), "kvc_plan_stream")
     return [int(x) for x in levels[:n]], [float(x) for x in finish[:n]]
+
+
+# ------------------------------------------------- several requests, one call
+def request_chunks(enc: Encoded, out: torch.Tensor,
+                   chunks: Optional[Sequence[int]] = None) -> List[RequestChunk]:
+    """RequestChunks of (a subset of) one request's Encoded context, each
+    going back to its own token range of that request's cache `out`."""
+    _kv_ptr(out)
+    ks = list(range(enc.n_chunks)) if chunks is None else list(chunks)
+    base = enc.blob.data_ptr()
+    res = []
+    for k in ks:
+        c = RequestChunk()
+        c.container = base + enc.offsets[k]
+        c.container_bytes = enc.offsets[k + 1] - enc.offsets[k]
+        c.first_token = k * enc.chunk_tokens
+        c.n_tokens = enc.n_tokens[k]
+        c.level = enc.levels[k]
+        c.reserved = 0
+        c.kv_out = out.data_ptr()
+        c.T_total = out.shape[2]
+        c.reserved2 = 0
+        res.append(c)
+    return res
+
+
+def decode_multi_async(desc: CodecDesc, tables: torch.Tensor, chunks: Sequence[RequestChunk],
+                       wsp: DecodeWorkspace, stream=None) -> None:
+    """Queue kvc_decode_multi: every chunk into its own request's cache."""
+    arr = (RequestChunk * max(len(chunks), 1))()
+    for i, c in enumerate(chunks):
+        arr[i] = c
+    _check(lib().kvc_decode_multi(ctypes.byref(desc), tables.data_ptr(), arr, len(chunks),
+                                  wsp.ws.data_ptr(), wsp.ws_bytes, wsp.status.data_ptr(),
+                                  _stream(stream)), "kvc_decode_multi")
+
+
+def decode_multi(desc: CodecDesc, tables: torch.Tensor, chunks: Sequence[RequestChunk],
+                 stream=None, wsp: Optional[DecodeWorkspace] = None) -> None:
+    if wsp is None:
+        wsp = DecodeWorkspace(desc, len(chunks), tables.device)
+    decode_multi_async(desc, tables, chunks, wsp, stream)
+    read_status(wsp.status, "kvc_decode_multi")

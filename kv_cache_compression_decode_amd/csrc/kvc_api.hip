@@ -17,8 +17,8 @@ hipError_t launch_load_groups(const DecodeGroup *host_groups, uint32_t n_groups,
                               DecodeGroup *dev_groups, hipStream_t stream);
 hipError_t launch_decode(const Desc &d, const ChunkInfo *dev_chunks, const DecodeGroup *groups,
                          uint32_t n_groups, uint32_t levels, uint32_t waves, const uint8_t *valid,
-                         const uint32_t *offsets, const uint8_t *tables, void *out,
-                         uint32_t T_total, bool symbols, int32_t *status, hipStream_t stream);
+                         const uint32_t *offsets, const uint8_t *tables, bool symbols,
+                         int32_t *status, hipStream_t stream);
 size_t decode_lds_bytes(uint32_t levels, uint32_t waves);
 hipError_t launch_encode(const Desc &d, const uint8_t *tables, const uint16_t *kv, uint32_t T,
                          const ChunkInfo *dev_chunks, uint32_t n_chunks,
@@ -100,10 +100,17 @@ uint64_t container_bound_n(const Desc &d, uint32_t n) {
 
 kvc_status hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
 
-kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc_chunk_ref *chunks,
-                         uint32_t n_chunks, void *out, uint32_t T_total, void *ws,
-                         uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream, int mode,
-                         uint32_t *offsets_out, bool reset_status = true) {
+// A chunk to decode and the output cache its values go to.
+struct OutChunk {
+  kvc_chunk_ref r;
+  void *out;   // [L][2][T][C] binary16 (values) or u8 (symbols)
+  uint32_t T;  // that cache's token capacity
+};
+
+kvc_status decode_chunks(const kvc_codec_desc *dd, const void *tables, const OutChunk *chunks,
+                         uint32_t n_chunks, void *ws, uint64_t ws_bytes, int32_t *dev_status,
+                         hipStream_t stream, int mode, uint32_t *offsets_out,
+                         bool reset_status = true) {
   // mode 0: values, 1: symbols, 2: index only
   if (!desc_ok(dd)) return KVC_ERR_INVALID_ARG;
   const Desc d = to_desc(dd);
@@ -111,8 +118,9 @@ kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc
     return KVC_ERR_INVALID_ARG;
   if (n_chunks > 65535) return KVC_ERR_SHAPE;
   if (n_chunks && !chunks) return KVC_ERR_INVALID_ARG;
-  if (mode != 2 && n_chunks && (!out || !aligned(out, mode == 0 ? 2 : 1)))
-    return KVC_ERR_INVALID_ARG;
+  const uint32_t esz = mode == 0 ? 2 : 1;
+  for (uint32_t k = 0; mode != 2 && k < n_chunks; ++k)
+    if (!chunks[k].out || !aligned(chunks[k].out, esz)) return KVC_ERR_INVALID_ARG;
   if (mode == 2 && n_chunks && (!offsets_out || !aligned(offsets_out, 4)))
     return KVC_ERR_INVALID_ARG;
   const WsLayout w = ws_layout(d, n_chunks, false);
@@ -120,13 +128,17 @@ kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc
   if (ws_bytes < w.total) return KVC_ERR_CAPACITY;
   const uint64_t S = n_streams(d);
   std::vector<ChunkInfo> info(n_chunks);
-  std::vector<std::pair<uint32_t, uint32_t>> ranges(n_chunks);
+  struct Range {
+    uintptr_t out;
+    uint32_t T, a, b;
+  };
+  std::vector<Range> ranges(n_chunks);
   for (uint32_t k = 0; k < n_chunks; ++k) {
-    const kvc_chunk_ref &c = chunks[k];
+    const kvc_chunk_ref &c = chunks[k].r;
     if (!c.container || !aligned(c.container, 4)) return KVC_ERR_INVALID_ARG;
     if (c.level >= d.nlev || c.reserved != 0) return KVC_ERR_INVALID_ARG;
     if (c.n_tokens < 1 || c.n_tokens > d.chunk) return KVC_ERR_SHAPE;
-    if (mode != 2 && (uint64_t)c.first_token + c.n_tokens > T_total) return KVC_ERR_SHAPE;
+    if (mode != 2 && (uint64_t)c.first_token + c.n_tokens > chunks[k].T) return KVC_ERR_SHAPE;
     if (c.container_bytes < kHdrBytes + kRecBytes * S) return KVC_ERR_SHAPE;
     // decode reads containers through 32-bit bounded buffer resources
     if (c.container_bytes > 0xFFFFFFFFull) return KVC_ERR_SHAPE;
@@ -136,14 +148,25 @@ kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc
     info[k].first_token = c.first_token;
     info[k].n_tokens = c.n_tokens;
     info[k].level = c.level;
-    info[k].pad0 = 0;
-    info[k].pad1 = 0;
-    ranges[k] = {c.first_token, c.first_token + c.n_tokens};
+    info[k].out_tokens = mode == 2 ? 0 : chunks[k].T;
+    info[k].out = mode == 2 ? nullptr : chunks[k].out;
+    ranges[k] = {(uintptr_t)chunks[k].out, chunks[k].T, c.first_token, c.first_token + c.n_tokens};
   }
-  if (mode != 2) {
-    std::sort(ranges.begin(), ranges.end());
-    for (uint32_t k = 1; k < n_chunks; ++k)
-      if (ranges[k].first < ranges[k - 1].second) return KVC_ERR_SHAPE;
+  if (mode != 2 && n_chunks) {
+    // chunks sharing an output cache: one token capacity, disjoint token
+    // ranges; distinct output caches must not overlap in memory
+    std::sort(ranges.begin(), ranges.end(), [](const Range &x, const Range &y) {
+      return x.out != y.out ? x.out < y.out : x.a < y.a;
+    });
+    const uint64_t row_bytes = 2ull * d.L * d.C * esz;  // [L][2] rows of C per token
+    for (uint32_t k = 1; k < n_chunks; ++k) {
+      const Range &p = ranges[k - 1], &q = ranges[k];
+      if (q.out == p.out) {
+        if (q.T != p.T || q.a < p.b) return KVC_ERR_SHAPE;
+      } else if (q.out < p.out + row_bytes * p.T) {
+        return KVC_ERR_SHAPE;
+      }
+    }
   }
   // Decode groups (values / symbols): the chunk table is ordered by level so
   // that the two chunks a wave decodes together mostly share an alphabet
@@ -196,9 +219,21 @@ kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc
   e = launch_load_groups(groups.data(), (uint32_t)groups.size(), dgr, stream);
   if (e != hipSuccess) return KVC_ERR_HIP;
   e = launch_decode(d, dch, dgr, (uint32_t)groups.size(), levels, waves, base + w.valid, offs,
-                    static_cast<const uint8_t *>(tables), out, T_total, mode == 1, dev_status,
-                    stream);
+                    static_cast<const uint8_t *>(tables), mode == 1, dev_status, stream);
   return hip_status(e);
+}
+
+// Every chunk into one output cache.
+kvc_status decode_common(const kvc_codec_desc *dd, const void *tables, const kvc_chunk_ref *chunks,
+                         uint32_t n_chunks, void *out, uint32_t T_total, void *ws,
+                         uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream, int mode,
+                         uint32_t *offsets_out, bool reset_status = true) {
+  if (n_chunks && !chunks) return KVC_ERR_INVALID_ARG;
+  if (n_chunks > 65535) return KVC_ERR_SHAPE;
+  std::vector<OutChunk> v(n_chunks);
+  for (uint32_t k = 0; k < n_chunks; ++k) v[k] = {chunks[k], out, T_total};
+  return decode_chunks(dd, tables, v.data(), n_chunks, ws, ws_bytes, dev_status, stream, mode,
+                       offsets_out, reset_status);
 }
 
 // Largest batch of a restore: the sum of its containers, each rounded up to
@@ -346,8 +381,8 @@ kvc_status kvc_encode(const kvc_codec_desc *dd, const void *tables, const uint16
     info[k].first_token = (uint32_t)t0;
     info[k].n_tokens = (uint32_t)std::min<uint64_t>(d.chunk, T - t0);
     info[k].level = chunk_levels[k];
-    info[k].pad0 = 0;
-    info[k].pad1 = 0;
+    info[k].out_tokens = 0;
+    info[k].out = nullptr;
   }
   hipError_t e = launch_reset_status(dev_status, stream);
   if (e != hipSuccess) return KVC_ERR_HIP;
@@ -415,6 +450,22 @@ kvc_status kvc_decode_index(const kvc_codec_desc *d, const void *tables,
                             void *ws, uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream) {
   return decode_common(d, tables, chunks, n_chunks, nullptr, 0, ws, ws_bytes, dev_status, stream,
                        2, offsets_out);
+}
+
+kvc_status kvc_decode_multi(const kvc_codec_desc *d, const void *tables,
+                            const kvc_request_chunk *chunks, uint32_t n_chunks, void *ws,
+                            uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream) {
+  if (n_chunks && !chunks) return KVC_ERR_INVALID_ARG;
+  if (n_chunks > 65535) return KVC_ERR_SHAPE;
+  std::vector<OutChunk> v(n_chunks);
+  for (uint32_t k = 0; k < n_chunks; ++k) {
+    const kvc_request_chunk &c = chunks[k];
+    if (c.reserved2 != 0) return KVC_ERR_INVALID_ARG;
+    v[k] = {{c.container, c.container_bytes, c.first_token, c.n_tokens, c.level, c.reserved},
+            c.kv_out, c.T_total};
+  }
+  return decode_chunks(d, tables, v.data(), n_chunks, ws, ws_bytes, dev_status, stream, 0,
+                       nullptr);
 }
 
 uint64_t kvc_restore_staging_bytes(const kvc_host_chunk *chunks, uint32_t n_chunks,

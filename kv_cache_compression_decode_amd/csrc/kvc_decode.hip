@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
     Desc d, const ChunkInfo *__restrict__ ci, const DecodeGroup *__restrict__ groups,
     uint32_t n_groups, uint32_t n_units, const uint8_t *__restrict__ valid,
     const uint32_t *__restrict__ offsets, const uint8_t *__restrict__ tables,
-    void *__restrict__ out, uint32_t T_total, int32_t *status) {
+    int32_t *status) {
   // ---- which (unit, chunk group) this block owns (XCD-aware numbering)
   const uint32_t id = blockIdx.x;
   const uint32_t local = id / kXcds;
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
         __asm__ volatile("" : "+v"(ra));
         s.ring = (lds_u32 *)(uintptr_t)ra;
       }
-      ob[q] = (gbyte *)out;
+      ob[q] = (gbyte *)ci[k].out;
       s.dbase = lds_addr(sD) + 2 * lane_col(lane);
       s.dbaseM = s.dbase;
       s.rem = 0;
@@ -453,7 +453,8 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
       src[q].rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)c.cont, (short)0,
                                                       (int)(uint32_t)c.cont_bytes, kBufferWord3);
       src[q].ubase = (uint32_t)(kHdrBytes + (uint64_t)kRecBytes * S) + offsets[(uint64_t)k * S + m0];
-      ob[q] = uniform_ptr((gbyte *)out + (((uint64_t)row * T_total + c.first_token) * d.C + c0) * esz);
+      ob[q] = uniform_ptr((gbyte *)c.out +
+                          (((uint64_t)row * c.out_tokens + c.first_token) * d.C + c0) * esz);
       s.ahat = 0.0f;
       // start of the reading rule: every lane asks for its blocks 0, 1 and 2
       // (block outer, lane inner); 0 and 1 fill the ring, 2 is held.  A lane
@@ -544,20 +545,18 @@ size_t decode_lds_bytes(uint32_t levels, uint32_t waves) {
 
 hipError_t launch_decode(const Desc &d, const ChunkInfo *dev_chunks, const DecodeGroup *groups,
                          uint32_t n_groups, uint32_t levels, uint32_t waves, const uint8_t *valid,
-                         const uint32_t *offsets, const uint8_t *tables, void *out,
-                         uint32_t T_total, bool symbols, int32_t *status, hipStream_t stream) {
+                         const uint32_t *offsets, const uint8_t *tables, bool symbols,
+                         int32_t *status, hipStream_t stream) {
   const uint32_t ncb = (d.C + kWave - 1) / kWave;
   const uint32_t n_units = 2u * d.L * ncb;
   const uint64_t blocks = (uint64_t)((n_units + kXcds - 1) / kXcds) * kXcds * n_groups;
   const size_t lds = decode_lds_bytes(levels, waves);
   if (symbols)
     hipLaunchKernelGGL(k_decode<true>, dim3((uint32_t)blocks), dim3(waves * kWave), lds, stream,
-                       d, dev_chunks, groups, n_groups, n_units, valid, offsets, tables, out,
-                       T_total, status);
+                       d, dev_chunks, groups, n_groups, n_units, valid, offsets, tables, status);
   else
     hipLaunchKernelGGL(k_decode<false>, dim3((uint32_t)blocks), dim3(waves * kWave), lds, stream,
-                       d, dev_chunks, groups, n_groups, n_units, valid, offsets, tables, out,
-                       T_total, status);
+                       d, dev_chunks, groups, n_groups, n_units, valid, offsets, tables, status);
   return hipGetLastError();
 }
 

@@ -43,8 +43,8 @@ struct ChunkInfo {
   uint32_t first_token;    // destination token (decode) / source token (encode)
   uint32_t n_tokens;
   uint32_t level;
-  uint32_t pad0;
-  uint64_t pad1;
+  uint32_t out_tokens;     // decode: token capacity T of the chunk's output cache
+  void *out;               // decode: the chunk's output cache [L][2][T][C]
 };
 static_assert(sizeof(ChunkInfo) == 48, "ChunkInfo layout");
 

@@ -173,3 +173,40 @@ def test_restore_synchronous_errors(L):
     bad = _host_chunks([size] * 3, [0, 10, 20])
     bad[1].host_container = None
     assert call(bad, 3, 2) == kvc.ERR_INVALID_ARG
+
+
+def test_decode_multi_synchronous_errors(L):
+    """kvc_decode_multi: chunks of one cache need one capacity and disjoint
+    ranges; distinct caches must not overlap in memory; reserved fields 0."""
+    d = kvc.make_desc(2, 64)
+    S = d.n_streams
+    size = 64 + 16 * S + 4 * S
+    status = ctypes.c_int32()
+    cache_bytes = 2 * 2 * 64 * 2  # per token: [L][2] rows of C binary16
+
+    def chunks(spec):
+        arr = (kvc.RequestChunk * len(spec))()
+        for i, (out, T, t0) in enumerate(spec):
+            arr[i].container = 4096 * (i + 1)
+            arr[i].container_bytes = size
+            arr[i].first_token = t0
+            arr[i].n_tokens = 10
+            arr[i].kv_out = out
+            arr[i].T_total = T
+        return arr
+
+    def call(arr):
+        return L.kvc_decode_multi(ctypes.byref(d), ctypes.c_void_p(256), arr, len(arr),
+                                  ctypes.c_void_p(256), 1 << 30, ctypes.byref(status), None)
+
+    A, B = 1 << 20, (1 << 20) + 100 * cache_bytes  # two caches of 100 tokens, back to back
+    assert call(chunks([(A, 100, 0), (A, 100, 5)])) == kvc.ERR_SHAPE     # overlap in one cache
+    assert call(chunks([(A, 100, 0), (A, 120, 50)])) == kvc.ERR_SHAPE    # one cache, two capacities
+    assert call(chunks([(A, 100, 0), (B - 2, 100, 0)])) == kvc.ERR_SHAPE  # caches overlap in memory
+    assert call(chunks([(A, 100, 95)])) == kvc.ERR_SHAPE                 # past the capacity
+    bad = chunks([(A, 100, 0)])
+    bad[0].reserved2 = 1
+    assert call(bad) == kvc.ERR_INVALID_ARG
+    bad = chunks([(A, 100, 0)])
+    bad[0].kv_out = None
+    assert call(bad) == kvc.ERR_INVALID_ARG
