@@ -226,8 +226,8 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_stats(
     uint32_t shifts = 0;
     float ahat = 0.0f;
     uint32_t g = 0;
-    for (uint32_t j = 0; j < n; ++j) {
-      const float v = h2f(x[(uint64_t)j * ld]);
+    bool damaged = false;
+    for_each_token<kTokenBatch>(x, ld, 0, 1, n, [&](float v) {
       uint32_t f;
       if (g == 0) {
         const uint32_t qa = quant_anchor(v, lo, sa);
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_stats(
       }
       g = g + 1 == d.G ? 0 : g + 1;
       if (f == 0 || f > kTot) {  // damaged tables
-        set_status(status, KVC_ERR_CORRUPT_STREAM);
+        damaged = true;
         f = 1;
       }
       range = (range >> kPrec) * f;
@@ -247,7 +247,8 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_stats(
         range <<= 8;
         ++shifts;
       }
-    }
+    });
+    if (damaged) set_status(status, KVC_ERR_CORRUPT_STREAM);
     uint32_t *rec = reinterpret_cast<uint32_t *>(records + ((uint64_t)k * S + m) * kRecBytes);
     rec[0] = __builtin_bit_cast(uint32_t, lo);
     rec[1] = __builtin_bit_cast(uint32_t, sa);
@@ -373,9 +374,10 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
     const uint32_t n = c.n_tokens;
     float ahat = 0.0f;
     uint32_t g = 0;
-    for (uint32_t j = 0; j < n; ++j) {
-      // before token j: a reader ring with at most 8 bytes (anchor) or fewer
-      // than 2 bytes (other tokens) takes its next block and asks for one
+    for_each_token<kTokenBatch>(x, ld, 0, 1, n, [&](float v) {
+      // before this token: a reader ring with at most 8 bytes (anchor) or
+      // fewer than 2 bytes (other tokens) takes its next block and asks for
+      // one
       {
         const uint32_t ahead = W - R;
         const bool need = g == 0 ? ahead <= 8u : ahead < 2u;
@@ -389,7 +391,6 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
         cnt += (uint32_t)__builtin_popcountll(mask);
         sink.cnt = cnt;
       }
-      const float v = h2f(x[(uint64_t)j * ld]);
       uint32_t cs, f;
       if (g == 0) {
         const uint32_t qa = quant_anchor(v, lo, sa);
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
       g = g + 1 == d.G ? 0 : g + 1;
       if (f == 0 || f > kTot) f = 1;  // damaged tables: already reported by the stats pass
       R += enc.encode(cs, f, sink);
-    }
+    });
     enc.finish(sink);
     sink.flush();
     if (sink.window) {

@@ -168,29 +168,48 @@ __device__ inline int32_t quant_delta(float d, float dl, int32_t M) {
 
 // Stream statistics: lo, sa (anchor scale) and maxabs of the closed-loop
 // deltas.  Returns false if a value is not finite.
+// Visits the tokens first, first + step, ... (< n) of a lane's column x
+// (row stride ld elements) in order, calling f(value).  The values are
+// loaded kBatch at a time, so a wave waits for memory once per batch
+// rather than once per token.
+template <uint32_t kBatch, class F>
+__device__ inline void for_each_token(const uint16_t *__restrict__ x, uint64_t ld, uint32_t first,
+                                      uint32_t step, uint32_t n, F &&f) {
+  uint32_t j = first;
+  for (; j + (kBatch - 1) * step < n; j += kBatch * step) {
+    uint16_t v[kBatch];
+#pragma unroll
+    for (uint32_t u = 0; u < kBatch; ++u) v[u] = x[(uint64_t)(j + u * step) * ld];
+#pragma unroll
+    for (uint32_t u = 0; u < kBatch; ++u) f(h2f(v[u]));
+  }
+  for (; j < n; j += step) f(h2f(x[(uint64_t)j * ld]));
+}
+constexpr uint32_t kTokenBatch = 16;
+
 __device__ inline bool stream_stats(const uint16_t *__restrict__ x, uint64_t ld, uint32_t n,
                                     uint32_t G, float &lo_out, float &sa_out, float &maxabs_out) {
   float lo = h2f(x[0]);
   float hi = lo;
-  for (uint32_t j = G; j < n; j += G) {
-    const float v = h2f(x[(uint64_t)j * ld]);
+  for_each_token<kTokenBatch>(x, ld, G, G, n, [&](float v) {
     if (v < lo) lo = v;
     if (v > hi) hi = v;
-  }
+  });
   const float sa = (hi - lo) / 255.0f;
   bool finite = true;
   float maxabs = 0.0f;
   float ahat = 0.0f;
-  for (uint32_t j = 0; j < n; ++j) {
-    const float v = h2f(x[(uint64_t)j * ld]);
+  uint32_t g = 0;  // position in the group (0: the anchor)
+  for_each_token<kTokenBatch>(x, ld, 0, 1, n, [&](float v) {
     finite = finite && is_finite(v);
-    if (j % G == 0) {
+    if (g == 0) {
       ahat = __builtin_fmaf((float)quant_anchor(v, lo, sa), sa, lo);
     } else {
       const float a = __builtin_fabsf(v - ahat);
       if (a > maxabs) maxabs = a;
     }
-  }
+    g = g + 1 == G ? 0 : g + 1;
+  });
   lo_out = lo;
   sa_out = sa;
   maxabs_out = maxabs;
