@@ -301,6 +301,9 @@ def main() -> int:
     ap.add_argument("--oracle-chunks", type=int, default=11,
                     help="chunks decoded by the CPU oracle for the baseline and the bit-exact check")
     ap.add_argument("--no-oracle", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="skip the restore, level-choice and multi-request measurements "
+                         "(profiler passes of the decode kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer three times (HBM counter calibration)")
     args = ap.parse_args()
@@ -409,9 +412,11 @@ def main() -> int:
     copy_gbs = copy_rate(out)
     torch.cuda.synchronize()
 
-    restore = measure_restore(kvc, d, tables, enc, cfg, out)
-    controller = measure_controller(kvc, d, tables, kv_dev, cfg)
-    multi = measure_multi(kvc, d, tables, kv_dev, cfg)
+    restore = controller = multi = None
+    if not args.decode_only:
+        restore = measure_restore(kvc, d, tables, enc, cfg, out)
+        controller = measure_controller(kvc, d, tables, kv_dev, cfg)
+        multi = measure_multi(kvc, d, tables, kv_dev, cfg)
 
     traffic, traffic_note = measured_traffic()
     valu_insts = measured_valu_insts()
