@@ -495,6 +495,15 @@ def main() -> int:
         "multi_request": multi,
         "sha256": {"kv_fp16": sha256_of(kv), "profile_kv_fp16": sha256_of(kvp)},
     }
+    props = torch.cuda.get_device_properties(dev)
+    result["device"] = {
+        "name": props.name, "arch": getattr(props, "gcnArchName", ""),
+        "compute_units": props.multi_processor_count,
+    }
+    for key, attr in (("max_engine_clock_MHz", "clock_rate"),
+                      ("max_memory_clock_MHz", "memory_clock_rate")):
+        if getattr(props, attr, 0):  # not reported by every runtime
+            result["device"][key] = round(getattr(props, attr) / 1000)
 
     # ---- CPU oracle: bit-exact check on a sample of chunks + its own rate
     if not args.no_oracle:
@@ -530,6 +539,22 @@ def main() -> int:
                       f"{sample_bytes / 1e9:.2f} GB of binary16) in {cpu_s:.2f} s",
         }
         log(f"oracle decode {sample_bytes / 1e9:.2f} GB in {cpu_s:.1f} s; bit_exact={exact}")
+        # the same oracle on one core, on its first chunk
+        threads = oracle.get_threads()
+        oracle.set_threads(1)
+        one = np.zeros((cfg.n_layers, 2, cfg.chunk_tokens(0), cfg.n_channels), np.uint16)
+        t0 = time.perf_counter()
+        oracle.decode_chunk_into(od, otb, conts[0], 0, cfg.chunk_tokens(0), levels[0], one)
+        one_s = time.perf_counter() - t0
+        oracle.set_threads(threads)
+        one_bytes = one.size * 2
+        result["cpu_baseline_one_core"] = {
+            "value": round(one_bytes / one_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"oracle decode of chunk 0 ({cfg.chunk_tokens(0)} tokens, "
+                      f"{one_bytes / 1e9:.2f} GB of binary16) in {one_s:.2f} s on one thread",
+        }
+        log(f"oracle on one core: {one_bytes / 1e9:.2f} GB in {one_s:.1f} s")
     print(json.dumps(result), flush=True)
     return 0
 
