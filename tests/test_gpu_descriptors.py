@@ -48,3 +48,32 @@ def test_descriptor_bit_exact(name):
     want = oracle.decode(od, otb, ocont, levels, T)
     got = kvc.decode(d, tables, kvc.chunk_refs(enc), T).cpu().numpy().view(np.uint16)
     np.testing.assert_array_equal(got, want)
+
+
+def test_many_chunks_in_one_call():
+    """140 chunks of 10 tokens: the chunk table reaches the device in three
+    batches of at most 64 and each channel block's chunks split into
+    several groups (at most four pairs per wave); tables, containers and the
+    decoded KV must still equal the oracle's, and so must a decode of the
+    chunks in reverse order through kvc_decode_multi."""
+    L, C, T, G, chunk = 2, 64, 1400, 5, 10
+    print("\n[gpu descriptor] 140 chunks", flush=True)
+    cfg = synth.small_config(L, C, T, n_levels=3, index=78)
+    kv = synth.make_kv(cfg)
+    kvp = synth.make_profile_kv(cfg)
+    bits = ((6, 5, 4), (5, 4, 3), (4, 3, 2))
+    levels = [(k * 7) % 3 for k in range(T // chunk)]
+    od = oracle.Desc(L, C, G, chunk, 8, bits, 15)
+    d = kvc.make_desc(L, C, bits, group_tokens=G, chunk_tokens=chunk)
+    otb = oracle.profile(od, kvp)
+    tables = kvc.profile(d, _t(kvp))
+    ocont = oracle.encode(od, otb, kv, levels)
+    enc = kvc.encode(d, tables, _t(kv), levels)
+    for k, c in enumerate(ocont):
+        np.testing.assert_array_equal(enc.container(k).cpu().numpy(), c)
+    want = oracle.decode(od, otb, ocont, levels, T)
+    got = kvc.decode(d, tables, kvc.chunk_refs(enc), T).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, want)
+    out = torch.zeros((L, 2, T, C), dtype=torch.int16, device=DEV)
+    kvc.decode_multi(d, tables, kvc.request_chunks(enc, out)[::-1])
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint16), want)
