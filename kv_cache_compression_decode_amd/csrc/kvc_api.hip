@@ -169,10 +169,10 @@ kvc_status decode_chunks(const kvc_codec_desc *dd, const void *tables, const Out
     }
   }
   // Decode groups (values / symbols): the chunk table is ordered by level so
-  // that the two chunks a wave decodes together mostly share an alphabet
-  // size, then split into near-equal groups of whole pairs, each decoded by
-  // one workgroup per (row, channel block) whose waves take at most
-  // kMaxRounds pairs each.  The index-only call keeps the caller's order.
+  // that a group's chunks span few levels (fewer delta models to stage),
+  // then split into near-equal groups, each decoded by one workgroup per
+  // (row, channel block) whose waves take at most kMaxRounds chunks each.
+  // The index-only call keeps the caller's order.
   std::vector<DecodeGroup> groups;
   uint32_t levels = 1, waves = 1;
   if (mode != 2 && n_chunks) {
@@ -188,17 +188,16 @@ kvc_status decode_chunks(const kvc_codec_desc *dd, const void *tables, const Out
         wmax = w;
         break;
       }
-    const uint32_t pairs = (n_chunks + 1) / 2;
-    const uint32_t ng = (pairs + wmax * kMaxRounds - 1) / (wmax * kMaxRounds);
+    const uint32_t ng = (n_chunks + wmax * kMaxRounds - 1) / (wmax * kMaxRounds);
     for (uint32_t gi = 0; gi < ng; ++gi) {
-      const uint32_t a = 2 * (uint32_t)((uint64_t)pairs * gi / ng);
-      const uint32_t b = std::min<uint32_t>(n_chunks, 2 * (uint32_t)((uint64_t)pairs * (gi + 1) / ng));
+      const uint32_t a = (uint32_t)((uint64_t)n_chunks * gi / ng);
+      const uint32_t b = (uint32_t)((uint64_t)n_chunks * (gi + 1) / ng);
       DecodeGroup g{};
       g.start = a;
       g.count = b - a;
       for (uint32_t i = a; i < b; ++i) g.level |= 1u << info[i].level;
       levels = std::max<uint32_t>(levels, (uint32_t)__builtin_popcount(g.level));
-      waves = std::max<uint32_t>(waves, std::min<uint32_t>(wmax, (g.count + 1) / 2));
+      waves = std::max<uint32_t>(waves, std::min<uint32_t>(wmax, g.count));
       groups.push_back(g);
     }
   }

@@ -11,19 +11,19 @@
 //    of chunks (normally every chunk of the call), and stages the 64
 //    channels' anchor models and their delta models of every level the group
 //    uses into LDS once;
-//  * its W waves take the group's chunks two at a time (the host sorts a
-//    group's chunks by level, so the two chunks of a pair mostly share one
-//    alphabet size); every lane decodes the streams of its channel in both
-//    chunks in lockstep, so each lane runs two independent dependency chains
-//    and one LDS copy of the models serves every chunk of the group;
+//  * its W waves take the group's chunks one at a time: every lane decodes
+//    the stream of its channel in the wave's chunk, and one LDS copy of the
+//    models serves every chunk of the group.  One stream per wave rather
+//    than several per lane in lockstep: a wave waiting for an LDS read then
+//    holds up only its own stream, and the SIMDs switch between the
+//    workgroups' waves (about 22 per CU for an 11-chunk call);
 //  * all lanes of a wave are at the same token, so the anchor/delta switch
 //    and the search depth are wave-uniform, and the 64 results of a token are
 //    64 consecutive channels: one coalesced 128-byte store per stream,
 //    addressed from a wave-uniform base;
 //  * a symbol is the largest k with r * cum[k] <= code, found by binary
 //    search with one 24-bit multiply per probe (no division): 8 steps for
-//    anchors, b steps for a b-bit delta alphabet, the two streams' probes
-//    interleaved;
+//    anchors, b steps for a b-bit delta alphabet;
 //  * the models are staged row-interleaved (entry i of lane l in row i, a
 //    128-byte row per entry index), so a probe is a constant offset from the
 //    lane's current row and the symbol index is a shift of the address;
@@ -52,7 +52,6 @@ namespace kvc {
 namespace {
 
 constexpr uint32_t kMaxWaves = kDecodeMaxWaves;  // waves per workgroup (host picks W <= this)
-constexpr uint32_t kSlots = 2;                   // streams per lane
 constexpr uint32_t kARows = 258;    // staged anchor model rows: cum[0..256] + pad
 constexpr uint32_t kDRows = 66;     // staged delta model rows: cum[0..63] + 2 pads
 constexpr uint32_t kRowBytes = 2 * kWave;  // one u16 entry for each of the 64 lanes
@@ -122,7 +121,6 @@ struct Stream {
                         // aligned register pair, the load's own destination)
   uint32_t rem;         // the stream's blocks the lane has not asked for
   uint32_t hpos;        // payload block number of the held block
-  uint32_t n;
   int32_t M;
   uint32_t dbase;       // LDS byte address of this lane's delta row 0
   uint32_t dbaseM;      // dbase + M rows: (addr - dbaseM) >> 7 is q = s - M
@@ -172,92 +170,71 @@ __device__ inline void refill(Stream &s, Source &src) {
 // block (rare).
 __device__ inline void ensure(Stream &s, Source &src) { advance(s, src, s.nrpos < s.nwlim); }
 
-// Keeps the instruction scheduler from moving code across this point, so that
-// the LDS reads of a lane's streams are issued back to back and waited for
-// together rather than one after the other.
-#define PAIR_BARRIER() __builtin_amdgcn_sched_barrier(0)
+// Keeps the instruction scheduler from moving code across this point: each
+// binary-search probe is read, then compared, with nothing hoisted between.
+#define SEARCH_BARRIER() __builtin_amdgcn_sched_barrier(0)
 
-// One token of Q streams of a lane, in lockstep: range decode, dequantize.
-// The symbol is the largest k with r * cum[k] <= code (the division-free form
-// of cum[k] <= floor(code / r)); kSteps binary-search steps cover indices
+// One token of a lane's stream: range decode, dequantize.  The symbol is the
+// largest k with r * cum[k] <= code (the division-free form of
+// cum[k] <= floor(code / r)); kSteps binary-search steps cover indices
 // [0, 2^kSteps), and delta entries past an alphabet are staged as 2^15 so
-// that no product can wrap and a valid code never selects them.  Writes the
-// value to store (binary16 bits, or the symbol) to v[q].
-template <uint32_t Q, bool kSymbols, bool kAnchor, uint32_t kSteps>
-__device__ inline void step(Stream *st, uint32_t abase, uint32_t *v) {
-  uint32_t in[Q];
-#pragma unroll
-  for (uint32_t q = 0; q < Q; ++q) {
-    // the next four stream bytes, most significant first
-    const lds_u32 *rd = (const lds_u32 *)(uintptr_t)(lds_addr(st[q].ring) + (dword_of(st[q].nrpos) << 2));
-    in[q] = __builtin_amdgcn_alignbit(rd[1], rd[0], st[q].nrpos);
-  }
-  uint32_t r[Q], a[Q];
-#pragma unroll
-  for (uint32_t q = 0; q < Q; ++q) {
-    r[q] = st[q].range >> kPrec;
-    a[q] = kAnchor ? abase : st[q].dbase;
-  }
-  // binary search, the streams' probes interleaved
+// that no product can wrap and a valid code never selects them.  Returns the
+// value to store (binary16 bits, or the symbol).
+template <bool kSymbols, bool kAnchor, uint32_t kSteps>
+__device__ inline uint32_t step(Stream &x, uint32_t abase) {
+  // the next four stream bytes, most significant first
+  const lds_u32 *rd =
+      (const lds_u32 *)(uintptr_t)(lds_addr(x.ring) + (dword_of(x.nrpos) << 2));
+  const uint32_t in = __builtin_amdgcn_alignbit(rd[1], rd[0], x.nrpos);
+  const uint32_t r = x.range >> kPrec;
+  uint32_t a = kAnchor ? abase : x.dbase;
+  // binary search
 #pragma unroll
   for (uint32_t sz = 1u << (kSteps - 1); sz; sz >>= 1) {
-    uint32_t probe[Q];
-#pragma unroll
-    for (uint32_t q = 0; q < Q; ++q) probe[q] = lds_read_u16(a[q] + sz * kRowBytes);
-    PAIR_BARRIER();
-#pragma unroll
-    for (uint32_t q = 0; q < Q; ++q)
-      if (__umul24(r[q], probe[q]) <= st[q].code) a[q] += sz * kRowBytes;
-    PAIR_BARRIER();
+    const uint32_t probe = lds_read_u16(a + sz * kRowBytes);
+    SEARCH_BARRIER();
+    if (__umul24(r, probe) <= x.code) a += sz * kRowBytes;
+    SEARCH_BARRIER();
   }
-  uint32_t csv[Q], cnv[Q];
-#pragma unroll
-  for (uint32_t q = 0; q < Q; ++q) {
-    csv[q] = lds_read_u16(a[q]);
-    cnv[q] = lds_read_u16(a[q] + kRowBytes);
+  const uint32_t cs = lds_read_u16(a);
+  const uint32_t cn = lds_read_u16(a + kRowBytes);
+  SEARCH_BARRIER();
+  int32_t xq;  // 128 (symbol - M) for deltas, 128 symbol for anchors
+  // A code at or past r * 2^15 has no symbol.  For a delta the search then
+  // ends on a staged pad (2^15, as is cum[A]), so the interval is empty and
+  // the range becomes 0; an anchor's search cannot pass symbol 255, so the
+  // range is cleared explicitly.  A zero range stays zero (r = 0 from then
+  // on) and is reported at the end of the stream.
+  bool lost = false;
+  if constexpr (kAnchor) {
+    xq = (int32_t)(a - abase);
+    lost = x.code >= (r << kPrec);
+  } else {
+    xq = (int32_t)(a - x.dbaseM);
   }
-  PAIR_BARRIER();
-#pragma unroll
-  for (uint32_t q = 0; q < Q; ++q) {
-    Stream &x = st[q];
-    const uint32_t cs = csv[q], cn = cnv[q];
-    int32_t xq;  // 128 (symbol - M) for deltas, 128 symbol for anchors
-    // A code at or past r * 2^15 has no symbol.  For a delta the search
-    // then ends on a staged pad (2^15, as is cum[A]), so the interval is
-    // empty and the range becomes 0; an anchor's search cannot pass symbol
-    // 255, so the range is cleared explicitly.  A zero range stays zero
-    // (r = 0 from then on) and is reported at the end of the stream.
-    bool lost = false;
+  // 24-bit multiplies: r < 2^17 and staged cumulative counts <= 2^15
+  x.code -= __umul24(r, cs);
+  uint32_t range = __umul24(r, cn - cs);
+  if constexpr (kAnchor) range = lost ? 0u : range;
+  // whole bytes to shift in: 0, 1 or 2 (range >= 2^9 for a valid stream)
+  const uint32_t sh = ffbh(range) & 24u;
+  x.range = range << sh;
+  // code << sh with the next sh / 8 stream bytes below it: one 64-bit shift
+  x.code = (uint32_t)((((uint64_t)x.code << 32) | in) << sh >> 32);
+  x.nrpos -= sh;
+  if constexpr (kSymbols) {
+    return kAnchor ? (uint32_t)xq >> 7 : (uint32_t)((xq >> 7) + x.M);
+  } else {
+    float y;
+    // 128 q is exact in binary32 and (128 q)(dl / 128) = q dl exactly, so
+    // this is the single rounding of fma(q, dl, ahat)
     if constexpr (kAnchor) {
-      xq = (int32_t)(a[q] - abase);
-      lost = x.code >= (r[q] << kPrec);
+      x.ahat = __builtin_fmaf((float)xq, x.sa7, x.lo);
+      y = x.ahat;
     } else {
-      xq = (int32_t)(a[q] - x.dbaseM);
+      y = __builtin_fmaf((float)xq, x.dl7, x.ahat);
     }
-    // 24-bit multiplies: r < 2^17 and staged cumulative counts <= 2^15
-    x.code -= __umul24(r[q], cs);
-    uint32_t range = __umul24(r[q], cn - cs);
-    if constexpr (kAnchor) range = lost ? 0u : range;
-    // whole bytes to shift in: 0, 1 or 2 (range >= 2^9 for a valid stream)
-    const uint32_t sh = ffbh(range) & 24u;
-    x.range = range << sh;
-    // code << sh with the next sh / 8 stream bytes below it: one 64-bit shift
-    x.code = (uint32_t)((((uint64_t)x.code << 32) | in[q]) << sh >> 32);
-    x.nrpos -= sh;
-    if constexpr (kSymbols) {
-      v[q] = kAnchor ? (uint32_t)xq >> 7 : (uint32_t)((xq >> 7) + x.M);
-    } else {
-      float y;
-      // 128 q is exact in binary32 and (128 q)(dl / 128) = q dl exactly, so
-      // this is the single rounding of fma(q, dl, ahat)
-      if constexpr (kAnchor) {
-        x.ahat = __builtin_fmaf((float)xq, x.sa7, x.lo);
-        y = x.ahat;
-      } else {
-        y = __builtin_fmaf((float)xq, x.dl7, x.ahat);
-      }
-      v[q] = f2h(y);
-    }
+    return f2h(y);
   }
 }
 
@@ -280,47 +257,27 @@ __device__ inline gbyte *uniform_ptr(gbyte *p) {
   return (gbyte *)(((uint64_t)hi << 32) | lo);
 }
 
-// The `count` delta tokens of one group, both streams.
+// The `count` delta tokens of one group.
 template <bool kSymbols, uint32_t kSteps>
-__device__ inline void delta_run(Stream *st, uint32_t abase, Source *src,
-                                 gbyte **ob, uint64_t ld, uint32_t lane, uint32_t count) {
+__device__ inline void delta_run(Stream &s, uint32_t abase, Source &src, gbyte *&ob, uint64_t ld,
+                                 uint32_t lane, uint32_t count) {
   for (uint32_t i = 0; i < count; ++i) {
-    ensure(st[0], src[0]);
-    ensure(st[1], src[1]);
-    uint32_t v[2];
-    step<2, kSymbols, false, kSteps>(st, abase, v);
-    put<kSymbols>(ob[0], lane, v[0]);
-    put<kSymbols>(ob[1], lane, v[1]);
-    ob[0] += ld;
-    ob[1] += ld;
+    ensure(s, src);
+    put<kSymbols>(ob, lane, step<kSymbols, false, kSteps>(s, abase));
+    ob += ld;
   }
 }
 
+// The search depth is the chunk's delta bits in this layer third.
 template <bool kSymbols>
-__device__ inline void delta_dispatch(uint32_t steps, Stream *st, uint32_t abase, Source *src,
-                                      gbyte **ob, uint64_t ld, uint32_t lane, uint32_t count) {
+__device__ inline void delta_dispatch(uint32_t steps, Stream &s, uint32_t abase, Source &src,
+                                      gbyte *&ob, uint64_t ld, uint32_t lane, uint32_t count) {
   switch (steps) {
-    case 2: delta_run<kSymbols, 2>(st, abase, src, ob, ld, lane, count); break;
-    case 3: delta_run<kSymbols, 3>(st, abase, src, ob, ld, lane, count); break;
-    case 4: delta_run<kSymbols, 4>(st, abase, src, ob, ld, lane, count); break;
-    case 5: delta_run<kSymbols, 5>(st, abase, src, ob, ld, lane, count); break;
-    default: delta_run<kSymbols, 6>(st, abase, src, ob, ld, lane, count); break;
-  }
-}
-
-template <bool kSymbols>
-__device__ inline void single_step(uint32_t steps, bool anchor, Stream *st, uint32_t abase,
-                                   uint32_t *v) {
-  if (anchor) {
-    step<1, kSymbols, true, 8>(st, abase, v);
-    return;
-  }
-  switch (steps) {
-    case 2: step<1, kSymbols, false, 2>(st, abase, v); break;
-    case 3: step<1, kSymbols, false, 3>(st, abase, v); break;
-    case 4: step<1, kSymbols, false, 4>(st, abase, v); break;
-    case 5: step<1, kSymbols, false, 5>(st, abase, v); break;
-    default: step<1, kSymbols, false, 6>(st, abase, v); break;
+    case 2: delta_run<kSymbols, 2>(s, abase, src, ob, ld, lane, count); break;
+    case 3: delta_run<kSymbols, 3>(s, abase, src, ob, ld, lane, count); break;
+    case 4: delta_run<kSymbols, 4>(s, abase, src, ob, ld, lane, count); break;
+    case 5: delta_run<kSymbols, 5>(s, abase, src, ob, ld, lane, count); break;
+    default: delta_run<kSymbols, 6>(s, abase, src, ob, ld, lane, count); break;
   }
 }
 
@@ -353,7 +310,7 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
   lds_u32 *lds = (lds_u32 *)lds_raw;
   lds_u32 *sA = lds;                                    // [kARows][64] u16 anchor cum
   lds_u32 *sD = sA + kARows * kWave / 2;                // [levels used][kDRows][64] u16 delta cum
-  lds_u32 *sR = sD + nlev_used * kDRows * kWave / 2;    // [waves][kSlots][64][kRing] rings
+  lds_u32 *sR = sD + nlev_used * kDRows * kWave / 2;    // [waves][64][kRing] rings
   lds_u16 *hA = (lds_u16 *)sA;
   lds_u16 *hD = (lds_u16 *)sD;
 
@@ -400,147 +357,89 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
   const uint32_t esz = kSymbols ? 1u : 2u;
   const uint64_t ld = (uint64_t)d.C * esz;
   const uint32_t m = m0 + lane;
-  const uint32_t npairs = (gp.count + 1) / 2;
+  // this wave's ring (one register holds its address, so that a ring read
+  // is one bit-field extract and one shift-add)
+  uint32_t ring_addr = lds_addr(sR + (wave * kWave + lane) * kRing);
+  __asm__ volatile("" : "+v"(ring_addr));
 
-  for (uint32_t pair = wave; pair < npairs; pair += n_waves) {
-    Stream st[kSlots];
-    gbyte *ob[kSlots];  // wave-uniform output row of the current token
-    Source src[kSlots];
-    uint32_t steps = 2;
-    bool active[kSlots];
+  for (uint32_t i = wave; i < gp.count; i += n_waves) {
+    const uint32_t k = gp.start + i;
+    if (!valid[k]) continue;
+    const ChunkInfo c = ci[k];
+    Stream s;
+    s.ring = (lds_u32 *)(uintptr_t)ring_addr;
+    const uint32_t lslot = __builtin_popcount(level_mask & ((1u << c.level) - 1u));
+    s.dbase = lds_addr(sD) + lslot * kDRows * kRowBytes + 2 * lane_col(lane);
+    const uint32_t b = __builtin_amdgcn_readfirstlane(d.bits[c.level][third]);
+    s.M = (1 << (b - 1)) - 1;
+    s.dbaseM = s.dbase + (uint32_t)s.M * kRowBytes;
+    const uint32_t *rec = reinterpret_cast<const uint32_t *>(c.records + (uint64_t)m * kRecBytes);
+    s.lo = __builtin_bit_cast(float, rec[0]);
+    // sa / 128 and dl / 128 are exact: sa is 0 or at least 2^-24 / 255 (a
+    // binary16 difference), dl is 0 or above 2^-70 (a difference of a
+    // binary16 value and an anchor on a 2^-55 grid), far from subnormals
+    s.sa7 = __builtin_bit_cast(float, rec[1]) * 0.0078125f;
+    s.dl7 = __builtin_bit_cast(float, rec[2]) * 0.0078125f;
+    const uint32_t nblk = (uint32_t)(pad8(rec[3]) / kBlock);
+    // containers are below 2^32 bytes (checked on the host); this unit's
+    // payload starts at its first stream's block offset
+    Source src;
+    src.rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)c.cont, (short)0,
+                                                 (int)(uint32_t)c.cont_bytes, kBufferWord3);
+    src.ubase = (uint32_t)(kHdrBytes + (uint64_t)kRecBytes * S) + offsets[(uint64_t)k * S + m0];
+    src.cnt = 0;
+    gbyte *ob = uniform_ptr((gbyte *)c.out +
+                            (((uint64_t)row * c.out_tokens + c.first_token) * d.C + c0) * esz);
+    s.ahat = 0.0f;
+    // start of the reading rule: every lane asks for its blocks 0, 1 and 2
+    // (block outer, lane inner); 0 and 1 fill the ring, 2 is held.  A lane
+    // without the block loads some other block and never uses it.
+    uint32_t blk[3][2];
 #pragma unroll
-    for (uint32_t q = 0; q < kSlots; ++q) {
-      Stream &s = st[q];
-      const uint32_t idx = 2 * pair + q;
-      const uint32_t k = gp.start + (idx < gp.count ? idx : 0u);
-      active[q] = idx < gp.count && valid[k];
-      s.n = 0;
-      s.M = 0;
-      {
-        // one register per ring address, so that a ring read is one
-        // bit-field extract and one shift-add
-        uint32_t ra = lds_addr(sR + ((wave * kSlots + q) * kWave + lane) * kRing);
-        __asm__ volatile("" : "+v"(ra));
-        s.ring = (lds_u32 *)(uintptr_t)ra;
-      }
-      ob[q] = (gbyte *)ci[k].out;
-      s.dbase = lds_addr(sD) + 2 * lane_col(lane);
-      s.dbaseM = s.dbase;
-      s.rem = 0;
-      s.hpos = 0;
-      src[q].rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)ci[k].cont, (short)0, 0, kBufferWord3);
-      src[q].ubase = 0;
-      src[q].cnt = 0;
-      if (!active[q]) continue;
-      const ChunkInfo c = ci[k];
-      const uint32_t lslot = __builtin_popcount(level_mask & ((1u << c.level) - 1u));
-      s.dbase = lds_addr(sD) + lslot * kDRows * kRowBytes + 2 * lane_col(lane);
-      const uint32_t b = d.bits[c.level][third];
-      steps = b > steps ? b : steps;
-      s.M = (1 << (b - 1)) - 1;
-      s.dbaseM = s.dbase + (uint32_t)s.M * kRowBytes;
-      const uint32_t *rec = reinterpret_cast<const uint32_t *>(c.records + (uint64_t)m * kRecBytes);
-      s.lo = __builtin_bit_cast(float, rec[0]);
-      // sa / 128 and dl / 128 are exact: sa is 0 or at least 2^-24 / 255 (a
-      // binary16 difference), dl is 0 or above 2^-70 (a difference of a
-      // binary16 value and an anchor on a 2^-55 grid), far from subnormals
-      s.sa7 = __builtin_bit_cast(float, rec[1]) * 0.0078125f;
-      s.dl7 = __builtin_bit_cast(float, rec[2]) * 0.0078125f;
-      const uint32_t nblk = (uint32_t)(pad8(rec[3]) / kBlock);
-      s.n = c.n_tokens;
-      // containers are below 2^32 bytes (checked on the host); this unit's
-      // payload starts at its first stream's block offset
-      src[q].rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)c.cont, (short)0,
-                                                      (int)(uint32_t)c.cont_bytes, kBufferWord3);
-      src[q].ubase = (uint32_t)(kHdrBytes + (uint64_t)kRecBytes * S) + offsets[(uint64_t)k * S + m0];
-      ob[q] = uniform_ptr((gbyte *)c.out +
-                          (((uint64_t)row * c.out_tokens + c.first_token) * d.C + c0) * esz);
-      s.ahat = 0.0f;
-      // start of the reading rule: every lane asks for its blocks 0, 1 and 2
-      // (block outer, lane inner); 0 and 1 fill the ring, 2 is held.  A lane
-      // without the block loads some other block and never uses it.
-      uint32_t blk[3][2];
-#pragma unroll
-      for (uint32_t b = 0; b < 3; ++b) {
-        const uint64_t mask = __builtin_amdgcn_ballot_w64(b < nblk);
-        const uint32_t pos = src[q].cnt + lanes_below(mask);
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(src[q].rsrc, src[q].ubase + pos * kBlock, 0, 0);
-        blk[b][0] = v[0];
-        blk[b][1] = v[1];
-        if (b == 2) s.hpos = pos;
-        src[q].cnt += (uint32_t)__builtin_popcountll(mask);
-      }
-      s.rem = nblk < 3 ? 0u : nblk - 3;
-      s.ring[4] = __builtin_bswap32(blk[0][0]);
-      s.ring[3] = __builtin_bswap32(blk[0][1]);
-      s.ring[2] = __builtin_bswap32(blk[1][0]);
-      s.ring[1] = __builtin_bswap32(blk[1][1]);
-      s.ring[0] = __builtin_bswap32(blk[0][0]);
-      s.held[0] = blk[2][0];
-      s.held[1] = blk[2][1];
-      s.nwlim = 0u - (128 - 16);
-      s.code = bswap32(blk[0][0]);
-      s.nrpos = 0u - 32;
-      s.range = 0xFFFFFFFFu;
+    for (uint32_t q = 0; q < 3; ++q) {
+      const uint64_t mask = __builtin_amdgcn_ballot_w64(q < nblk);
+      const uint32_t pos = src.cnt + lanes_below(mask);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(src.rsrc, src.ubase + pos * kBlock, 0, 0);
+      blk[q][0] = v[0];
+      blk[q][1] = v[1];
+      if (q == 2) s.hpos = pos;
+      src.cnt += (uint32_t)__builtin_popcountll(mask);
     }
-    steps = __builtin_amdgcn_readfirstlane(steps);
+    s.rem = nblk < 3 ? 0u : nblk - 3;
+    s.ring[4] = __builtin_bswap32(blk[0][0]);
+    s.ring[3] = __builtin_bswap32(blk[0][1]);
+    s.ring[2] = __builtin_bswap32(blk[1][0]);
+    s.ring[1] = __builtin_bswap32(blk[1][1]);
+    s.ring[0] = __builtin_bswap32(blk[0][0]);
+    s.held[0] = blk[2][0];
+    s.held[1] = blk[2][1];
+    s.nwlim = 0u - (128 - 16);
+    s.code = bswap32(blk[0][0]);
+    s.nrpos = 0u - 32;
+    s.range = 0xFFFFFFFFu;
 
-    // Both streams live: one lockstep step per token, so the two dependency
-    // chains interleave; only the ring refills branch.
-    const uint32_t nmin = st[0].n < st[1].n ? st[0].n : st[1].n;
-    const uint32_t nmax = st[0].n > st[1].n ? st[0].n : st[1].n;
-    uint32_t j = 0;
-    while (j < nmin) {
+    // groups of an anchor and up to G - 1 deltas
+    const uint32_t n = c.n_tokens;
+    for (uint32_t j = 0; j < n;) {
       // after a refill at least 8 bytes are buffered: no check for the anchor
-      refill(st[0], src[0]);
-      refill(st[1], src[1]);
-      {
-        uint32_t v[2];
-        step<2, kSymbols, true, 8>(st, abase, v);
-        put<kSymbols>(ob[0], lane, v[0]);
-        put<kSymbols>(ob[1], lane, v[1]);
-        ob[0] += ld;
-        ob[1] += ld;
-      }
-      const uint32_t jend = j + d.G < nmin ? j + d.G : nmin;
-      delta_dispatch<kSymbols>(steps, st, abase, src, ob, ld, lane, jend - j - 1);
+      refill(s, src);
+      put<kSymbols>(ob, lane, step<kSymbols, true, 8>(s, abase));
+      ob += ld;
+      const uint32_t jend = j + d.G < n ? j + d.G : n;
+      delta_dispatch<kSymbols>(b, s, abase, src, ob, ld, lane, jend - j - 1);
       j = jend;
     }
-    // Tail: one stream left (odd chunk count, or a shorter last chunk).
-    uint32_t g = nmin % d.G;
-    for (; j < nmax; ++j) {
-      const bool anchor = g == 0;
-      g = g + 1 == d.G ? 0 : g + 1;
-#pragma unroll
-      for (uint32_t q = 0; q < kSlots; ++q) {
-        if (j < st[q].n) {
-          if (anchor)
-            refill(st[q], src[q]);
-          else
-            ensure(st[q], src[q]);
-          uint32_t v;
-          single_step<kSymbols>(steps, anchor, &st[q], abase, &v);
-          put<kSymbols>(ob[q], lane, v);
-          ob[q] += ld;
-        }
-      }
-    }
     // a valid stream ends exactly at its last byte, with every block asked for
-#pragma unroll
-    for (uint32_t q = 0; q < kSlots; ++q) {
-      if (!active[q]) continue;
-      const uint32_t k = gp.start + 2 * pair + q;
-      const uint32_t nbytes =
-          reinterpret_cast<const uint32_t *>(ci[k].records + (uint64_t)m * kRecBytes)[3];
-      if (st[q].range == 0 || st[q].nrpos != 0u - 8 * nbytes || st[q].rem != 0)
-        set_status(status, KVC_ERR_CORRUPT_STREAM);
-    }
+    const uint32_t nbytes =
+        reinterpret_cast<const uint32_t *>(ci[k].records + (uint64_t)m * kRecBytes)[3];
+    if (s.range == 0 || s.nrpos != 0u - 8 * nbytes || s.rem != 0)
+      set_status(status, KVC_ERR_CORRUPT_STREAM);
   }
 }
 
 size_t decode_lds_bytes(uint32_t levels, uint32_t waves) {
   return (size_t)kARows * kRowBytes + (size_t)levels * kDRows * kRowBytes +
-         sizeof(uint32_t) * (size_t)waves * kSlots * kWave * kRing;
+         sizeof(uint32_t) * (size_t)waves * kWave * kRing;
 }
 
 hipError_t launch_decode(const Desc &d, const ChunkInfo *dev_chunks, const DecodeGroup *groups,

@@ -62,9 +62,9 @@ struct DecodeGroup {
 };
 static_assert(sizeof(DecodeGroup) == 16, "DecodeGroup layout");
 
-// Decode workgroups have at most this many waves; a wave takes the group's
-// chunks two at a time.
-constexpr uint32_t kDecodeMaxWaves = 8;
+// Decode workgroups have at most this many waves; a wave decodes one of the
+// group's chunks at a time.
+constexpr uint32_t kDecodeMaxWaves = 16;
 // Encode workgroups have at most this many waves (one chunk each at a time).
 constexpr uint32_t kEncodeMaxWaves = 8;
 // LDS per decode workgroup that still lets two of them share a CU.
