@@ -460,10 +460,18 @@ class HipEvents:
         if self._hip.hipEventSynchronize(ctypes.c_void_p(self.handles[i])) != 0:
             raise RuntimeError("hipEventSynchronize failed")
 
-    def __del__(self):
+    def close(self) -> None:
+        """Destroy the events (also done when the object is collected)."""
         for i in range(self.n):
             if self.handles[i]:
                 self._hip.hipEventDestroy(ctypes.c_void_p(self.handles[i]))
+                self.handles[i] = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown: the runtime may be gone
+            pass
 
 
 def restore_async(desc: CodecDesc, tables: torch.Tensor, chunks: Sequence[HostChunk],
