@@ -28,6 +28,7 @@ hipError_t launch_encode(const Desc &d, const uint8_t *tables, const uint16_t *k
                          uint64_t *chunk_off_ws, uint32_t *fits, uint8_t *out, uint64_t out_cap,
                          uint64_t *chunk_off_out, int32_t *status, hipStream_t stream);
 size_t encode_lds_bytes(uint32_t levels);
+size_t encode_emit_lds_bytes(uint32_t levels, uint32_t waves);
 hipError_t launch_profile(const Desc &d, const uint16_t *kv, uint32_t T, uint8_t *tables,
                           uint32_t *counts, uint64_t *model_hash, uint64_t *row_hash,
                           int32_t *status, hipStream_t stream);
@@ -184,7 +185,7 @@ kvc_status decode_chunks(const kvc_codec_desc *dd, const void *tables, const Out
     const uint32_t lv_all = (uint32_t)__builtin_popcount(all_levels);
     uint32_t wmax = 1;
     for (uint32_t w = kDecodeMaxWaves; w >= 1; --w)
-      if (decode_lds_bytes(lv_all, w) <= kDecodeLdsBudget) {
+      if (decode_lds_bytes(lv_all, w) <= kLdsBudget) {
         wmax = w;
         break;
       }
@@ -390,12 +391,23 @@ kvc_status kvc_encode(const kvc_codec_desc *dd, const void *tables, const uint16
   if (e != hipSuccess) return KVC_ERR_HIP;
   // Encode groups: contiguous chunk ranges, each encoded by one workgroup
   // per (row, channel block) that stages the models of the levels it uses;
-  // its waves take the group's chunks in turn, at most kMaxRounds each.
+  // its waves take the group's chunks in turn, at most kMaxRounds each.  A
+  // workgroup has as many waves as the group has chunks, up to the most
+  // whose models and block queues still let two emit workgroups share a CU.
   std::vector<DecodeGroup> groups;
   uint32_t levels = 1, waves = 1;
   {
     constexpr uint32_t kMaxRounds = 4;
-    const uint32_t per = kEncodeMaxWaves * kMaxRounds;
+    uint32_t all_levels = 0;
+    for (uint32_t k = 0; k < K; ++k) all_levels |= 1u << chunk_levels[k];
+    const uint32_t lv_all = (uint32_t)__builtin_popcount(all_levels);
+    uint32_t wmax = 1;
+    for (uint32_t w = kEncodeMaxWaves; w >= 1; --w)
+      if (encode_emit_lds_bytes(lv_all, w) <= kLdsBudget) {
+        wmax = w;
+        break;
+      }
+    const uint32_t per = wmax * kMaxRounds;
     const uint32_t ng = (K + per - 1) / per;
     for (uint32_t gi = 0; gi < ng; ++gi) {
       const uint32_t a = (uint32_t)((uint64_t)K * gi / ng);
@@ -405,7 +417,7 @@ kvc_status kvc_encode(const kvc_codec_desc *dd, const void *tables, const uint16
       g.count = b - a;
       for (uint32_t i = a; i < b; ++i) g.level |= 1u << chunk_levels[i];
       levels = std::max<uint32_t>(levels, (uint32_t)__builtin_popcount(g.level));
-      waves = std::max<uint32_t>(waves, std::min<uint32_t>(kEncodeMaxWaves, g.count));
+      waves = std::max<uint32_t>(waves, std::min<uint32_t>(wmax, g.count));
       groups.push_back(g);
     }
   }

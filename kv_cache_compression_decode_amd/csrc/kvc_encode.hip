@@ -457,6 +457,11 @@ size_t encode_lds_bytes(uint32_t levels) {
   return sizeof(uint32_t) * ((size_t)kWave * kEA + (size_t)levels * kWave * kED);
 }
 
+// The emit kernel's LDS: the models plus every lane's block queue.
+size_t encode_emit_lds_bytes(uint32_t levels, uint32_t waves) {
+  return encode_lds_bytes(levels) + sizeof(uint32_t) * (size_t)waves * kWave * kQueue;
+}
+
 // Stream-ordered encode sequence; dev_chunks already holds the chunk table
 // (records pointing into the workspace record array), `groups` the chunk
 // groups (contiguous ranges of it) and their level masks.
@@ -471,7 +476,7 @@ hipError_t launch_encode(const Desc &d, const uint8_t *tables, const uint16_t *k
   const uint32_t n_units = 2u * d.L * ncb;
   const uint64_t blocks = (uint64_t)((n_units + kXcds - 1) / kXcds) * kXcds * n_groups;
   const size_t lds = encode_lds_bytes(levels);
-  const size_t lds_emit = lds + sizeof(uint32_t) * (size_t)waves * kWave * kQueue;
+  const size_t lds_emit = encode_emit_lds_bytes(levels, waves);
   hipLaunchKernelGGL(k_encode_stats, dim3((uint32_t)blocks), dim3(waves * kWave), lds, stream, d,
                      dev_chunks, groups, n_groups, n_units, tables, kv, T, records, status);
   hipError_t e = launch_index(d, dev_chunks, n_chunks, row_sums, flags, offsets, valid, payload,

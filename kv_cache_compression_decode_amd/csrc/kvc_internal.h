@@ -66,9 +66,9 @@ static_assert(sizeof(DecodeGroup) == 16, "DecodeGroup layout");
 // group's chunks at a time.
 constexpr uint32_t kDecodeMaxWaves = 16;
 // Encode workgroups have at most this many waves (one chunk each at a time).
-constexpr uint32_t kEncodeMaxWaves = 8;
-// LDS per decode workgroup that still lets two of them share a CU.
-constexpr uint32_t kDecodeLdsBudget = 80u * 1024u;
+constexpr uint32_t kEncodeMaxWaves = 16;
+// LDS per decode or emit workgroup that still lets two of them share a CU.
+constexpr uint32_t kLdsBudget = 80u * 1024u;
 
 // Fourth dword of a raw buffer resource on gfx9-family GPUs (32-bit data
 // format, no swizzle): loads are bounds-checked against num_records bytes.
