@@ -23,7 +23,11 @@
 //    addressed from a wave-uniform base;
 //  * a symbol is the largest k with r * cum[k] <= code, found by binary
 //    search with one 24-bit multiply per probe (no division): 8 steps for
-//    anchors, b steps for a b-bit delta alphabet;
+//    anchors, b steps for a b-bit delta alphabet.  The entries probed by the
+//    first two steps are the same for every token of a stream and sit in
+//    registers, so a symbol waits on b - 1 rounds of LDS reads (the other
+//    steps and its interval), not b + 1: the decoder is bound by this chain
+//    of LDS latencies as much as by instruction issue;
 //  * the models are staged row-interleaved (entry i of lane l in row i, a
 //    128-byte row per entry index), so a probe is a constant offset from the
 //    lane's current row and the symbol index is a shift of the address;
@@ -124,6 +128,8 @@ struct Stream {
   int32_t M;
   uint32_t dbase;       // LDS byte address of this lane's delta row 0
   uint32_t dbaseM;      // dbase + M rows: (addr - dbaseM) >> 7 is q = s - M
+  uint32_t dmid;        // dbase + 2^(b-1) rows: the search's first step taken
+  uint32_t d1, d2lo, d2hi;  // delta cum[2^(b-1)], cum[2^(b-2)], cum[3 2^(b-2)]
   float lo, sa7, dl7, ahat;  // sa7 = sa / 128, dl7 = dl / 128 (exact)
 
   // The held block, byte-reversed, into the free half of the ring: its
@@ -174,6 +180,13 @@ __device__ inline void ensure(Stream &s, Source &src) { advance(s, src, s.nrpos 
 // binary-search probe is read, then compared, with nothing hoisted between.
 #define SEARCH_BARRIER() __builtin_amdgcn_sched_barrier(0)
 
+// The anchor model's entries at the top two levels of its search, the same
+// for every token of the workgroup.
+struct AnchorTop {
+  uint32_t base, mid;   // LDS byte addresses of the lane's rows 0 and 128
+  uint32_t c1, c2lo, c2hi;  // cum[128], cum[64], cum[192]
+};
+
 // One token of a lane's stream: range decode, dequantize.  The symbol is the
 // largest k with r * cum[k] <= code (the division-free form of
 // cum[k] <= floor(code / r)); kSteps binary-search steps cover indices
@@ -181,16 +194,22 @@ __device__ inline void ensure(Stream &s, Source &src) { advance(s, src, s.nrpos 
 // that no product can wrap and a valid code never selects them.  Returns the
 // value to store (binary16 bits, or the symbol).
 template <bool kSymbols, bool kAnchor, uint32_t kSteps>
-__device__ inline uint32_t step(Stream &x, uint32_t abase) {
+__device__ inline uint32_t step(Stream &x, const AnchorTop &at) {
   // the next four stream bytes, most significant first
   const lds_u32 *rd =
       (const lds_u32 *)(uintptr_t)(lds_addr(x.ring) + (dword_of(x.nrpos) << 2));
   const uint32_t in = __builtin_amdgcn_alignbit(rd[1], rd[0], x.nrpos);
   const uint32_t r = x.range >> kPrec;
-  uint32_t a = kAnchor ? abase : x.dbase;
-  // binary search
+  // binary search; the entries of its first two steps are fixed for the
+  // whole stream and held in registers, the rest are read from LDS
+  constexpr uint32_t kTop = 1u << (kSteps - 1);
+  const bool upper = __umul24(r, kAnchor ? at.c1 : x.d1) <= x.code;
+  uint32_t a = upper ? (kAnchor ? at.mid : x.dmid) : (kAnchor ? at.base : x.dbase);
+  const uint32_t p2 = upper ? (kAnchor ? at.c2hi : x.d2hi) : (kAnchor ? at.c2lo : x.d2lo);
+  if (__umul24(r, p2) <= x.code) a += (kTop / 2) * kRowBytes;
+  SEARCH_BARRIER();
 #pragma unroll
-  for (uint32_t sz = 1u << (kSteps - 1); sz; sz >>= 1) {
+  for (uint32_t sz = kTop / 4; sz; sz >>= 1) {
     const uint32_t probe = lds_read_u16(a + sz * kRowBytes);
     SEARCH_BARRIER();
     if (__umul24(r, probe) <= x.code) a += sz * kRowBytes;
@@ -207,7 +226,7 @@ __device__ inline uint32_t step(Stream &x, uint32_t abase) {
   // on) and is reported at the end of the stream.
   bool lost = false;
   if constexpr (kAnchor) {
-    xq = (int32_t)(a - abase);
+    xq = (int32_t)(a - at.base);
     lost = x.code >= (r << kPrec);
   } else {
     xq = (int32_t)(a - x.dbaseM);
@@ -238,15 +257,21 @@ __device__ inline uint32_t step(Stream &x, uint32_t abase) {
   }
 }
 
+// Stores a lane's value at its byte offset `loff` from the wave-uniform row
+// base.  The empty asm makes the offset opaque at every store, so that the
+// address stays "scalar base + 32-bit lane offset" (one global store with a
+// scalar base, no 64-bit address arithmetic per token).
 template <bool kSymbols>
-__device__ inline void put(gbyte *base, uint32_t lane, uint32_t v) {
-  if constexpr (kSymbols)
-    base[lane] = (uint8_t)v;
-  else
+__device__ inline void put(gbyte *base, uint32_t &loff, uint32_t v) {
+  if constexpr (kSymbols) {
+    base[loff] = (uint8_t)v;
+  } else {
+    __asm__("" : "+v"(loff));
     // streaming store: the kernel never reads its output back, so the rows
     // should not displace the stream blocks the lanes are still reading
     __builtin_nontemporal_store((uint16_t)v,
-                                &((__attribute__((address_space(1))) uint16_t *)base)[lane]);
+                                (__attribute__((address_space(1))) uint16_t *)(base + loff));
+  }
 }
 
 // Wave-uniform 64-bit pointer (kept in scalar registers).
@@ -259,25 +284,36 @@ __device__ inline gbyte *uniform_ptr(gbyte *p) {
 
 // The `count` delta tokens of one group.
 template <bool kSymbols, uint32_t kSteps>
-__device__ inline void delta_run(Stream &s, uint32_t abase, Source &src, gbyte *&ob, uint64_t ld,
-                                 uint32_t lane, uint32_t count) {
-  for (uint32_t i = 0; i < count; ++i) {
+__device__ inline void delta_run(Stream &s, const AnchorTop &at, Source &src, gbyte *&ob, uint64_t ld,
+                                 uint32_t &loff, uint32_t count) {
+  // The anchor's refill leaves at least 8 bytes in every ring and a token
+  // takes at most 2 (range >= 2^24 after renormalization, a symbol's
+  // frequency >= 1), so the group's first three deltas cannot run low.  A
+  // corrupt stream whose range reached 0 takes 3 bytes a token, but stays
+  // at 0 and is reported at the end.
+  const uint32_t safe = count < 3 ? count : 3;
+  uint32_t i = 0;
+  for (; i < safe; ++i) {
+    put<kSymbols>(ob, loff, step<kSymbols, false, kSteps>(s, at));
+    ob += ld;
+  }
+  for (; i < count; ++i) {
     ensure(s, src);
-    put<kSymbols>(ob, lane, step<kSymbols, false, kSteps>(s, abase));
+    put<kSymbols>(ob, loff, step<kSymbols, false, kSteps>(s, at));
     ob += ld;
   }
 }
 
 // The search depth is the chunk's delta bits in this layer third.
 template <bool kSymbols>
-__device__ inline void delta_dispatch(uint32_t steps, Stream &s, uint32_t abase, Source &src,
-                                      gbyte *&ob, uint64_t ld, uint32_t lane, uint32_t count) {
+__device__ inline void delta_dispatch(uint32_t steps, Stream &s, const AnchorTop &at, Source &src,
+                                      gbyte *&ob, uint64_t ld, uint32_t &loff, uint32_t count) {
   switch (steps) {
-    case 2: delta_run<kSymbols, 2>(s, abase, src, ob, ld, lane, count); break;
-    case 3: delta_run<kSymbols, 3>(s, abase, src, ob, ld, lane, count); break;
-    case 4: delta_run<kSymbols, 4>(s, abase, src, ob, ld, lane, count); break;
-    case 5: delta_run<kSymbols, 5>(s, abase, src, ob, ld, lane, count); break;
-    default: delta_run<kSymbols, 6>(s, abase, src, ob, ld, lane, count); break;
+    case 2: delta_run<kSymbols, 2>(s, at, src, ob, ld, loff, count); break;
+    case 3: delta_run<kSymbols, 3>(s, at, src, ob, ld, loff, count); break;
+    case 4: delta_run<kSymbols, 4>(s, at, src, ob, ld, loff, count); break;
+    case 5: delta_run<kSymbols, 5>(s, at, src, ob, ld, loff, count); break;
+    default: delta_run<kSymbols, 6>(s, at, src, ob, ld, loff, count); break;
   }
 }
 
@@ -352,7 +388,12 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   if (lane >= nv) return;
 
-  const uint32_t abase = lds_addr(sA) + 2 * lane_col(lane);
+  AnchorTop at;
+  at.base = lds_addr(sA) + 2 * lane_col(lane);
+  at.mid = at.base + 128 * kRowBytes;
+  at.c1 = lds_read_u16(at.mid);
+  at.c2lo = lds_read_u16(at.base + 64 * kRowBytes);
+  at.c2hi = lds_read_u16(at.base + 192 * kRowBytes);
   const uint32_t third = third_of(row >> 1, d.L);
   const uint32_t esz = kSymbols ? 1u : 2u;
   const uint64_t ld = (uint64_t)d.C * esz;
@@ -361,6 +402,8 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
   // is one bit-field extract and one shift-add)
   uint32_t ring_addr = lds_addr(sR + (wave * kWave + lane) * kRing);
   __asm__ volatile("" : "+v"(ring_addr));
+  uint32_t loff = lane * esz;
+  __asm__ volatile("" : "+v"(loff));
 
   for (uint32_t i = wave; i < gp.count; i += n_waves) {
     const uint32_t k = gp.start + i;
@@ -373,6 +416,10 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
     const uint32_t b = __builtin_amdgcn_readfirstlane(d.bits[c.level][third]);
     s.M = (1 << (b - 1)) - 1;
     s.dbaseM = s.dbase + (uint32_t)s.M * kRowBytes;
+    s.dmid = s.dbase + (1u << (b - 1)) * kRowBytes;
+    s.d1 = lds_read_u16(s.dmid);
+    s.d2lo = lds_read_u16(s.dbase + (1u << (b - 2)) * kRowBytes);
+    s.d2hi = lds_read_u16(s.dbase + 3u * (1u << (b - 2)) * kRowBytes);
     const uint32_t *rec = reinterpret_cast<const uint32_t *>(c.records + (uint64_t)m * kRecBytes);
     s.lo = __builtin_bit_cast(float, rec[0]);
     // sa / 128 and dl / 128 are exact: sa is 0 or at least 2^-24 / 255 (a
@@ -423,10 +470,10 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
     for (uint32_t j = 0; j < n;) {
       // after a refill at least 8 bytes are buffered: no check for the anchor
       refill(s, src);
-      put<kSymbols>(ob, lane, step<kSymbols, true, 8>(s, abase));
+      put<kSymbols>(ob, loff, step<kSymbols, true, 8>(s, at));
       ob += ld;
       const uint32_t jend = j + d.G < n ? j + d.G : n;
-      delta_dispatch<kSymbols>(b, s, abase, src, ob, ld, lane, jend - j - 1);
+      delta_dispatch<kSymbols>(b, s, at, src, ob, ld, loff, jend - j - 1);
       j = jend;
     }
     // a valid stream ends exactly at its last byte, with every block asked for
