@@ -162,11 +162,11 @@ uint64_t kvc_encode_ws_bytes(const kvc_codec_desc *d, uint32_t T);
  * the decoder's 64 lanes ask for them while decoding (so that one wave's
  * requests are consecutive bytes); a stream's block padding is zero.
  * Device errors: KVC_ERR_NONFINITE, KVC_ERR_CAPACITY (out_cap too small; the
- * offsets are still written, `out` is not), KVC_ERR_UNIMPLEMENTED (the
- * decoder would ask for more than 8 of one stream's blocks before the
- * encoder has written them, the size of the encoder's per-lane block queue:
- * only reachable when a pending carry holds back a run of about 25 0xFF
- * bytes).
+ * offsets are still written, `out` is not), KVC_ERR_UNIMPLEMENTED (a
+ * range-coder carry would have to pass every byte the encoder still holds
+ * back, at least 6, all 0xFF; or the decoder would ask for more than 8 of
+ * one stream's blocks before the encoder has written them; neither occurs
+ * short of such a run of 0xFF bytes).
  */
 kvc_status kvc_encode(const kvc_codec_desc *d, const void *tables, const uint16_t *kv_fp16,
                       uint32_t T, const uint8_t *chunk_levels, uint8_t *out, uint64_t out_cap,

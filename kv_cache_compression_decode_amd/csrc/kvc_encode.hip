@@ -14,9 +14,10 @@
 //                    bytes are produced); records go to the workspace;
 //   (index kernels): per-stream payload offsets from those lengths;
 //   k_encode_layout: container start offsets, capacity check;
-//   k_encode_emit  : quantize and range-encode into the final position, with
-//                    the carry resolved by holding back the last byte that
-//                    a carry can still reach (plus the run of 0xFF after it);
+//   k_encode_emit  : quantize and range-encode into the final position; the
+//                    output bytes wait in registers (6 to 11 of them) until
+//                    a carry can no longer reach them, so a carry is one
+//                    add-with-carry chain and no lane branches per byte;
 //   k_encode_header: the 64-byte headers.
 #include "kvc_internal.h"
 
@@ -25,6 +26,13 @@ namespace kvc {
 namespace {
 
 constexpr uint32_t kXcds = 8;
+
+// Leading zero bits of a nonzero word (v_ffbh_u32, no test for zero).
+__device__ inline uint32_t lead_zeros(uint32_t v) {
+  uint32_t r;
+  __asm__("v_ffbh_u32 %0, %1" : "=v"(r) : "v"(v));
+  return r;
+}
 constexpr uint32_t kEA = 133;  // dwords per staged anchor model (cum[0..256] + pad; odd)
 constexpr uint32_t kED = 33;   // dwords per staged delta model (cum[0..63] + pad; odd)
 
@@ -68,25 +76,65 @@ __device__ inline EncodeBlock encode_block(uint32_t n_groups) {
 }
 
 // Entries of the per-lane queue of payload blocks asked for (by the reading
-// rule) but not yet written.  The queue holds the blocks between the last
-// byte written and the reader's position: about 5, plus one per 8 bytes the
-// range coder still holds back for a pending carry.  8 entries keep the
-// emit kernel's LDS (models + queues) small enough for two workgroups per
-// CU; a longer queue would be needed only by a run of some 25 pending 0xFF
-// bytes.
+// rule) but not yet written.  The decoder asks for a block about 3 blocks
+// ahead of what it has consumed, and the encoder holds back at most 11
+// bytes, so about 5 entries are ever in use; 8 keep the emit kernel's LDS
+// small enough for two workgroups per CU.
 constexpr uint32_t kQueue = 8;
 
-// Byte sink writing a stream's bytes, little-endian, in 8-byte blocks to the
-// payload blocks the reading rule gave them (queued in block order); at most
-// `cap` bytes.
+// Tokens loaded per batch by the emit loop.
+constexpr uint32_t kEmitBatch = 8;
+
+// Range encoder whose output bytes wait in a 96-bit register (p2:p1:p0,
+// newest byte lowest, `nbits` = 8 x bytes held) until a carry can no longer
+// reach them: a carry adds 1 to the held bytes as one integer and runs
+// through any trailing 0xFF bytes by itself.  Bytes leave 4 at a time, the
+// oldest first, once 10 are held, so at least 6 stay behind; a carry that
+// would pass all of them (a run of 6 or more 0xFF bytes) sets the bit above
+// the held bytes, which is checked whenever bytes leave.
+struct RangeEncoder {
+  uint32_t low, range;
+  uint32_t p0, p1, p2;
+  uint32_t nbits;
+
+  // Codes the interval [cum, cum + f) of 2^15; returns the whole bytes
+  // shifted out (0, 1 or 2: f >= 1 keeps range >= 2^9).
+  __device__ inline uint32_t encode(uint32_t cum, uint32_t f) {
+    const uint32_t r = range >> kPrec;
+    // 24-bit multiplies: r < 2^17, cum and f <= 2^15
+    uint32_t c;
+    low = __builtin_addc(low, __umul24(r, cum), 0u, &c);
+    p0 = __builtin_addc(p0, 0u, c, &c);
+    p1 = __builtin_addc(p1, 0u, c, &c);
+    p2 = p2 + c;
+    range = __umul24(r, f);
+    const uint32_t sh = lead_zeros(range) & 24u;
+    append(sh);
+    range <<= sh;
+    return sh >> 3;
+  }
+  // Moves the top `sh` bits (0, 8 or 16) of low into the held bytes.
+  __device__ inline void append(uint32_t sh) {
+    const uint64_t l = (uint64_t)low << sh;
+    low = (uint32_t)l;
+    p2 = (uint32_t)((((uint64_t)p2 << 32) | p1) << sh >> 32);
+    p1 = (uint32_t)((((uint64_t)p1 << 32) | p0) << sh >> 32);
+    p0 = (p0 << sh) | (uint32_t)(l >> 32);
+    nbits += sh;
+  }
+};
+
+// Writes a stream's bytes, 4 at a time, into the payload blocks the reading
+// rule gave it (queued in block order in LDS); at most `cap` bytes.
 struct BlockSink {
   uint8_t *pay;      // the unit's payload
   uint32_t *queue;   // this lane's kQueue payload block numbers (LDS)
   uint32_t cnt;      // blocks of the unit handed out so far (wave-uniform)
   uint32_t head, tail;
-  uint32_t w0, w1, nacc, count, cap;
-  bool overflow;     // more bytes than cap, or no block to write to
-  bool window;       // the queue ran full
+  uint32_t slot;     // block being written (when `written` is 4 past a multiple of 8)
+  uint32_t written, cap;
+  bool overflow;     // more bytes than cap, or no block asked for
+  bool window;       // the queue ran full, or a carry passed every held byte
   __device__ inline void push(uint32_t blk) {
     if (tail - head >= kQueue) {
       window = true;
@@ -95,84 +143,30 @@ struct BlockSink {
     queue[tail % kQueue] = blk;
     ++tail;
   }
-  __device__ inline void emit() {
-    const uint32_t blk = head == tail ? cnt : queue[head % kQueue];
-    if (blk >= cnt) {
-      overflow = true;  // no block asked for: never write past those handed out
-    } else {
-      uint32_t *dst = reinterpret_cast<uint32_t *>(pay + (uint64_t)blk * kBlock);
-      ++head;
-      dst[0] = w0;
-      dst[1] = w1;
-    }
-    w0 = w1 = nacc = 0;
-  }
-  __device__ inline void put(uint32_t b) {
-    if (count >= cap) {
-      overflow = true;
-      return;
-    }
-    if (nacc < 4)
-      w0 |= (b & 0xFFu) << (8 * nacc);
-    else
-      w1 |= (b & 0xFFu) << (8 * (nacc - 4));
-    ++count;
-    if (++nacc == kBlock) emit();
-  }
-  __device__ inline void flush() {
-    if (nacc) emit();  // the rest of the block is zero padding
-  }
-};
-
-// Range encoder with the carry applied through a held-back byte.
-struct RangeEncoder {
-  uint64_t low;  // up to 33 bits between shifts
-  uint32_t range;
-  uint32_t cache;
-  uint32_t nff;  // 0xFF bytes pending after `cache`
-  bool have_cache;
-  bool bad;
-
-  __device__ inline void shift_low(BlockSink &out) {
-    const uint32_t top = (uint32_t)(low >> 24);  // 9 bits: carry in bit 8
-    if (top != 0xFFu) {
-      const uint32_t carry = top >> 8;
-      if (have_cache) {
-        out.put(cache + carry);
-        for (; nff; --nff) out.put(0xFFu + carry);
-      } else if (carry) {
-        bad = true;  // a carry past the first byte cannot happen
+  // The 4 oldest held bytes of `e` (which holds at least 4 when `take`) to
+  // the stream, for the lanes with `take`.  Wave-uniform apart from `take`.
+  __device__ inline void take4(RangeEncoder &e, bool take) {
+    const uint32_t s = e.nbits - 64u;  // 16..24 (nbits 80..88), or the end's 32..
+    // a carry past the held bytes shows as a bit at or above nbits
+    const bool lost = ((uint64_t)e.p2 >> s) != 0;
+    const uint32_t v = (uint32_t)(((((uint64_t)e.p2 << 32) | e.p1) >> s));
+    const bool first = (written & 4u) == 0;
+    const uint32_t q = queue[head % kQueue];
+    const bool have = !first || head != tail;
+    if (take) {
+      if (first) slot = q;
+      head += first ? 1u : 0u;
+      window = window || lost;
+      overflow = overflow || !have || written + 4u > pad8(cap);
+      if (have && !lost && written + 4u <= pad8(cap)) {
+        // stream order: the oldest byte first
+        *reinterpret_cast<uint32_t *>(pay + (uint64_t)slot * kBlock + (written & 4u)) =
+            __builtin_bswap32(v);
       }
-      cache = top & 0xFFu;
-      have_cache = true;
-    } else if (!have_cache) {
-      cache = 0xFFu;
-      have_cache = true;
-    } else {
-      ++nff;
-    }
-    low = (low & 0x00FFFFFFull) << 8;
-  }
-
-  // Encodes one symbol; returns the bytes the decoder shifts in for it.
-  __device__ inline uint32_t encode(uint32_t cum, uint32_t f, BlockSink &out) {
-    const uint32_t r = range >> kPrec;
-    low += (uint64_t)r * cum;
-    range = r * f;
-    uint32_t k = 0;
-    while (range < (1u << 24)) {
-      shift_low(out);
-      range <<= 8;
-      ++k;
-    }
-    return k;
-  }
-
-  __device__ inline void finish(BlockSink &out) {
-    for (int i = 0; i < 4; ++i) shift_low(out);
-    if (have_cache) {
-      out.put(cache);
-      for (; nff; --nff) out.put(0xFFu);
+      written += 4u;
+      e.p2 = 0u;
+      e.p1 = s >= 32u ? 0u : e.p1 & ((1u << s) - 1u);
+      e.nbits -= 32u;
     }
   }
 };
@@ -220,6 +214,7 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_stats(
     float lo, sa, maxabs;
     if (!stream_stats(x, ld, n, d.G, lo, sa, maxabs)) set_status(status, KVC_ERR_NONFINITE);
     const float dl = maxabs / (float)M;
+    const float inv_sa = 1.0f / sa, inv_dl = 1.0f / dl;
 
     // coded length = 4 + number of renormalisation shifts
     uint32_t range = 0xFFFFFFFFu;
@@ -230,11 +225,11 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_stats(
     for_each_token<kTokenBatch>(x, ld, 0, 1, n, [&](float v) {
       uint32_t f;
       if (g == 0) {
-        const uint32_t qa = quant_anchor(v, lo, sa);
+        const uint32_t qa = quant_anchor(v, lo, sa, inv_sa);
         ahat = __builtin_fmaf((float)qa, sa, lo);
         f = (uint32_t)ta[qa + 1] - ta[qa];
       } else {
-        const uint32_t s = (uint32_t)(quant_delta(v - ahat, dl, M) + M);
+        const uint32_t s = (uint32_t)(quant_delta(v - ahat, dl, inv_dl, M) + M);
         f = (uint32_t)td[s + 1] - td[s];
       }
       g = g + 1 == d.G ? 0 : g + 1;
@@ -243,10 +238,10 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_stats(
         f = 1;
       }
       range = (range >> kPrec) * f;
-      while (range < (1u << 24)) {
-        range <<= 8;
-        ++shifts;
-      }
+      // whole bytes to shift: 0, 1 or 2 (range >= 2^9 with f >= 1)
+      const uint32_t sh = lead_zeros(range) & 24u;
+      range <<= sh;
+      shifts += sh >> 3;
     });
     if (damaged) set_status(status, KVC_ERR_CORRUPT_STREAM);
     uint32_t *rec = reinterpret_cast<uint32_t *>(records + ((uint64_t)k * S + m) * kRecBytes);
@@ -324,6 +319,7 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
     const float lo = __builtin_bit_cast(float, rin[0]);
     const float sa = __builtin_bit_cast(float, rin[1]);
     const float dl = __builtin_bit_cast(float, rin[2]);
+    const float inv_sa = 1.0f / sa, inv_dl = 1.0f / dl;
     const uint32_t nbytes = rin[3];
 
     uint8_t *cont = out + chunk_off[k];
@@ -340,18 +336,16 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
     sink.queue = queues + (wave * kWave + lane) * kQueue;
     sink.cnt = 0;
     sink.head = sink.tail = 0;
-    sink.w0 = sink.w1 = sink.nacc = 0;
-    sink.count = 0;
+    sink.slot = 0;
+    sink.written = 0;
     sink.cap = nbytes;
     sink.overflow = false;
     sink.window = false;
     RangeEncoder enc;
     enc.low = 0;
     enc.range = 0xFFFFFFFFu;
-    enc.cache = 0;
-    enc.nff = 0;
-    enc.have_cache = false;
-    enc.bad = false;
+    enc.p0 = enc.p1 = enc.p2 = 0;
+    enc.nbits = 0;
 
     // The decoder's reading rule, run alongside: R bytes consumed by the
     // decoder, W bytes it holds, q its next block to ask for; the unit's
@@ -374,7 +368,7 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
     const uint32_t n = c.n_tokens;
     float ahat = 0.0f;
     uint32_t g = 0;
-    for_each_token<kTokenBatch>(x, ld, 0, 1, n, [&](float v) {
+    for_each_token<kEmitBatch>(x, ld, 0, 1, n, [&](float v) {
       // before this token: a reader ring with at most 8 bytes (anchor) or
       // fewer than 2 bytes (other tokens) takes its next block and asks for
       // one
@@ -393,25 +387,69 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
       }
       uint32_t cs, f;
       if (g == 0) {
-        const uint32_t qa = quant_anchor(v, lo, sa);
+        const uint32_t qa = quant_anchor(v, lo, sa, inv_sa);
         ahat = __builtin_fmaf((float)qa, sa, lo);
         cs = ta[qa];
         f = (uint32_t)ta[qa + 1] - cs;
       } else {
-        const uint32_t s = (uint32_t)(quant_delta(v - ahat, dl, M) + M);
+        const uint32_t s = (uint32_t)(quant_delta(v - ahat, dl, inv_dl, M) + M);
         cs = td[s];
         f = (uint32_t)td[s + 1] - cs;
       }
       g = g + 1 == d.G ? 0 : g + 1;
       if (f == 0 || f > kTot) f = 1;  // damaged tables: already reported by the stats pass
-      R += enc.encode(cs, f, sink);
+      R += enc.encode(cs, f);
+      const bool full = enc.nbits >= 80u;
+      if (__builtin_amdgcn_ballot_w64(full) != 0) sink.take4(enc, full);
     });
-    enc.finish(sink);
-    sink.flush();
+    // the final 4 bytes of low, 2 at a time
+#pragma unroll
+    for (uint32_t h = 0; h < 2; ++h) {
+      enc.append(16u);
+      const bool full = enc.nbits >= 80u;
+      if (__builtin_amdgcn_ballot_w64(full) != 0) sink.take4(enc, full);
+    }
+    // The rest (nbits <= 72): a carry past the held bytes shows as a set bit
+    // at or above nbits; then zero bytes up to whole dwords, which leave the
+    // oldest first, and a zero dword to complete the last block.
+    {
+      const uint32_t nb = enc.nbits;
+      const uint64_t hi = ((uint64_t)enc.p2 << 32) | enc.p1;
+      const bool lost = nb >= 32u ? (hi >> (nb - 32u)) != 0
+                                  : (hi != 0 || ((uint64_t)enc.p0 >> nb) != 0);
+      const uint32_t pad = (32u - (nb & 31u)) & 31u;
+      enc.append(pad);  // low is spent; its bits are no longer used
+      sink.window = sink.window || lost;
+      uint32_t words[3] = {enc.p0, enc.p1, enc.p2};
+#pragma unroll
+      for (uint32_t w = 3; w-- > 0;) {
+        const bool take = enc.nbits > 32u * w;
+        if (take) {
+          const bool first = (sink.written & 4u) == 0;
+          if (first) {
+            if (sink.head == sink.tail) sink.overflow = true;
+            else sink.slot = sink.queue[sink.head % kQueue];
+            ++sink.head;
+          }
+          if (sink.written + 4u > pad8(nbytes)) sink.overflow = true;
+          if (!sink.overflow && !sink.window)
+            *reinterpret_cast<uint32_t *>(sink.pay + (uint64_t)sink.slot * kBlock +
+                                          (sink.written & 4u)) = __builtin_bswap32(words[w]);
+          sink.written += 4u;
+        }
+      }
+      if ((sink.written & 4u) != 0) {
+        if (sink.written + 4u > pad8(nbytes)) sink.overflow = true;
+        if (!sink.overflow && !sink.window)
+          *reinterpret_cast<uint32_t *>(sink.pay + (uint64_t)sink.slot * kBlock + 4u) = 0u;
+        sink.written += 4u;
+      }
+    }
     if (sink.window) {
-      // a run of pending carry bytes longer than the block queue
+      // the decoder more blocks ahead than the queue holds, or a carry
+      // through a run of 6 or more 0xFF bytes
       set_status(status, KVC_ERR_UNIMPLEMENTED);
-    } else if (enc.bad || sink.overflow || sink.count != nbytes || q != nblk ||
+    } else if (sink.overflow || R != nbytes || sink.written != pad8(nbytes) || q != nblk ||
                sink.head != sink.tail) {
       set_status(status, KVC_ERR_CORRUPT_STREAM);
     }

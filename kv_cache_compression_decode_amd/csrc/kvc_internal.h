@@ -148,22 +148,42 @@ __device__ inline bool is_finite(float v) { return __builtin_isfinite(v); }
 // One stream = column c of x (stride `ld` elements), tokens 0..n-1.
 // Anchors: j % G == 0, 8-bit affine over [min, max] of the anchors
 // (first occurrence kept on ties: strict comparisons).
-__device__ inline uint32_t quant_anchor(float x, float lo, float sa) {
-  if (sa == 0.0f) return 0u;
-  float v = __builtin_rintf((x - lo) / sa);
-  int q = (int)v;
-  q = q < 0 ? 0 : q;
-  q = q > 255 ? 255 : q;
-  return (uint32_t)q;
+//
+// rintf(num / den) with the correctly rounded quotient, from the product
+// y = num * inv, inv = 1 / den rounded: y is within |q| 1.5 2^-23 of the
+// rounded quotient q, at most 2^-14 for the |q| <= 257 of both quantizers,
+// so the two round to the same integer unless y lies within that distance
+// of a half-integer; only then (rarely, and per lane) is the division done.
+// The quantizers' denominators are normal (sa >= 2^-24 / 255 and dl > 2^-70
+// for binary16 inputs), so inv is finite.
+// The test is wave-uniform (a branch on the ballot, not a divergent one),
+// and the rare division is done by the whole wave.
+__device__ inline float rint_quot(float num, float den, float inv) {
+  const float y = num * inv;
+  float r = __builtin_rintf(y);
+  // y - r and |y - r| - 0.5 are exact near the threshold
+  const bool near_half = __builtin_fabsf(__builtin_fabsf(y - r) - 0.5f) <= 0x1p-13f;
+  if (__builtin_amdgcn_ballot_w64(near_half) != 0) {
+    const float e = __builtin_rintf(num / den);
+    r = near_half ? e : r;
+  }
+  return r;
 }
 
-__device__ inline int32_t quant_delta(float d, float dl, int32_t M) {
-  if (dl == 0.0f) return 0;
-  float v = __builtin_rintf(d / dl);
-  int q = (int)v;
+// inv_sa = 1 / sa (any value when sa = 0: the result is then 0)
+__device__ inline uint32_t quant_anchor(float x, float lo, float sa, float inv_sa) {
+  int q = (int)rint_quot(x - lo, sa, inv_sa);
+  q = q < 0 ? 0 : q;
+  q = q > 255 ? 255 : q;
+  return sa == 0.0f ? 0u : (uint32_t)q;
+}
+
+// inv_dl = 1 / dl (any value when dl = 0: the result is then 0)
+__device__ inline int32_t quant_delta(float d, float dl, float inv_dl, int32_t M) {
+  int q = (int)rint_quot(d, dl, inv_dl);
   q = q < -M ? -M : q;
   q = q > M ? M : q;
-  return q;
+  return dl == 0.0f ? 0 : q;
 }
 
 // Stream statistics: lo, sa (anchor scale) and maxabs of the closed-loop
@@ -196,6 +216,7 @@ __device__ inline bool stream_stats(const uint16_t *__restrict__ x, uint64_t ld,
     if (v > hi) hi = v;
   });
   const float sa = (hi - lo) / 255.0f;
+  const float inv_sa = 1.0f / sa;
   bool finite = true;
   float maxabs = 0.0f;
   float ahat = 0.0f;
@@ -203,7 +224,7 @@ __device__ inline bool stream_stats(const uint16_t *__restrict__ x, uint64_t ld,
   for_each_token<kTokenBatch>(x, ld, 0, 1, n, [&](float v) {
     finite = finite && is_finite(v);
     if (g == 0) {
-      ahat = __builtin_fmaf((float)quant_anchor(v, lo, sa), sa, lo);
+      ahat = __builtin_fmaf((float)quant_anchor(v, lo, sa, inv_sa), sa, lo);
     } else {
       const float a = __builtin_fabsf(v - ahat);
       if (a > maxabs) maxabs = a;

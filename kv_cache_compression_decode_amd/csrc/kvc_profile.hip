@@ -44,9 +44,10 @@ __global__ __launch_bounds__(64) void k_profile_count(Desc d, const uint16_t *__
     const uint16_t *x = kv + ((uint64_t)row * T + t0) * ld + c0 + lane;
     float lo, sa, maxabs;
     if (!stream_stats(x, ld, n, d.G, lo, sa, maxabs)) set_status(status, KVC_ERR_NONFINITE);
+    const float inv_sa = 1.0f / sa;
     // anchors
     for (uint32_t j = 0; j < n; j += d.G) {
-      const uint32_t qa = quant_anchor(h2f(x[(uint64_t)j * ld]), lo, sa);
+      const uint32_t qa = quant_anchor(h2f(x[(uint64_t)j * ld]), lo, sa, inv_sa);
       hist[qa * kWave + lane] += 1;
     }
     // deltas, once per level
@@ -54,15 +55,16 @@ __global__ __launch_bounds__(64) void k_profile_count(Desc d, const uint16_t *__
       const uint32_t b = d.bits[lv][third];
       const int32_t M = (1 << (b - 1)) - 1;
       const float dl = maxabs / (float)M;
+      const float inv_dl = 1.0f / dl;
       const uint32_t base = kAnchorAlpha + lv * kDeltaStride;
       float ahat = 0.0f;
       uint32_t g = 0;
       for (uint32_t j = 0; j < n; ++j) {
         const float v = h2f(x[(uint64_t)j * ld]);
         if (g == 0) {
-          ahat = __builtin_fmaf((float)quant_anchor(v, lo, sa), sa, lo);
+          ahat = __builtin_fmaf((float)quant_anchor(v, lo, sa, inv_sa), sa, lo);
         } else {
-          const uint32_t s = (uint32_t)(quant_delta(v - ahat, dl, M) + M);
+          const uint32_t s = (uint32_t)(quant_delta(v - ahat, dl, inv_dl, M) + M);
           hist[(base + s) * kWave + lane] += 1;
         }
         g = g + 1 == d.G ? 0 : g + 1;
