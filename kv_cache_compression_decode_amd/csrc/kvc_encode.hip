@@ -113,13 +113,16 @@ struct RangeEncoder {
     range <<= sh;
     return sh >> 3;
   }
-  // Moves the top `sh` bits (0, 8 or 16) of low into the held bytes.
+  // Moves the top `sh` bits (0, 8, 16 or 24) of low into the held bytes:
+  // each register takes the dword `sh` bits down in (itself : the next
+  // lower one), one byte permute whose selector, bytes 7 - k .. 4 - k for
+  // k = sh / 8, is the high dword of 0x0706050403020100 << sh.
   __device__ inline void append(uint32_t sh) {
-    const uint64_t l = (uint64_t)low << sh;
-    low = (uint32_t)l;
-    p2 = (uint32_t)((((uint64_t)p2 << 32) | p1) << sh >> 32);
-    p1 = (uint32_t)((((uint64_t)p1 << 32) | p0) << sh >> 32);
-    p0 = (p0 << sh) | (uint32_t)(l >> 32);
+    const uint32_t sel = (uint32_t)((0x0706050403020100ull << sh) >> 32);
+    p2 = __builtin_amdgcn_perm(p2, p1, sel);
+    p1 = __builtin_amdgcn_perm(p1, p0, sel);
+    p0 = __builtin_amdgcn_perm(p0, low, sel);
+    low <<= sh;
     nbits += sh;
   }
 };
@@ -143,31 +146,37 @@ struct BlockSink {
     queue[tail % kQueue] = blk;
     ++tail;
   }
-  // The 4 oldest held bytes of `e` (which holds at least 4 when `take`) to
-  // the stream, for the lanes with `take`.  Wave-uniform apart from `take`.
+  // The 4 oldest held bytes of `e` (80 to 96 bits held when `take`) to the
+  // stream, for the lanes with `take`.  Wave-uniform apart from `take`.
+  // Every slot is a block this lane asked for, inside the unit's payload;
+  // a lane that has no block left to write (a byte count that disagrees
+  // with the statistics pass) only records it.
   __device__ inline void take4(RangeEncoder &e, bool take) {
-    const uint32_t s = e.nbits - 64u;  // 16..24 (nbits 80..88), or the end's 32..
+    const uint32_t s = e.nbits - 64u;  // 16..32
     // a carry past the held bytes shows as a bit at or above nbits
-    const bool lost = ((uint64_t)e.p2 >> s) != 0;
-    const uint32_t v = (uint32_t)(((((uint64_t)e.p2 << 32) | e.p1) >> s));
+    const uint32_t above = (uint32_t)((uint64_t)e.p2 >> s);
+    const uint32_t v = (uint32_t)((((uint64_t)e.p2 << 32) | e.p1) >> s);
     const bool first = (written & 4u) == 0;
     const uint32_t q = queue[head % kQueue];
-    const bool have = !first || head != tail;
     if (take) {
-      if (first) slot = q;
-      head += first ? 1u : 0u;
-      window = window || lost;
-      overflow = overflow || !have || written + 4u > pad8(cap);
-      if (have && !lost && written + 4u <= pad8(cap)) {
-        // stream order: the oldest byte first
-        *reinterpret_cast<uint32_t *>(pay + (uint64_t)slot * kBlock + (written & 4u)) =
-            __builtin_bswap32(v);
+      window = window || above != 0;
+      const bool have = !first || head != tail;
+      overflow = overflow || !have;
+      if (first) {
+        slot = q;
+        ++head;
       }
+      if (have) put(slot * kBlock + (written & 4u), __builtin_bswap32(v));
       written += 4u;
       e.p2 = 0u;
       e.p1 = s >= 32u ? 0u : e.p1 & ((1u << s) - 1u);
       e.nbits -= 32u;
     }
+  }
+  // A dword at byte `off` of the unit's payload, from a wave-uniform base.
+  __device__ inline void put(uint32_t off, uint32_t v) {
+    __asm__("" : "+v"(off));
+    *reinterpret_cast<uint32_t *>(pay + off) = v;
   }
 };
 
@@ -209,12 +218,13 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_stats(
     const uint16_t *td = reinterpret_cast<const uint16_t *>(sD + (lslot * kWave + lane) * kED);
     const uint32_t b = d.bits[level][third];
     const int32_t M = (1 << (b - 1)) - 1;
-    const uint16_t *x = kv + ((uint64_t)row * T + c.first_token) * ld + c0 + lane;
+    Column x{reinterpret_cast<const uint8_t *>(kv + ((uint64_t)row * T + c.first_token) * ld + c0),
+             2 * ld, 2 * lane};
     const uint32_t n = c.n_tokens;
     float lo, sa, maxabs;
-    if (!stream_stats(x, ld, n, d.G, lo, sa, maxabs)) set_status(status, KVC_ERR_NONFINITE);
+    if (!stream_stats(x, n, d.G, lo, sa, maxabs)) set_status(status, KVC_ERR_NONFINITE);
     const float dl = maxabs / (float)M;
-    const float inv_sa = 1.0f / sa, inv_dl = 1.0f / dl;
+    const float inv_sa = recip_or_zero(sa), inv_dl = recip_or_zero(dl);
 
     // coded length = 4 + number of renormalisation shifts
     uint32_t range = 0xFFFFFFFFu;
@@ -222,7 +232,7 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_stats(
     float ahat = 0.0f;
     uint32_t g = 0;
     bool damaged = false;
-    for_each_token<kTokenBatch>(x, ld, 0, 1, n, [&](float v) {
+    for_each_token<kTokenBatch>(x, 0, 1, n, [&](float v) {
       uint32_t f;
       if (g == 0) {
         const uint32_t qa = quant_anchor(v, lo, sa, inv_sa);
@@ -319,7 +329,7 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
     const float lo = __builtin_bit_cast(float, rin[0]);
     const float sa = __builtin_bit_cast(float, rin[1]);
     const float dl = __builtin_bit_cast(float, rin[2]);
-    const float inv_sa = 1.0f / sa, inv_dl = 1.0f / dl;
+    const float inv_sa = recip_or_zero(sa), inv_dl = recip_or_zero(dl);
     const uint32_t nbytes = rin[3];
 
     uint8_t *cont = out + chunk_off[k];
@@ -364,17 +374,19 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
     }
     sink.cnt = cnt;
 
-    const uint16_t *x = kv + ((uint64_t)row * T + c.first_token) * ld + c0 + lane;
+    Column x{reinterpret_cast<const uint8_t *>(kv + ((uint64_t)row * T + c.first_token) * ld + c0),
+             2 * ld, 2 * lane};
     const uint32_t n = c.n_tokens;
     float ahat = 0.0f;
     uint32_t g = 0;
-    for_each_token<kEmitBatch>(x, ld, 0, 1, n, [&](float v) {
+    for_each_token<kEmitBatch>(x, 0, 1, n, [&](float v) {
       // before this token: a reader ring with at most 8 bytes (anchor) or
       // fewer than 2 bytes (other tokens) takes its next block and asks for
       // one
-      {
-        const uint32_t ahead = W - R;
-        const bool need = g == 0 ? ahead <= 8u : ahead < 2u;
+      // (rare off the anchors: the whole step is skipped when no lane needs)
+      const uint32_t ahead = W - R;
+      const bool need = g == 0 ? ahead <= 8u : ahead < 2u;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
         const bool req = need && q < nblk;
         const uint64_t mask = __builtin_amdgcn_ballot_w64(req);
         if (req) {
@@ -397,7 +409,8 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
         f = (uint32_t)td[s + 1] - cs;
       }
       g = g + 1 == d.G ? 0 : g + 1;
-      if (f == 0 || f > kTot) f = 1;  // damaged tables: already reported by the stats pass
+      // (damaged tables, f = 0 or past 2^15, were reported by the statistics
+      // pass; the bytes then differ from its count and are reported again)
       R += enc.encode(cs, f);
       const bool full = enc.nbits >= 80u;
       if (__builtin_amdgcn_ballot_w64(full) != 0) sink.take4(enc, full);
@@ -433,15 +446,13 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
           }
           if (sink.written + 4u > pad8(nbytes)) sink.overflow = true;
           if (!sink.overflow && !sink.window)
-            *reinterpret_cast<uint32_t *>(sink.pay + (uint64_t)sink.slot * kBlock +
-                                          (sink.written & 4u)) = __builtin_bswap32(words[w]);
+            sink.put(sink.slot * kBlock + (sink.written & 4u), __builtin_bswap32(words[w]));
           sink.written += 4u;
         }
       }
       if ((sink.written & 4u) != 0) {
         if (sink.written + 4u > pad8(nbytes)) sink.overflow = true;
-        if (!sink.overflow && !sink.window)
-          *reinterpret_cast<uint32_t *>(sink.pay + (uint64_t)sink.slot * kBlock + 4u) = 0u;
+        if (!sink.overflow && !sink.window) sink.put(sink.slot * kBlock + 4u, 0u);
         sink.written += 4u;
       }
     }

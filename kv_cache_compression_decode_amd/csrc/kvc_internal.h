@@ -170,58 +170,78 @@ __device__ inline float rint_quot(float num, float den, float inv) {
   return r;
 }
 
-// inv_sa = 1 / sa (any value when sa = 0: the result is then 0)
+// 1 / s, or 0 for a zero scale.  A zero scale quantizes everything to 0:
+// sa = 0 only when every anchor equals lo, dl = 0 only when every delta is
+// 0, so the numerator times 0 is 0 (for finite inputs), far from a
+// half-integer.
+__device__ inline float recip_or_zero(float s) { return s == 0.0f ? 0.0f : 1.0f / s; }
+
+// inv_sa = recip_or_zero(sa)
 __device__ inline uint32_t quant_anchor(float x, float lo, float sa, float inv_sa) {
   int q = (int)rint_quot(x - lo, sa, inv_sa);
   q = q < 0 ? 0 : q;
   q = q > 255 ? 255 : q;
-  return sa == 0.0f ? 0u : (uint32_t)q;
+  return (uint32_t)q;
 }
 
-// inv_dl = 1 / dl (any value when dl = 0: the result is then 0)
+// inv_dl = recip_or_zero(dl)
 __device__ inline int32_t quant_delta(float d, float dl, float inv_dl, int32_t M) {
   int q = (int)rint_quot(d, dl, inv_dl);
   q = q < -M ? -M : q;
   q = q > M ? M : q;
-  return dl == 0.0f ? 0 : q;
+  return q;
 }
 
-// Stream statistics: lo, sa (anchor scale) and maxabs of the closed-loop
-// deltas.  Returns false if a value is not finite.
-// Visits the tokens first, first + step, ... (< n) of a lane's column x
-// (row stride ld elements) in order, calling f(value).  The values are
-// loaded kBatch at a time, so a wave waits for memory once per batch
-// rather than once per token.
+// A lane's column of binary16 KV values: token j of the lane's channel is
+// at base + j * ld2 + loff, with base the same for the whole wave.  The
+// empty asm makes the lane offset opaque at every load, so that the
+// address stays "scalar base + 32-bit lane offset" (a global load with a
+// scalar base and no per-lane 64-bit address arithmetic).
+struct Column {
+  const uint8_t *base;  // wave-uniform
+  uint64_t ld2;         // bytes from one token to the next
+  uint32_t loff;        // this lane's byte offset
+  __device__ inline float at(uint32_t j) {
+    __asm__("" : "+v"(loff));
+    return h2f(*reinterpret_cast<const uint16_t *>(base + (uint64_t)j * ld2 + loff));
+  }
+};
+
+// Visits the tokens first, first + step, ... (< n) of a lane's column in
+// order, calling f(value).  The values are loaded kBatch at a time, so a
+// wave waits for memory once per batch rather than once per token.
 template <uint32_t kBatch, class F>
-__device__ inline void for_each_token(const uint16_t *__restrict__ x, uint64_t ld, uint32_t first,
-                                      uint32_t step, uint32_t n, F &&f) {
+__device__ inline void for_each_token(Column &x, uint32_t first, uint32_t step, uint32_t n,
+                                      F &&f) {
   uint32_t j = first;
   for (; j + (kBatch - 1) * step < n; j += kBatch * step) {
-    uint16_t v[kBatch];
+    float v[kBatch];
 #pragma unroll
-    for (uint32_t u = 0; u < kBatch; ++u) v[u] = x[(uint64_t)(j + u * step) * ld];
+    for (uint32_t u = 0; u < kBatch; ++u) v[u] = x.at(j + u * step);
 #pragma unroll
-    for (uint32_t u = 0; u < kBatch; ++u) f(h2f(v[u]));
+    for (uint32_t u = 0; u < kBatch; ++u) f(v[u]);
   }
-  for (; j < n; j += step) f(h2f(x[(uint64_t)j * ld]));
+  for (; j < n; j += step) f(x.at(j));
 }
 constexpr uint32_t kTokenBatch = 16;
 
-__device__ inline bool stream_stats(const uint16_t *__restrict__ x, uint64_t ld, uint32_t n,
-                                    uint32_t G, float &lo_out, float &sa_out, float &maxabs_out) {
-  float lo = h2f(x[0]);
+// Stream statistics: lo, sa (anchor scale) and maxabs of the closed-loop
+// deltas.  Returns false if a value is not finite.
+__device__ inline bool stream_stats(Column &x, uint32_t n, uint32_t G, float &lo_out,
+                                    float &sa_out, float &maxabs_out) {
+  float lo = x.at(0);
   float hi = lo;
-  for_each_token<kTokenBatch>(x, ld, G, G, n, [&](float v) {
+  for_each_token<kTokenBatch>(x, G, G, n, [&](float v) {
     if (v < lo) lo = v;
     if (v > hi) hi = v;
   });
   const float sa = (hi - lo) / 255.0f;
-  const float inv_sa = 1.0f / sa;
+  const float inv_sa = recip_or_zero(sa);
   bool finite = true;
   float maxabs = 0.0f;
   float ahat = 0.0f;
   uint32_t g = 0;  // position in the group (0: the anchor)
-  for_each_token<kTokenBatch>(x, ld, 0, 1, n, [&](float v) {
+  for_each_token<kTokenBatch>(x, 0, 1, n, [&](float v) {
     finite = finite && is_finite(v);
     if (g == 0) {
       ahat = __builtin_fmaf((float)quant_anchor(v, lo, sa, inv_sa), sa, lo);

@@ -41,13 +41,14 @@ __global__ __launch_bounds__(64) void k_profile_count(Desc d, const uint16_t *__
   for (uint32_t k = 0; k < nchunks; ++k) {
     const uint32_t t0 = k * d.chunk;
     const uint32_t n = T - t0 < d.chunk ? T - t0 : d.chunk;
-    const uint16_t *x = kv + ((uint64_t)row * T + t0) * ld + c0 + lane;
+    Column x{reinterpret_cast<const uint8_t *>(kv + ((uint64_t)row * T + t0) * ld + c0), 2 * ld,
+             2 * lane};
     float lo, sa, maxabs;
-    if (!stream_stats(x, ld, n, d.G, lo, sa, maxabs)) set_status(status, KVC_ERR_NONFINITE);
-    const float inv_sa = 1.0f / sa;
+    if (!stream_stats(x, n, d.G, lo, sa, maxabs)) set_status(status, KVC_ERR_NONFINITE);
+    const float inv_sa = recip_or_zero(sa);
     // anchors
     for (uint32_t j = 0; j < n; j += d.G) {
-      const uint32_t qa = quant_anchor(h2f(x[(uint64_t)j * ld]), lo, sa, inv_sa);
+      const uint32_t qa = quant_anchor(x.at(j), lo, sa, inv_sa);
       hist[qa * kWave + lane] += 1;
     }
     // deltas, once per level
@@ -55,12 +56,12 @@ __global__ __launch_bounds__(64) void k_profile_count(Desc d, const uint16_t *__
       const uint32_t b = d.bits[lv][third];
       const int32_t M = (1 << (b - 1)) - 1;
       const float dl = maxabs / (float)M;
-      const float inv_dl = 1.0f / dl;
+      const float inv_dl = recip_or_zero(dl);
       const uint32_t base = kAnchorAlpha + lv * kDeltaStride;
       float ahat = 0.0f;
       uint32_t g = 0;
       for (uint32_t j = 0; j < n; ++j) {
-        const float v = h2f(x[(uint64_t)j * ld]);
+        const float v = x.at(j);
         if (g == 0) {
           ahat = __builtin_fmaf((float)quant_anchor(v, lo, sa, inv_sa), sa, lo);
         } else {
