@@ -254,3 +254,53 @@ def test_constant_and_extreme_channels_bit_exact():
     assert np.array_equal(enc.container(0).cpu().numpy(), oc[0])
     out = kvc.decode(d, tables, kvc.chunk_refs(enc), 1500)
     np.testing.assert_array_equal(out.cpu().numpy().view(np.uint16), oo)
+
+
+def test_quantizer_ties_bit_exact():
+    """Inputs whose quantizer quotients are exact half-integers, where rint's
+    ties-to-even decides the symbol (CacheGen page, 核心方法: 8-bit anchors,
+    delta bins per layer third): the encoder's reciprocal shortcut must
+    fall back to the correctly rounded quotient there and match the
+    oracle's plain division.
+      channel 1: anchors (2k + 1) / 32 for k = 0..254 plus lo = 0 and
+        hi = 255/16 in each chunk, so sa = 2^-4 and (x - lo) / sa = k + 1/2;
+      channel 2: anchors all 1.0 (sa = 0, ahat = 1), deltas (2k + 1) / 128
+        for k = -M..M-1 plus one of M / 64 in each chunk, so dl = 2^-6 and
+        d / dl = k + 1/2 (M = 31, 15, 7 in the three layers' thirds)."""
+    cfg = synth.small_config(3, 64, 3000, n_levels=1, index=97)
+    kv = synth.make_kv(cfg).copy()
+    n = cfg.n_tokens
+    f16 = lambda a: np.asarray(a, np.float16).view(np.uint16)
+    anchors = np.arange(0, n, 10)
+    ks = np.arange(len(anchors)) % 255
+    ch1 = np.full(n, f16(3.0))
+    ch1[anchors] = f16((2 * ks + 1) / 32.0)
+    for t0 in (0, 1500):  # each chunk has its own lo and hi
+        ch1[t0] = f16(0.0)
+        ch1[t0 + 10] = f16(255 / 16.0)
+    rows = [0, 1]
+    for layer in range(3):
+        M = (1 << (cfg.delta_bits[0][layer] - 1)) - 1
+        ch2 = np.empty(n, np.uint16)
+        ch2[:] = f16(1.0)
+        deltas = [j for j in range(n) if j % 10]
+        k = (np.arange(len(deltas)) % (2 * M)) - M
+        ch2[deltas] = f16(1.0 + (2 * k + 1) / 128.0)
+        for t0 in (0, 1500):  # and its own largest delta
+            ch2[t0 + 5] = f16(1.0 + M / 64.0)
+        for kvr in rows:
+            kv[layer, kvr, :, 1] = ch1
+            kv[layer, kvr, :, 2] = ch2
+    kvp = np.concatenate([kv, kv, kv], axis=2)
+    od = oracle.desc_for(cfg)
+    otb = oracle.profile(od, kvp)
+    oc = oracle.encode(od, otb, kv, [0, 0])
+    oo = oracle.decode(od, otb, oc, [0, 0], n)
+    d = kvc.make_desc(3, 64, cfg.delta_bits)
+    tables = kvc.profile(d, _t(kvp))
+    assert kvc.profile_id(tables) == otb.profile_id
+    enc = kvc.encode(d, tables, _t(kv), [0, 0])
+    for c in range(2):
+        assert np.array_equal(enc.container(c).cpu().numpy(), oc[c])
+    out = kvc.decode(d, tables, kvc.chunk_refs(enc), n)
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint16), oo)
