@@ -146,27 +146,29 @@ struct BlockSink {
     queue[tail % kQueue] = blk;
     ++tail;
   }
+  // Starts the next block: its slot is the oldest queued request.  A lane
+  // with no request left (a byte count that disagrees with the statistics
+  // pass, from damaged tables) stops writing for good, so every store goes
+  // to a block this lane asked for, inside the unit's payload.
+  __device__ inline void next_block() {
+    if (head == tail) {
+      overflow = true;
+    } else {
+      slot = queue[head % kQueue];
+      ++head;
+    }
+  }
   // The 4 oldest held bytes of `e` (80 to 96 bits held when `take`) to the
   // stream, for the lanes with `take`.  Wave-uniform apart from `take`.
-  // Every slot is a block this lane asked for, inside the unit's payload;
-  // a lane that has no block left to write (a byte count that disagrees
-  // with the statistics pass) only records it.
   __device__ inline void take4(RangeEncoder &e, bool take) {
     const uint32_t s = e.nbits - 64u;  // 16..32
     // a carry past the held bytes shows as a bit at or above nbits
     const uint32_t above = (uint32_t)((uint64_t)e.p2 >> s);
     const uint32_t v = (uint32_t)((((uint64_t)e.p2 << 32) | e.p1) >> s);
-    const bool first = (written & 4u) == 0;
-    const uint32_t q = queue[head % kQueue];
     if (take) {
       window = window || above != 0;
-      const bool have = !first || head != tail;
-      overflow = overflow || !have;
-      if (first) {
-        slot = q;
-        ++head;
-      }
-      if (have) put(slot * kBlock + (written & 4u), __builtin_bswap32(v));
+      if ((written & 4u) == 0) next_block();
+      if (!overflow) put(slot * kBlock + (written & 4u), __builtin_bswap32(v));
       written += 4u;
       e.p2 = 0u;
       e.p1 = s >= 32u ? 0u : e.p1 & ((1u << s) - 1u);
@@ -438,12 +440,7 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
       for (uint32_t w = 3; w-- > 0;) {
         const bool take = enc.nbits > 32u * w;
         if (take) {
-          const bool first = (sink.written & 4u) == 0;
-          if (first) {
-            if (sink.head == sink.tail) sink.overflow = true;
-            else sink.slot = sink.queue[sink.head % kQueue];
-            ++sink.head;
-          }
+          if ((sink.written & 4u) == 0) sink.next_block();
           if (sink.written + 4u > pad8(nbytes)) sink.overflow = true;
           if (!sink.overflow && !sink.window)
             sink.put(sink.slot * kBlock + (sink.written & 4u), __builtin_bswap32(words[w]));

@@ -206,6 +206,20 @@ def test_corrupt_containers_are_reported(mixed):
     assert e.value.code == kvc.ERR_CORRUPT_STREAM
 
 
+def test_damaged_tables_are_reported_by_encode(mixed):
+    """A model whose every frequency is 0 (all cumulative counts 0, so no
+    symbol has an interval): the statistics pass reports the stream, and
+    emit, whose coder then shifts out 3 bytes a token, more than the blocks
+    its lane asked for, stops writing instead of storing past them."""
+    bad_tables = mixed.tables.clone()
+    S = mixed.d.n_streams
+    anchor = bad_tables[128:128 + S * 528].view(torch.int16).view(S, 264)
+    anchor[5, :257] = 0
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.encode(mixed.d, bad_tables, mixed.kv_dev, mixed.levels)
+    assert e.value.code == kvc.ERR_CORRUPT_STREAM
+
+
 def test_overlap_rejected_synchronously(mixed):
     enc = _upload_oracle(mixed)
     refs = kvc.chunk_refs(enc, chunks=[0, 1], first_tokens=[0, 1000])
