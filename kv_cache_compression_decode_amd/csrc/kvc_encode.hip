@@ -64,6 +64,14 @@ __device__ inline void stage_tables(const Desc &d, const uint8_t *tables, uint32
   }
 }
 
+// A staged model is well formed: cum[0] = 0, cum[A] = 2^15, and every
+// symbol's frequency at least 1.
+__device__ inline bool model_ok(const uint16_t *cum, uint32_t A) {
+  bool ok = cum[0] == 0 && cum[A] == kTot;
+  for (uint32_t s = 0; s < A; ++s) ok = ok && cum[s] < cum[s + 1];
+  return ok;
+}
+
 // Which (unit, group) a block owns: the groups of one (row, channel block)
 // on the same XCD.
 struct EncodeBlock {
@@ -211,6 +219,20 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_stats(
   const uint16_t *ta = reinterpret_cast<const uint16_t *>(sA + lane * kEA);
   const uint32_t third = third_of(row >> 1, d.L);
   const uint64_t ld = d.C;
+  // Damaged tables are reported once, from the staged models.  The coders
+  // of this pass and of emit then run the same (meaningless) range
+  // evolution, so their byte counts still agree.
+  if (wave == 0) {
+    bool ok = model_ok(ta, 256);
+    uint32_t slot = 0;
+    for (uint32_t lv = 0; lv < d.nlev; ++lv) {
+      if (!((gp.level >> lv) & 1u)) continue;
+      const uint16_t *td = reinterpret_cast<const uint16_t *>(sD + (slot * kWave + lane) * kED);
+      ok = ok && model_ok(td, (1u << d.bits[lv][third]) - 1u);
+      ++slot;
+    }
+    if (!ok) set_status(status, KVC_ERR_CORRUPT_STREAM);
+  }
 
   for (uint32_t i = wave; i < gp.count; i += n_waves) {
     const uint32_t k = gp.start + i;
@@ -233,7 +255,6 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_stats(
     uint32_t shifts = 0;
     float ahat = 0.0f;
     uint32_t g = 0;
-    bool damaged = false;
     for_each_token<kTokenBatch>(x, 0, 1, n, [&](float v) {
       uint32_t f;
       if (g == 0) {
@@ -245,17 +266,13 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_stats(
         f = (uint32_t)td[s + 1] - td[s];
       }
       g = g + 1 == d.G ? 0 : g + 1;
-      if (f == 0 || f > kTot) {  // damaged tables
-        damaged = true;
-        f = 1;
-      }
-      range = (range >> kPrec) * f;
+      // the encoder's update (24-bit multiply: r < 2^17, f <= 2^15)
+      range = __umul24(range >> kPrec, f);
       // whole bytes to shift: 0, 1 or 2 (range >= 2^9 with f >= 1)
       const uint32_t sh = lead_zeros(range) & 24u;
       range <<= sh;
       shifts += sh >> 3;
     });
-    if (damaged) set_status(status, KVC_ERR_CORRUPT_STREAM);
     uint32_t *rec = reinterpret_cast<uint32_t *>(records + ((uint64_t)k * S + m) * kRecBytes);
     rec[0] = __builtin_bit_cast(uint32_t, lo);
     rec[1] = __builtin_bit_cast(uint32_t, sa);
@@ -411,8 +428,8 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
         f = (uint32_t)td[s + 1] - cs;
       }
       g = g + 1 == d.G ? 0 : g + 1;
-      // (damaged tables, f = 0 or past 2^15, were reported by the statistics
-      // pass; the bytes then differ from its count and are reported again)
+      // (damaged tables were reported by the statistics pass, which ran the
+      // same coder on them)
       R += enc.encode(cs, f);
       const bool full = enc.nbits >= 80u;
       if (__builtin_amdgcn_ballot_w64(full) != 0) sink.take4(enc, full);
