@@ -167,21 +167,26 @@ struct BlockSink {
     }
   }
   // The 4 oldest held bytes of `e` (80 to 96 bits held when `take`) to the
-  // stream, for the lanes with `take`.  Wave-uniform apart from `take`.
+  // stream, for the lanes with `take`.  Wave-uniform apart from `take`, and
+  // written as selects: only the store itself is predicated.
   __device__ inline void take4(RangeEncoder &e, bool take) {
-    const uint32_t s = e.nbits - 64u;  // 16..32
+    const uint32_t s = (e.nbits - 64u) & 63u;  // 16..32 where taken
     // a carry past the held bytes shows as a bit at or above nbits
     const uint32_t above = (uint32_t)((uint64_t)e.p2 >> s);
     const uint32_t v = (uint32_t)((((uint64_t)e.p2 << 32) | e.p1) >> s);
-    if (take) {
-      window = window || above != 0;
-      if ((written & 4u) == 0) next_block();
-      if (!overflow) put(slot * kBlock + (written & 4u), __builtin_bswap32(v));
-      written += 4u;
-      e.p2 = 0u;
-      e.p1 = s >= 32u ? 0u : e.p1 & ((1u << s) - 1u);
-      e.nbits -= 32u;
-    }
+    const uint32_t queued = queue[head % kQueue];
+    const bool starts = take && (written & 4u) == 0;  // a new block
+    const bool got = starts && head != tail;
+    window = window || (take && above != 0);
+    overflow = overflow || (starts && !got);
+    slot = got ? queued : slot;
+    head += got ? 1u : 0u;
+    if (take && !overflow) put(slot * kBlock + (written & 4u), __builtin_bswap32(v));
+    written += take ? 4u : 0u;
+    const uint32_t kept = s >= 32u ? 0u : e.p1 & ((1u << (s & 31u)) - 1u);
+    e.p1 = take ? kept : e.p1;
+    e.p2 = take ? 0u : e.p2;
+    e.nbits -= take ? 32u : 0u;
   }
   // A dword at byte `off` of the unit's payload, from a wave-uniform base.
   __device__ inline void put(uint32_t off, uint32_t v) {
