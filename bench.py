@@ -94,6 +94,40 @@ def measured_valu_insts():
         return None
 
 
+def hip_clocks(compute_units: int) -> dict:
+    """Peak engine and memory clocks (MHz) from hipDeviceGetAttribute, called
+    through the HIP runtime this process has already loaded (found in
+    /proc/self/maps, so no second copy is opened).  Attribute numbers of
+    hipDeviceAttribute_t in hip_runtime_api.h: 5 clock rate, 60 memory clock
+    rate, 63 multiprocessor count, which must read back the CU count torch
+    reports; otherwise nothing is recorded."""
+    import ctypes
+
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {ln.split()[-1] for ln in f if "libamdhip64.so" in ln}
+        if len(paths) != 1:
+            return {}
+        hip = ctypes.CDLL(paths.pop())
+        value = ctypes.c_int()
+
+        def attr(n: int):
+            if hip.hipDeviceGetAttribute(ctypes.byref(value), ctypes.c_int(n), ctypes.c_int(0)) != 0:
+                return None
+            return value.value
+
+        if attr(63) != compute_units:
+            return {}
+        out = {}
+        for key, n in (("max_engine_clock_MHz", 5), ("max_memory_clock_MHz", 60)):
+            v = attr(n)
+            if v:
+                out[key] = round(v / 1000)
+        return out
+    except OSError:
+        return {}
+
+
 def sha256_of(a) -> str:
     import hashlib
 
@@ -500,10 +534,7 @@ def main() -> int:
         "name": props.name, "arch": getattr(props, "gcnArchName", ""),
         "compute_units": props.multi_processor_count,
     }
-    for key, attr in (("max_engine_clock_MHz", "clock_rate"),
-                      ("max_memory_clock_MHz", "memory_clock_rate")):
-        if getattr(props, attr, 0):  # not reported by every runtime
-            result["device"][key] = round(getattr(props, attr) / 1000)
+    result["device"].update(hip_clocks(props.multi_processor_count))
 
     # ---- CPU oracle: bit-exact check on a sample of chunks + its own rate
     if not args.no_oracle:
