@@ -33,10 +33,11 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 # SIMD every 4 cycles (16 lanes per cycle) at 2.4 GHz
 VALU_PEAK_WAVE_INSTS = 256 * 4 * 2.4e9 / 4
 COPY_CALIBRATION_BYTES = 1 << 30
-# rocprofv3 HBM counter summary of the decode kernel on this workload; its
-# traffic figure is reported only while the kernel sources still hash to the
-# value recorded there.
+# rocprofv3 HBM counter summary of the decode kernel on the 70B-shaped GQA
+# workload; its figures are reported only for that workload, and only while the
+# kernel sources still hash to the value recorded there.
 COUNTERS_MD = os.path.join(ROOT, "profiles", "k_decode_70b-gqa-16K_hbm_counters.md")
+COUNTERS_WORKLOAD = "llama-70b-gqa-shape-16K"
 DECODE_SOURCES = [os.path.join(ROOT, "kv_cache_compression_decode_amd", "csrc", f)
                   for f in ("kvc_decode.hip", "kvc_internal.h")]
 METRIC = "decoded KV GB/s on 1 MI355X (+% HBM roofline), bit-exact vs oracle; compression ratio"
@@ -56,9 +57,12 @@ def decode_source_hash() -> str:
     return h.hexdigest()
 
 
-def counter_fields():
+def counter_fields(workload: str):
     """(fields, note): the committed counter summary's `- key: value` lines,
-    or None while the decode kernel sources no longer hash to its value."""
+    or None for another workload or while the decode kernel sources no longer
+    hash to its value."""
+    if workload != COUNTERS_WORKLOAD:
+        return None, f"counters were taken on {COUNTERS_WORKLOAD} only"
     if not os.path.exists(COUNTERS_MD):
         return None, "no counter summary"
     fields = {}
@@ -72,9 +76,9 @@ def counter_fields():
     return fields, "rocprofv3 counters of this kernel source"
 
 
-def measured_traffic():
+def measured_traffic(workload: str):
     """(bytes per decode launch, note) from the committed counter summary."""
-    fields, note = counter_fields()
+    fields, note = counter_fields(workload)
     if fields is None:
         return None, note
     try:
@@ -84,10 +88,10 @@ def measured_traffic():
     return traffic, f"rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a {COPY_CALIBRATION_BYTES}-byte copy"
 
 
-def measured_valu_insts():
+def measured_valu_insts(workload: str):
     """VALU wave-instructions per decode launch (rocprofv3 SQ_INSTS_VALU)
     from the committed counter summary, or None."""
-    fields, _ = counter_fields()
+    fields, _ = counter_fields(workload)
     try:
         return int(fields["valu_insts_per_launch"]) if fields else None
     except (KeyError, ValueError):
@@ -452,8 +456,8 @@ def main() -> int:
         controller = measure_controller(kvc, d, tables, kv_dev, cfg)
         multi = measure_multi(kvc, d, tables, kv_dev, cfg)
 
-    traffic, traffic_note = measured_traffic()
-    valu_insts = measured_valu_insts()
+    traffic, traffic_note = measured_traffic(cfg.name)
+    valu_insts = measured_valu_insts(cfg.name)
     value = fp16_bytes / (ms_per_step * 1e-3) / 1e9
     algo_bytes = fp16_bytes + container_bytes
     achieved = algo_bytes / (kernel_ms * 1e-3) / 1e9

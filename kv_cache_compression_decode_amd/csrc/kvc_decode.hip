@@ -194,7 +194,7 @@ struct AnchorTop {
 // that no product can wrap and a valid code never selects them.  Returns the
 // value to store (binary16 bits, or the symbol).
 template <bool kSymbols, bool kAnchor, uint32_t kSteps>
-__device__ inline uint32_t step(Stream &x, const AnchorTop &at) {
+__device__ inline uint32_t step(Stream &x, const AnchorTop &at, uint64_t &lost_anchor) {
   // the next four stream bytes, most significant first
   const lds_u32 *rd =
       (const lds_u32 *)(uintptr_t)(lds_addr(x.ring) + (dword_of(x.nrpos) << 2));
@@ -219,22 +219,22 @@ __device__ inline uint32_t step(Stream &x, const AnchorTop &at) {
   const uint32_t cn = lds_read_u16(a + kRowBytes);
   SEARCH_BARRIER();
   int32_t xq;  // 128 (symbol - M) for deltas, 128 symbol for anchors
-  // A code at or past r * 2^15 has no symbol.  For a delta the search then
-  // ends on a staged pad (2^15, as is cum[A]), so the interval is empty and
-  // the range becomes 0; an anchor's search cannot pass symbol 255, so the
-  // range is cleared explicitly.  A zero range stays zero (r = 0 from then
-  // on) and is reported at the end of the stream.
-  bool lost = false;
   if constexpr (kAnchor) {
     xq = (int32_t)(a - at.base);
-    lost = x.code >= (r << kPrec);
   } else {
     xq = (int32_t)(a - x.dbaseM);
   }
   // 24-bit multiplies: r < 2^17 and staged cumulative counts <= 2^15
   x.code -= __umul24(r, cs);
-  uint32_t range = __umul24(r, cn - cs);
-  if constexpr (kAnchor) range = lost ? 0u : range;
+  const uint32_t range = __umul24(r, cn - cs);
+  // A code at or past r * 2^15 has no symbol.  For a delta the search then
+  // ends on a staged pad (2^15, as is cum[A]), so the interval is empty and
+  // the range becomes 0; a zero range stays zero (r = 0 from then on) and is
+  // reported at the end of the stream.  An anchor's search cannot pass symbol
+  // 255, and then leaves code - r cum[255] >= r f[255], the new range, which a
+  // valid code never does (code < r cum[s + 1]): the wave keeps a mask of the
+  // lanes where that happened, reported at the end of the stream.
+  if constexpr (kAnchor) lost_anchor |= __builtin_amdgcn_ballot_w64(x.code >= range);
   // whole bytes to shift in: 0, 1 or 2 (range >= 2^9 for a valid stream)
   const uint32_t sh = ffbh(range) & 24u;
   x.range = range << sh;
@@ -285,7 +285,7 @@ __device__ inline gbyte *uniform_ptr(gbyte *p) {
 // The `count` delta tokens of one group.
 template <bool kSymbols, uint32_t kSteps>
 __device__ inline void delta_run(Stream &s, const AnchorTop &at, Source &src, gbyte *&ob, uint64_t ld,
-                                 uint32_t &loff, uint32_t count) {
+                                 uint32_t &loff, uint32_t count, uint64_t &lost_anchor) {
   // The anchor's refill leaves at least 8 bytes in every ring and a token
   // takes at most 2 (range >= 2^24 after renormalization, a symbol's
   // frequency >= 1), so the group's first three deltas cannot run low.  A
@@ -294,26 +294,44 @@ __device__ inline void delta_run(Stream &s, const AnchorTop &at, Source &src, gb
   const uint32_t safe = count < 3 ? count : 3;
   uint32_t i = 0;
   for (; i < safe; ++i) {
-    put<kSymbols>(ob, loff, step<kSymbols, false, kSteps>(s, at));
+    put<kSymbols>(ob, loff, step<kSymbols, false, kSteps>(s, at, lost_anchor));
     ob += ld;
   }
   for (; i < count; ++i) {
     ensure(s, src);
-    put<kSymbols>(ob, loff, step<kSymbols, false, kSteps>(s, at));
+    put<kSymbols>(ob, loff, step<kSymbols, false, kSteps>(s, at, lost_anchor));
     ob += ld;
   }
 }
 
-// The search depth is the chunk's delta bits in this layer third.
+// Every token of a lane's stream, in groups of an anchor and up to G - 1
+// deltas.  The search depth of the deltas is fixed for the whole stream (the
+// chunk's delta bits in this layer third), so the group loop is instantiated
+// per depth and chosen once per stream.
+template <bool kSymbols, uint32_t kSteps>
+__device__ inline void stream_run(Stream &s, const AnchorTop &at, Source &src, gbyte *ob, uint64_t ld,
+                                  uint32_t &loff, uint32_t n, uint32_t G, uint64_t &lost_anchor) {
+  for (uint32_t j = 0; j < n;) {
+    // after a refill at least 8 bytes are buffered: no check for the anchor
+    refill(s, src);
+    put<kSymbols>(ob, loff, step<kSymbols, true, 8>(s, at, lost_anchor));
+    ob += ld;
+    const uint32_t jend = j + G < n ? j + G : n;
+    delta_run<kSymbols, kSteps>(s, at, src, ob, ld, loff, jend - j - 1, lost_anchor);
+    j = jend;
+  }
+}
+
 template <bool kSymbols>
-__device__ inline void delta_dispatch(uint32_t steps, Stream &s, const AnchorTop &at, Source &src,
-                                      gbyte *&ob, uint64_t ld, uint32_t &loff, uint32_t count) {
+__device__ inline void stream_dispatch(uint32_t steps, Stream &s, const AnchorTop &at, Source &src,
+                                       gbyte *ob, uint64_t ld, uint32_t &loff, uint32_t n, uint32_t G,
+                                       uint64_t &lost_anchor) {
   switch (steps) {
-    case 2: delta_run<kSymbols, 2>(s, at, src, ob, ld, loff, count); break;
-    case 3: delta_run<kSymbols, 3>(s, at, src, ob, ld, loff, count); break;
-    case 4: delta_run<kSymbols, 4>(s, at, src, ob, ld, loff, count); break;
-    case 5: delta_run<kSymbols, 5>(s, at, src, ob, ld, loff, count); break;
-    default: delta_run<kSymbols, 6>(s, at, src, ob, ld, loff, count); break;
+    case 2: stream_run<kSymbols, 2>(s, at, src, ob, ld, loff, n, G, lost_anchor); break;
+    case 3: stream_run<kSymbols, 3>(s, at, src, ob, ld, loff, n, G, lost_anchor); break;
+    case 4: stream_run<kSymbols, 4>(s, at, src, ob, ld, loff, n, G, lost_anchor); break;
+    case 5: stream_run<kSymbols, 5>(s, at, src, ob, ld, loff, n, G, lost_anchor); break;
+    default: stream_run<kSymbols, 6>(s, at, src, ob, ld, loff, n, G, lost_anchor); break;
   }
 }
 
@@ -465,21 +483,12 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
     s.nrpos = 0u - 32;
     s.range = 0xFFFFFFFFu;
 
-    // groups of an anchor and up to G - 1 deltas
-    const uint32_t n = c.n_tokens;
-    for (uint32_t j = 0; j < n;) {
-      // after a refill at least 8 bytes are buffered: no check for the anchor
-      refill(s, src);
-      put<kSymbols>(ob, loff, step<kSymbols, true, 8>(s, at));
-      ob += ld;
-      const uint32_t jend = j + d.G < n ? j + d.G : n;
-      delta_dispatch<kSymbols>(b, s, at, src, ob, ld, loff, jend - j - 1);
-      j = jend;
-    }
+    uint64_t lost_anchor = 0;
+    stream_dispatch<kSymbols>(b, s, at, src, ob, ld, loff, c.n_tokens, d.G, lost_anchor);
     // a valid stream ends exactly at its last byte, with every block asked for
     const uint32_t nbytes =
         reinterpret_cast<const uint32_t *>(ci[k].records + (uint64_t)m * kRecBytes)[3];
-    if (s.range == 0 || s.nrpos != 0u - 8 * nbytes || s.rem != 0)
+    if (s.range == 0 || s.nrpos != 0u - 8 * nbytes || s.rem != 0 || ((lost_anchor >> lane) & 1))
       set_status(status, KVC_ERR_CORRUPT_STREAM);
   }
 }
