@@ -206,6 +206,29 @@ def test_corrupt_containers_are_reported(mixed):
     assert e.value.code == kvc.ERR_CORRUPT_STREAM
 
 
+def test_code_past_the_first_anchor_model_is_reported(mixed):
+    """A stream whose first four bytes are 0xFF starts with code 2^32 - 1,
+    which is at or past r * 2^15 for the initial range: its first symbol, an
+    anchor, has no interval.  The oracle reports it, and so must the decoder,
+    even though the anchor's search itself ends on a valid symbol."""
+    k, lane = 1, 37
+    cont = [c.copy() for c in mixed.ocont]
+    order, _ = oracle.unit_order(mixed.od, mixed.otb, cont[k], 0)
+    slot = int(np.nonzero(order == (lane << 16))[0][0])  # the lane's block 0
+    pay = 64 + 16 * mixed.od.n_streams
+    cont[k][pay + 8 * slot:pay + 8 * slot + 4] = 0xFF
+    with pytest.raises(oracle.OracleError):
+        oracle.decode(mixed.od, mixed.otb, cont, mixed.levels, mixed.cfg.n_tokens)
+    sizes = [len(c) for c in cont]
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    enc = kvc.Encoded(torch.from_numpy(np.concatenate(cont)).to(DEV), [int(x) for x in offs],
+                      list(mixed.levels),
+                      [min(1500, mixed.cfg.n_tokens - 1500 * j) for j in range(len(sizes))], 1500)
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.decode(mixed.d, mixed.tables, kvc.chunk_refs(enc), mixed.cfg.n_tokens)
+    assert e.value.code == kvc.ERR_CORRUPT_STREAM
+
+
 def test_damaged_tables_are_reported_by_encode(mixed):
     """A model whose every frequency is 0 (all cumulative counts 0, so no
     symbol has an interval): the statistics pass reports the stream, and
