@@ -59,7 +59,8 @@ constexpr uint32_t kMaxWaves = kDecodeMaxWaves;  // waves per workgroup (host pi
 constexpr uint32_t kARows = 258;    // staged anchor model rows: cum[0..256] + pad
 constexpr uint32_t kDRows = 66;     // staged delta model rows: cum[0..63] + 2 pads
 constexpr uint32_t kRowBytes = 2 * kWave;  // one u16 entry for each of the 64 lanes
-constexpr uint32_t kRing = 5;       // dwords per lane ring: 16 bytes + mirror of bytes 0..3
+constexpr uint32_t kRing = 7;       // dwords per lane ring: 2 spare, 16 bytes, mirror of bytes 0..3
+constexpr uint32_t kRingLead = 2;   // spare dwords before the ring's byte 0
 constexpr uint32_t kXcds = 8;
 
 // Explicit address spaces for the LDS tables / rings and the output, so that
@@ -114,7 +115,8 @@ struct Source {
 // bytes from p on are then the little-endian dword at ring byte -p mod 16,
 // most significant first, and that dword lies inside the two aligned dwords
 // at (-p mod 16) & 12: one paired LDS read and one funnel shift whose shift
-// count is the bit position itself.
+// count is the bit position itself.  Two spare dwords precede the ring, so
+// that both halves are written by the same three stores (below).
 struct Stream {
   lds_u32 *ring;        // this lane's ring in LDS (20 bytes)
   uint32_t code, range;
@@ -124,7 +126,10 @@ struct Stream {
   u32x2 held;           // the stream's next 8-byte block, loaded ahead (one
                         // aligned register pair, the load's own destination)
   uint32_t rem;         // the stream's blocks the lane has not asked for
-  uint32_t hpos;        // payload block number of the held block
+  uint32_t hoff;        // byte offset of the held block in the container
+  uint32_t wbase;       // LDS address the next block is written from: ring
+                        // byte 0, or 8 bytes before it (alternating)
+  uint32_t wsum;        // the sum of those two addresses
   int32_t M;
   uint32_t dbase;       // LDS byte address of this lane's delta row 0
   uint32_t dbaseM;      // dbase + M rows: (addr - dbaseM) >> 7 is q = s - M
@@ -134,13 +139,17 @@ struct Stream {
 
   // The held block, byte-reversed, into the free half of the ring: its
   // first stream byte is a multiple of 16 (dwords 4, 3 and the mirror 0) or
-  // 8 past one (dwords 2, 1).
+  // 8 past one (dwords 2, 1).  Written from w = ring byte 0 or 8 bytes before
+  // it, the same three stores do both: dwords w+0 and w+4 take the block's
+  // first four bytes (the mirror and dword 4, or a spare dword and dword 2),
+  // dword w+3 the other four (dword 3, or dword 1).
   __device__ inline void put_block() {
-    const uint32_t h = ((16u - nwlim) >> 5) & 2;
+    lds_u32 *w = (lds_u32 *)(uintptr_t)wbase;
     const uint32_t lo = __builtin_bswap32(held[0]);
-    ring[4 - h] = lo;
-    ring[3 - h] = __builtin_bswap32(held[1]);
-    if (h == 0) ring[0] = lo;
+    w[0] = lo;
+    w[4] = lo;
+    w[3] = __builtin_bswap32(held[1]);
+    wbase = wsum - wbase;
     nwlim -= 64;
   }
 };
@@ -162,10 +171,10 @@ __device__ inline void advance(Stream &s, Source &src, bool need) {
   const bool req = need && s.rem != 0;
   const uint64_t mask = __builtin_amdgcn_ballot_w64(req);
   if (need) s.put_block();
-  const uint32_t pos = src.cnt + lanes_below(mask);
-  s.hpos = need ? pos : s.hpos;
-  s.held = __builtin_amdgcn_raw_buffer_load_b64(src.rsrc, src.ubase + s.hpos * kBlock, 0, 0);
-  s.rem -= req ? 1u : 0u;
+  const uint32_t off = src.ubase + (src.cnt + lanes_below(mask)) * kBlock;
+  s.hoff = need ? off : s.hoff;
+  s.held = __builtin_amdgcn_raw_buffer_load_b64(src.rsrc, s.hoff, 0, 0);
+  s.rem = req ? s.rem - 1u : s.rem;
   src.cnt += (uint32_t)__builtin_popcountll(mask);
 }
 // At a group's anchor: a ring with at most 8 bytes left takes its block.
@@ -418,7 +427,7 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
   const uint32_t m = m0 + lane;
   // this wave's ring (one register holds its address, so that a ring read
   // is one bit-field extract and one shift-add)
-  uint32_t ring_addr = lds_addr(sR + (wave * kWave + lane) * kRing);
+  uint32_t ring_addr = lds_addr(sR + (wave * kWave + lane) * kRing + kRingLead);
   __asm__ volatile("" : "+v"(ring_addr));
   uint32_t loff = lane * esz;
   __asm__ volatile("" : "+v"(loff));
@@ -467,7 +476,7 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
       const auto v = __builtin_amdgcn_raw_buffer_load_b64(src.rsrc, src.ubase + pos * kBlock, 0, 0);
       blk[q][0] = v[0];
       blk[q][1] = v[1];
-      if (q == 2) s.hpos = pos;
+      if (q == 2) s.hoff = src.ubase + pos * kBlock;
       src.cnt += (uint32_t)__builtin_popcountll(mask);
     }
     s.rem = nblk < 3 ? 0u : nblk - 3;
@@ -479,6 +488,8 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
     s.held[0] = blk[2][0];
     s.held[1] = blk[2][1];
     s.nwlim = 0u - (128 - 16);
+    s.wbase = ring_addr;  // block 2 goes to dwords 4, 3 and the mirror
+    s.wsum = 2u * ring_addr - 8u;
     s.code = bswap32(blk[0][0]);
     s.nrpos = 0u - 32;
     s.range = 0xFFFFFFFFu;
