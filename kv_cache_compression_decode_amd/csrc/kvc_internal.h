@@ -201,27 +201,43 @@ struct Column {
   const uint8_t *base;  // wave-uniform
   uint64_t ld2;         // bytes from one token to the next
   uint32_t loff;        // this lane's byte offset
-  __device__ inline float at(uint32_t j) {
+  // the lane's value in the token row that starts at the wave-uniform `row`
+  typedef __attribute__((address_space(1))) const uint8_t grow;
+  __device__ inline float in_row(grow *row) {
     __asm__("" : "+v"(loff));
-    return h2f(*reinterpret_cast<const uint16_t *>(base + (uint64_t)j * ld2 + loff));
+    return h2f(*reinterpret_cast<__attribute__((address_space(1))) const uint16_t *>(row + loff));
   }
+  __device__ inline float at(uint32_t j) { return in_row((grow *)(base + (uint64_t)j * ld2)); }
 };
 
 // Visits the tokens first, first + step, ... (< n) of a lane's column in
 // order, calling f(value).  The values are loaded kBatch at a time, so a
-// wave waits for memory once per batch rather than once per token.
+// wave waits for memory once per batch rather than once per token.  The row
+// address is a wave-uniform pointer advanced by one stride per token (one
+// 64-bit scalar add) rather than recomputed from the token index (a 64-bit
+// scalar multiply and add per load).
 template <uint32_t kBatch, class F>
 __device__ inline void for_each_token(Column &x, uint32_t first, uint32_t step, uint32_t n,
                                       F &&f) {
   uint32_t j = first;
+  const uint64_t stride = (uint64_t)step * x.ld2;
+  Column::grow *row = (Column::grow *)(x.base + (uint64_t)first * x.ld2);
   for (; j + (kBatch - 1) * step < n; j += kBatch * step) {
     float v[kBatch];
 #pragma unroll
-    for (uint32_t u = 0; u < kBatch; ++u) v[u] = x.at(j + u * step);
+    for (uint32_t u = 0; u < kBatch; ++u) {
+      v[u] = x.in_row(row);
+      row += stride;
+      // one running pointer: no per-token offsets precomputed in registers
+      __asm__("" : "+s"(row));
+    }
 #pragma unroll
     for (uint32_t u = 0; u < kBatch; ++u) f(v[u]);
   }
-  for (; j < n; j += step) f(x.at(j));
+  for (; j < n; j += step) {
+    f(x.in_row(row));
+    row += stride;
+  }
 }
 constexpr uint32_t kTokenBatch = 16;
 
