@@ -259,10 +259,9 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_stats(
     uint32_t range = 0xFFFFFFFFu;
     uint32_t shifts = 0;
     float ahat = 0.0f;
-    uint32_t g = 0;
-    for_each_token<kTokenBatch>(x, 0, 1, n, [&](float v) {
+    for_each_group_token<2, kTokenBatch>(x, n, d.G, [&](float v, auto anchor) {
       uint32_t f;
-      if (g == 0) {
+      if constexpr (decltype(anchor)::value) {
         const uint32_t qa = quant_anchor(v, lo, sa, inv_sa);
         ahat = __builtin_fmaf((float)qa, sa, lo);
         f = (uint32_t)ta[qa + 1] - ta[qa];
@@ -270,7 +269,6 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_stats(
         const uint32_t s = (uint32_t)(quant_delta(v - ahat, dl, inv_dl, M) + M);
         f = (uint32_t)td[s + 1] - td[s];
       }
-      g = g + 1 == d.G ? 0 : g + 1;
       // the encoder's update (24-bit multiply: r < 2^17, f <= 2^15)
       range = __umul24(range >> kPrec, f);
       // whole bytes to shift: 0, 1 or 2 (range >= 2^9 with f >= 1)

@@ -13,6 +13,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include "kvc.h"
@@ -241,6 +242,47 @@ __device__ inline void for_each_token(Column &x, uint32_t first, uint32_t step, 
 }
 constexpr uint32_t kTokenBatch = 16;
 
+// Visits every token of a lane's column in order, calling f(value, tag) with
+// tag std::true_type for a group's anchor and std::false_type for the other
+// tokens.  With groups of the pages' size (10 tokens) whole groups are loaded
+// kGroups at a time and visited unrolled, so the anchor/delta choice and the
+// group position cost nothing per token; other group sizes and a partial
+// last group go through for_each_token with a running group position.
+constexpr uint32_t kGroup10 = 10;
+
+template <uint32_t kGroups, uint32_t kBatch, class F>
+__device__ inline void for_each_group_token(Column &x, uint32_t n, uint32_t G, F &&f) {
+  uint32_t j = 0;
+  if (G == kGroup10) {
+    Column::grow *row = (Column::grow *)x.base;
+    for (; j + kGroups * kGroup10 <= n; j += kGroups * kGroup10) {
+      float v[kGroups * kGroup10];
+#pragma unroll
+      for (uint32_t u = 0; u < kGroups * kGroup10; ++u) {
+        v[u] = x.in_row(row);
+        row += x.ld2;
+        __asm__("" : "+s"(row));
+      }
+#pragma unroll
+      for (uint32_t gi = 0; gi < kGroups; ++gi) {
+        f(v[gi * kGroup10], std::true_type{});
+#pragma unroll
+        for (uint32_t u = 1; u < kGroup10; ++u) f(v[gi * kGroup10 + u], std::false_type{});
+      }
+    }
+  }
+  // j is a multiple of G here
+  uint32_t g = 0;
+  for_each_token<kBatch>(x, j, 1, n, [&](float v) {
+    if (g == 0) {
+      f(v, std::true_type{});
+    } else {
+      f(v, std::false_type{});
+    }
+    g = g + 1 == G ? 0 : g + 1;
+  });
+}
+
 // Stream statistics: lo, sa (anchor scale) and maxabs of the closed-loop
 // deltas.  Returns false if a value is not finite.
 __device__ inline bool stream_stats(Column &x, uint32_t n, uint32_t G, float &lo_out,
@@ -256,16 +298,14 @@ __device__ inline bool stream_stats(Column &x, uint32_t n, uint32_t G, float &lo
   bool finite = true;
   float maxabs = 0.0f;
   float ahat = 0.0f;
-  uint32_t g = 0;  // position in the group (0: the anchor)
-  for_each_token<kTokenBatch>(x, 0, 1, n, [&](float v) {
+  for_each_group_token<2, kTokenBatch>(x, n, G, [&](float v, auto anchor) {
     finite = finite && is_finite(v);
-    if (g == 0) {
+    if constexpr (decltype(anchor)::value) {
       ahat = __builtin_fmaf((float)quant_anchor(v, lo, sa, inv_sa), sa, lo);
     } else {
       const float a = __builtin_fabsf(v - ahat);
       if (a > maxabs) maxabs = a;
     }
-    g = g + 1 == G ? 0 : g + 1;
   });
   lo_out = lo;
   sa_out = sa;
