@@ -247,6 +247,7 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_stats(
     const uint16_t *td = reinterpret_cast<const uint16_t *>(sD + (lslot * kWave + lane) * kED);
     const uint32_t b = d.bits[level][third];
     const int32_t M = (1 << (b - 1)) - 1;
+    const uint16_t *tdM = td + M;  // entry q of it is the cumulative count of q + M
     Column x{reinterpret_cast<const uint8_t *>(kv + ((uint64_t)row * T + c.first_token) * ld + c0),
              2 * ld, 2 * lane};
     const uint32_t n = c.n_tokens;
@@ -266,8 +267,8 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_stats(
         ahat = __builtin_fmaf((float)qa, sa, lo);
         f = (uint32_t)ta[qa + 1] - ta[qa];
       } else {
-        const uint32_t s = (uint32_t)(quant_delta(v - ahat, dl, inv_dl, M) + M);
-        f = (uint32_t)td[s + 1] - td[s];
+        const int32_t q = quant_delta(v - ahat, dl, inv_dl, M);
+        f = (uint32_t)tdM[q + 1] - tdM[q];
       }
       // the encoder's update (24-bit multiply: r < 2^17, f <= 2^15)
       range = __umul24(range >> kPrec, f);
@@ -345,6 +346,7 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
     const uint16_t *td = reinterpret_cast<const uint16_t *>(sD + (lslot * kWave + lane) * kED);
     const uint32_t b = d.bits[level][third];
     const int32_t M = (1 << (b - 1)) - 1;
+    const uint16_t *tdM = td + M;  // entry q of it is the cumulative count of q + M
 
     const uint32_t *rin =
         reinterpret_cast<const uint32_t *>(records + ((uint64_t)k * S + m) * kRecBytes);
@@ -426,9 +428,9 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
         cs = ta[qa];
         f = (uint32_t)ta[qa + 1] - cs;
       } else {
-        const uint32_t s = (uint32_t)(quant_delta(v - ahat, dl, inv_dl, M) + M);
-        cs = td[s];
-        f = (uint32_t)td[s + 1] - cs;
+        const int32_t q = quant_delta(v - ahat, dl, inv_dl, M);
+        cs = tdM[q];
+        f = (uint32_t)tdM[q + 1] - cs;
       }
       g = g + 1 == d.G ? 0 : g + 1;
       // (damaged tables were reported by the statistics pass, which ran the

@@ -162,8 +162,9 @@ __device__ inline bool is_finite(float v) { return __builtin_isfinite(v); }
 __device__ inline float rint_quot(float num, float den, float inv) {
   const float y = num * inv;
   float r = __builtin_rintf(y);
-  // y - r and |y - r| - 0.5 are exact near the threshold
-  const bool near_half = __builtin_fabsf(__builtin_fabsf(y - r) - 0.5f) <= 0x1p-13f;
+  // y - r is exact and at most 1/2 in magnitude: within 2^-13 of a
+  // half-integer means |y - r| >= 1/2 - 2^-13 (a binary32 constant)
+  const bool near_half = __builtin_fabsf(y - r) >= 0.5f - 0x1p-13f;
   if (__builtin_amdgcn_ballot_w64(near_half) != 0) {
     const float e = __builtin_rintf(num / den);
     r = near_half ? e : r;
