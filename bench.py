@@ -246,7 +246,8 @@ def measure_controller(kvc, d, tables, kv_dev, cfg, n_traces: int = 500, slo_s: 
            "level_bytes_GB": [round(float(x) / 1e9, 4) for x in sizes.sum(axis=0)],
            "scenarios": {}}
     plan_s, plans = 0.0, 0
-    for ref in (0, 1):
+    # the second link needs a second level to be just enough for
+    for ref in range(min(2, d.n_levels)):
         median = float(sizes[:, ref].sum()) / slo_s
         viol = np.zeros(d.n_levels + 1)
         share = np.zeros(d.n_levels)
@@ -285,6 +286,7 @@ def measure_multi(kvc, d, tables, kv_dev, cfg, n_req: int = 8, req_tokens: int =
     import torch
 
     dev = tables.device
+    n_req = min(n_req, cfg.n_tokens // req_tokens)  # whole requests of this context
     encs, outs_a, outs_b = [], [], []
     for r in range(n_req):
         kv_r = kv_dev[:, :, r * req_tokens:(r + 1) * req_tokens].contiguous()
