@@ -55,7 +55,7 @@ typedef enum {
   KVC_ERR_NONFINITE = -5,       /* inf / NaN in the KV to encode or profile */
   KVC_ERR_CAPACITY = -6,        /* workspace or output buffer too small */
   KVC_ERR_HIP = -7,             /* a HIP runtime call failed */
-  KVC_ERR_UNIMPLEMENTED = -8
+  KVC_ERR_UNIMPLEMENTED = -8     /* no entry point returns it */
 } kvc_status;
 
 /* Codec descriptor: the page's constants (chunks of ~1.5K tokens, groups of
@@ -161,12 +161,12 @@ uint64_t kvc_encode_ws_bytes(const kvc_codec_desc *d, uint32_t T);
  * of one (layer, K/V) row, the streams' 8-byte blocks in the order in which
  * the decoder's 64 lanes ask for them while decoding (so that one wave's
  * requests are consecutive bytes); a stream's block padding is zero.
+ * Every valid input is encoded: a range-coder carry may run back through any
+ * number of 0xFF bytes already produced (the few (chunk, unit)s where that
+ * happens are coded a second time, by a slower kernel).
  * Device errors: KVC_ERR_NONFINITE, KVC_ERR_CAPACITY (out_cap too small; the
- * offsets are still written, `out` is not), KVC_ERR_UNIMPLEMENTED (a
- * range-coder carry would have to pass every byte the encoder still holds
- * back, at least 6, all 0xFF; or the decoder would ask for more than 8 of
- * one stream's blocks before the encoder has written them; neither occurs
- * short of such a run of 0xFF bytes).
+ * offsets are still written, `out` is not), KVC_ERR_CORRUPT_STREAM (damaged
+ * tables).
  */
 kvc_status kvc_encode(const kvc_codec_desc *d, const void *tables, const uint16_t *kv_fp16,
                       uint32_t T, const uint8_t *chunk_levels, uint8_t *out, uint64_t out_cap,

@@ -25,8 +25,11 @@ hipError_t launch_encode(const Desc &d, const uint8_t *tables, const uint16_t *k
                          const DecodeGroup *groups, uint32_t n_groups, uint32_t levels,
                          uint32_t waves, uint8_t *records, uint64_t *row_sums, uint32_t *flags,
                          uint32_t *offsets, uint8_t *valid, uint64_t *payload,
-                         uint64_t *chunk_off_ws, uint32_t *fits, uint8_t *out, uint64_t out_cap,
-                         uint64_t *chunk_off_out, int32_t *status, hipStream_t stream);
+                         uint64_t *chunk_off_ws, uint32_t *fits, uint32_t *redo,
+                         uint8_t *redo_scratch, uint32_t redo_blocks, uint8_t *out,
+                         uint64_t out_cap, uint64_t *chunk_off_out, int32_t *status,
+                         hipStream_t stream);
+uint32_t encode_redo_lane_bytes(uint32_t chunk);
 size_t encode_lds_bytes(uint32_t levels);
 size_t encode_emit_lds_bytes(uint32_t levels, uint32_t waves);
 hipError_t launch_profile(const Desc &d, const uint16_t *kv, uint32_t T, uint8_t *tables,
@@ -67,9 +70,17 @@ Desc to_desc(const kvc_codec_desc *d) {
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Workgroups (one wave each) of the encoder's slow path, and the scratch
+// they share: at most 8, fewer when a chunk's scratch is large.
+uint32_t redo_blocks(const Desc &d) {
+  const uint64_t per = (uint64_t)kWave * encode_redo_lane_bytes(d.chunk);
+  return (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(8, (16ull << 20) / per));
+}
+
 // Workspace layout shared by decode and encode (encode adds its tail).
 struct WsLayout {
-  uint64_t chunks, groups, rows, hdr, valid, payload, offsets, records, chunk_off, fits, total;
+  uint64_t chunks, groups, rows, hdr, valid, payload, offsets, records, chunk_off, fits, redo,
+      redo_scratch, total;
 };
 
 WsLayout ws_layout(const Desc &d, uint32_t K, bool encode) {
@@ -83,12 +94,17 @@ WsLayout ws_layout(const Desc &d, uint32_t K, bool encode) {
   w.payload = align256(w.valid + K);
   w.offsets = align256(w.payload + (uint64_t)K * 8);
   uint64_t end = w.offsets + (uint64_t)K * S * 4;
-  w.records = w.chunk_off = w.fits = 0;
+  w.records = w.chunk_off = w.fits = w.redo = w.redo_scratch = 0;
   if (encode) {
+    // the slow path's list: a count, then (chunk, unit) pairs, at most one
+    // per chunk and unit
+    const uint64_t units = 2ull * d.L * ((d.C + kWave - 1) / kWave);
     w.records = align256(end);
     w.chunk_off = align256(w.records + (uint64_t)K * S * kRecBytes);
     w.fits = align256(w.chunk_off + (uint64_t)(K + 1) * 8);
-    end = w.fits + 4;
+    w.redo = align256(w.fits + 4);
+    w.redo_scratch = align256(w.redo + 4 + 8 * (uint64_t)K * units);
+    end = w.redo_scratch + (uint64_t)redo_blocks(d) * kWave * encode_redo_lane_bytes(d.chunk);
   }
   w.total = align256(end);
   return w;
@@ -431,8 +447,9 @@ kvc_status kvc_encode(const kvc_codec_desc *dd, const void *tables, const uint16
                     reinterpret_cast<uint32_t *>(base + w.offsets), base + w.valid,
                     reinterpret_cast<uint64_t *>(base + w.payload),
                     reinterpret_cast<uint64_t *>(base + w.chunk_off),
-                    reinterpret_cast<uint32_t *>(base + w.fits), out, out_cap, chunk_offsets_out,
-                    dev_status, stream);
+                    reinterpret_cast<uint32_t *>(base + w.fits),
+                    reinterpret_cast<uint32_t *>(base + w.redo), base + w.redo_scratch,
+                    redo_blocks(d), out, out_cap, chunk_offsets_out, dev_status, stream);
   return hip_status(e);
 }
 

@@ -17,7 +17,14 @@
 //   k_encode_emit  : quantize and range-encode into the final position; the
 //                    output bytes wait in registers (6 to 11 of them) until
 //                    a carry can no longer reach them, so a carry is one
-//                    add-with-carry chain and no lane branches per byte;
+//                    add-with-carry chain and no lane branches per byte; a
+//                    (chunk, unit) where a carry had to pass every held byte
+//                    (a run of 6 or more 0xFF bytes) or a lane's block queue
+//                    ran full is listed for the next kernel;
+//   k_encode_redo  : the listed (chunk, unit)s again, one stream per lane:
+//                    each stream's bytes into linear scratch with the carry
+//                    added into them, then the reading rule replayed for the
+//                    unit to put every block in its place;
 //   k_encode_header: the 64-byte headers.
 #include "kvc_internal.h"
 
@@ -289,8 +296,10 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_stats(
 __global__ void k_encode_layout(Desc d, uint32_t n_chunks, const uint64_t *__restrict__ payload,
                                 uint64_t *__restrict__ chunk_off_ws,
                                 uint64_t *__restrict__ chunk_off_out, uint64_t out_cap,
-                                uint32_t *__restrict__ fits, int32_t *status) {
+                                uint32_t *__restrict__ fits, uint32_t *__restrict__ redo,
+                                int32_t *status) {
   if (threadIdx.x != 0) return;
+  redo[0] = 0;
   const uint64_t fixed = (uint64_t)kHdrBytes + (uint64_t)kRecBytes * n_streams(d);
   uint64_t acc = 0;
   for (uint32_t k = 0; k < n_chunks; ++k) {
@@ -311,7 +320,8 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
     uint32_t n_groups, uint32_t n_units, const uint8_t *__restrict__ tables,
     const uint16_t *__restrict__ kv, uint32_t T, const uint8_t *__restrict__ records,
     const uint32_t *__restrict__ offsets, const uint64_t *__restrict__ chunk_off,
-    const uint32_t *__restrict__ fits, uint8_t *__restrict__ out, int32_t *status) {
+    const uint32_t *__restrict__ fits, uint8_t *__restrict__ out, uint32_t *__restrict__ redo,
+    int32_t *status) {
   if (*fits == 0) return;
   const EncodeBlock eb = encode_block(n_groups);
   if (eb.unit >= n_units) return;
@@ -475,14 +485,163 @@ __global__ __launch_bounds__(kEncodeMaxWaves *kWave) void k_encode_emit(
         sink.written += 4u;
       }
     }
-    if (sink.window) {
-      // the decoder more blocks ahead than the queue holds, or a carry
-      // through a run of 6 or more 0xFF bytes
-      set_status(status, KVC_ERR_UNIMPLEMENTED);
-    } else if (sink.overflow || R != nbytes || sink.written != pad8(nbytes) || q != nblk ||
-               sink.head != sink.tail) {
+    // A lane whose queue ran full (the decoder more blocks ahead than it
+    // holds) or whose carry passed every held byte has written some of its
+    // bytes wrong or not at all, into blocks of this unit only; the unit is
+    // coded again by k_encode_redo, which rewrites all of its blocks.
+    if (!sink.window && (sink.overflow || R != nbytes || sink.written != pad8(nbytes) ||
+                         q != nblk || sink.head != sink.tail))
       set_status(status, KVC_ERR_CORRUPT_STREAM);
+    if (__builtin_amdgcn_ballot_w64(sink.window) != 0 && lane == 0) {
+      const uint32_t e = atomicAdd(redo, 1u);
+      redo[1 + 2 * e] = k;
+      redo[2 + 2 * e] = eb.unit;
     }
+  }
+}
+
+// The (chunk, unit)s emit listed, one workgroup (one wave) at a time, each
+// lane coding one stream of the unit.  First every stream's bytes go into
+// the lane's linear scratch, with a carry added into the bytes already there
+// (the plain form of the coder: nothing is held back, so no run of 0xFF
+// bytes is too long), and the bytes each token shifts out are recorded; then
+// the reading rule is replayed over those counts, exactly as emit runs it,
+// and each block asked for is copied from the scratch to its place in the
+// unit's payload (a stream's padding bytes are zero).  Scratch per lane:
+// pad8(4 + 2 chunk) bytes, then one byte per token.
+__global__ __launch_bounds__(kWave) void k_encode_redo(
+    Desc d, const ChunkInfo *__restrict__ ci, const uint8_t *__restrict__ tables,
+    const uint16_t *__restrict__ kv, uint32_t T, const uint8_t *__restrict__ records,
+    const uint32_t *__restrict__ offsets, const uint64_t *__restrict__ chunk_off,
+    const uint32_t *__restrict__ fits, const uint32_t *__restrict__ redo,
+    uint8_t *__restrict__ scratch, uint32_t lane_stride, uint8_t *__restrict__ out,
+    int32_t *status) {
+  if (*fits == 0) return;
+  const uint32_t n_redo = redo[0];
+  const uint32_t lane = threadIdx.x;
+  const uint32_t ncb = (d.C + kWave - 1) / kWave;
+  const uint32_t S = n_streams(d);
+  const uint32_t cap = (uint32_t)pad8(4u + 2u * d.chunk);
+  uint8_t *buf = scratch + ((uint64_t)blockIdx.x * kWave + lane) * lane_stride;
+  uint8_t *shifts = buf + cap;
+  const uint16_t *tA = reinterpret_cast<const uint16_t *>(tables + kTablesHdr);
+  const uint16_t *tD =
+      reinterpret_cast<const uint16_t *>(tables + kTablesHdr + (uint64_t)S * kAnchorStride * 2);
+  for (uint32_t e = blockIdx.x; e < n_redo; e += gridDim.x) {
+    const uint32_t k = redo[1 + 2 * e], unit = redo[2 + 2 * e];
+    const uint32_t row = unit / ncb, c0 = (unit % ncb) * kWave;
+    const uint32_t nv = d.C - c0 < kWave ? d.C - c0 : kWave;
+    if (lane >= nv) continue;
+    const uint32_t m = row * d.C + c0 + lane;
+    const ChunkInfo c = ci[k];
+    const uint32_t n = c.n_tokens;
+    const uint32_t b = d.bits[c.level][third_of(row >> 1, d.L)];
+    const int32_t M = (1 << (b - 1)) - 1;
+    const uint16_t *ta = tA + (uint64_t)m * kAnchorStride;
+    const uint16_t *tdM = tD + ((uint64_t)c.level * S + m) * kDeltaStride + M;
+    const uint32_t *rin =
+        reinterpret_cast<const uint32_t *>(records + ((uint64_t)k * S + m) * kRecBytes);
+    const float lo = __builtin_bit_cast(float, rin[0]);
+    const float sa = __builtin_bit_cast(float, rin[1]);
+    const float dl = __builtin_bit_cast(float, rin[2]);
+    const uint32_t nbytes = rin[3];
+    const float inv_sa = recip_or_zero(sa), inv_dl = recip_or_zero(dl);
+    const uint16_t *x = kv + ((uint64_t)row * T + c.first_token) * d.C + c0 + lane;
+
+    // the stream's bytes, carries included
+    uint64_t low = 0;
+    uint32_t range = 0xFFFFFFFFu, pos = 0, g = 0;
+    bool bad = false;
+    float ahat = 0.0f;
+    for (uint32_t j = 0; j < n; ++j) {
+      const float v = h2f(x[(uint64_t)j * d.C]);
+      uint32_t cs, f;
+      if (g == 0) {
+        const uint32_t qa = quant_anchor(v, lo, sa, inv_sa);
+        ahat = __builtin_fmaf((float)qa, sa, lo);
+        cs = ta[qa];
+        f = (uint32_t)ta[qa + 1] - cs;
+      } else {
+        const int32_t q = quant_delta(v - ahat, dl, inv_dl, M);
+        cs = tdM[q];
+        f = (uint32_t)tdM[q + 1] - cs;
+      }
+      g = g + 1 == d.G ? 0 : g + 1;
+      const uint32_t r = range >> kPrec;
+      // (HIP's __umul24 returns int: widen the product through uint32_t)
+      low += (uint64_t)(uint32_t)__umul24(r, cs);
+      range = __umul24(r, f);
+      if (low >> 32) {
+        low &= 0xFFFFFFFFull;
+        // add 1 to the bytes emitted: trailing 0xFF bytes become 0x00
+        uint32_t p = pos;
+        for (;;) {
+          if (p == 0) {  // a carry past the first byte: impossible for valid models
+            bad = true;
+            break;
+          }
+          --p;
+          const uint8_t nb = (uint8_t)(buf[p] + 1u);
+          buf[p] = nb;
+          if (nb != 0) break;
+        }
+      }
+      // whole bytes out: 0, 1 or 2 (3 only for damaged tables, which the
+      // statistics pass reported; it counted the same bytes)
+      const uint32_t sh = lead_zeros(range) & 24u;
+      for (uint32_t t = 0; t < sh; t += 8) {
+        if (pos < cap) buf[pos] = (uint8_t)(low >> 24); else bad = true;
+        ++pos;
+        low = (low << 8) & 0xFFFFFFFFull;
+      }
+      range <<= sh;
+      shifts[j] = (uint8_t)(sh >> 3);
+    }
+    for (uint32_t t = 0; t < 4; ++t) {
+      if (pos < cap) buf[pos] = (uint8_t)(low >> 24); else bad = true;
+      ++pos;
+      low = (low << 8) & 0xFFFFFFFFull;
+    }
+    bad = bad || pos != nbytes;
+    for (uint32_t p = pos; p < cap && (p & 7u) != 0; ++p) buf[p] = 0;
+
+    // the reading rule, as in emit: a lane's i-th request takes the unit's
+    // next payload block; requests of one step in lane order
+    const uint32_t nblk = bad ? 0u : (uint32_t)(pad8(nbytes) / kBlock);
+    uint8_t *pay = out + chunk_off[k] + kHdrBytes + (uint64_t)kRecBytes * S +
+                   offsets[(uint64_t)k * S + row * d.C + c0];
+    auto copy_block = [&](uint32_t blk, uint32_t slot) {
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(buf + (uint64_t)blk * kBlock);
+      uint32_t *dst = reinterpret_cast<uint32_t *>(pay + (uint64_t)slot * kBlock);
+      dst[0] = src[0];
+      dst[1] = src[1];
+    };
+    uint32_t cnt = 0, R = 4, W = 16, q = 0;
+    for (uint32_t blk = 0; blk < 3; ++blk) {
+      const bool req = blk < nblk;
+      const uint64_t mask = __builtin_amdgcn_ballot_w64(req);
+      if (req) {
+        copy_block(blk, cnt + lanes_below(mask));
+        ++q;
+      }
+      cnt += (uint32_t)__builtin_popcountll(mask);
+    }
+    g = 0;
+    for (uint32_t j = 0; j < n; ++j) {
+      const uint32_t ahead = W - R;
+      const bool need = g == 0 ? ahead <= 8u : ahead < 2u;
+      const bool req = need && q < nblk;
+      const uint64_t mask = __builtin_amdgcn_ballot_w64(req);
+      if (req) {
+        copy_block(q, cnt + lanes_below(mask));
+        ++q;
+      }
+      if (need) W += kBlock;
+      cnt += (uint32_t)__builtin_popcountll(mask);
+      R += shifts[j];
+      g = g + 1 == d.G ? 0 : g + 1;
+    }
+    if (bad || R != nbytes || q != nblk) set_status(status, KVC_ERR_CORRUPT_STREAM);
   }
 }
 
@@ -525,6 +684,12 @@ size_t encode_lds_bytes(uint32_t levels) {
   return sizeof(uint32_t) * ((size_t)kWave * kEA + (size_t)levels * kWave * kED);
 }
 
+// Scratch of one k_encode_redo lane: a stream's bytes (at most 4 + 2 per
+// token, in whole blocks), then one byte per token.
+uint32_t encode_redo_lane_bytes(uint32_t chunk) {
+  return (uint32_t)(pad8(4u + 2u * (uint64_t)chunk) + pad8(chunk));
+}
+
 // The emit kernel's LDS: the models plus every lane's block queue.
 size_t encode_emit_lds_bytes(uint32_t levels, uint32_t waves) {
   return encode_lds_bytes(levels) + sizeof(uint32_t) * (size_t)waves * kWave * kQueue;
@@ -538,8 +703,10 @@ hipError_t launch_encode(const Desc &d, const uint8_t *tables, const uint16_t *k
                          const DecodeGroup *groups, uint32_t n_groups, uint32_t levels,
                          uint32_t waves, uint8_t *records, uint64_t *row_sums, uint32_t *flags,
                          uint32_t *offsets, uint8_t *valid, uint64_t *payload,
-                         uint64_t *chunk_off_ws, uint32_t *fits, uint8_t *out, uint64_t out_cap,
-                         uint64_t *chunk_off_out, int32_t *status, hipStream_t stream) {
+                         uint64_t *chunk_off_ws, uint32_t *fits, uint32_t *redo,
+                         uint8_t *redo_scratch, uint32_t redo_blocks, uint8_t *out,
+                         uint64_t out_cap, uint64_t *chunk_off_out, int32_t *status,
+                         hipStream_t stream) {
   const uint32_t ncb = (d.C + kWave - 1) / kWave;
   const uint32_t n_units = 2u * d.L * ncb;
   const uint64_t blocks = (uint64_t)((n_units + kXcds - 1) / kXcds) * kXcds * n_groups;
@@ -551,10 +718,13 @@ hipError_t launch_encode(const Desc &d, const uint8_t *tables, const uint16_t *k
                               tables, 0, status, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_encode_layout, dim3(1), dim3(64), 0, stream, d, n_chunks, payload,
-                     chunk_off_ws, chunk_off_out, out_cap, fits, status);
+                     chunk_off_ws, chunk_off_out, out_cap, fits, redo, status);
   hipLaunchKernelGGL(k_encode_emit, dim3((uint32_t)blocks), dim3(waves * kWave), lds_emit, stream, d,
                      dev_chunks, groups, n_groups, n_units, tables, kv, T, records, offsets,
-                     chunk_off_ws, fits, out, status);
+                     chunk_off_ws, fits, out, redo, status);
+  hipLaunchKernelGGL(k_encode_redo, dim3(redo_blocks), dim3(kWave), 0, stream, d, dev_chunks,
+                     tables, kv, T, records, offsets, chunk_off_ws, fits, redo, redo_scratch,
+                     encode_redo_lane_bytes(d.chunk), out, status);
   hipLaunchKernelGGL(k_encode_header, dim3(1), dim3(256), 0, stream, d, dev_chunks, n_chunks,
                      tables, payload, chunk_off_ws, fits, out);
   return hipGetLastError();
