@@ -1,16 +1,22 @@
 """GPU parity at the full workload sizes (configurations 1-4), through the C ABI.
 
-At these sizes the oracle checks what it can compute in seconds on the host:
+Against the oracle, chunk by chunk (one chunk's oracle container and
+decoded KV in host memory at a time):
  * the profiled tables, completely (every frequency of every model, and the
    profile id);
- * sampled chunks (the first, the last - partial where the context is not a
-   multiple of 1,500 tokens - and one in the middle): the GPU containers are
-   byte-identical to the oracle's and the GPU-decoded binary16 KV equals the
-   oracle's decode of its own containers, element by element;
-and for every chunk, properties that hold at any size: container invariants
+ * every chunk of every workload: the GPU container is byte-identical to the
+   oracle's, and the GPU-decoded binary16 KV equals the oracle's decode of its
+   own container, element by element;
+ * the 13B-shaped workload is also encoded with every chunk at level 0 and at
+   level 2 (its tables hold three levels): the first, middle and last chunks
+   of those containers equal the oracle's, and every chunk's container
+   shrinks from level 0 to level 1 to level 2;
+and, for every chunk, properties that hold at any size: container invariants
 (header fields, stream lengths summing to the payload) and the half-step
 reconstruction bound on every element, evaluated on the GPU.
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -120,8 +126,9 @@ def test_full_size_config(idx):
     print("[fullsize] half-step bound on every element", flush=True)
     _half_step_on_gpu(d, enc, kv_dev, out, cfg)
 
-    for k in _sample_chunks(cfg):
-        print(f"[fullsize] oracle chunk {k} (level {levels[k]})", flush=True)
+    t_start = time.time()
+    for k in range(enc.n_chunks):
+        print(f"[fullsize] oracle chunk {k} of {enc.n_chunks} (level {levels[k]})", flush=True)
         oc = oracle.encode_chunk(od, otb, kv, k, levels[k])
         assert np.array_equal(enc.container(k).cpu().numpy(), oc), f"container {k}"
         n = enc.n_tokens[k]
@@ -129,5 +136,22 @@ def test_full_size_config(idx):
         oracle.decode_chunk_into(od, otb, oc, 0, n, levels[k], oo)
         got = out[:, :, 1500 * k:1500 * k + n].cpu().numpy().view(np.uint16)
         np.testing.assert_array_equal(got, oo)
+        del oc, oo, got
+    t_all = time.time() - t_start
+
+    if cfg.schedule == "level1":
+        sizes = [[enc.offsets[k + 1] - enc.offsets[k] for k in range(enc.n_chunks)]]
+        del out
+        for lv in (0, 2):
+            print(f"[fullsize] every chunk at level {lv}", flush=True)
+            e2 = kvc.encode(d, tables, kv_dev, [lv] * enc.n_chunks)
+            sizes.insert(lv, [e2.offsets[k + 1] - e2.offsets[k] for k in range(enc.n_chunks)])
+            for k in _sample_chunks(cfg):
+                oc = oracle.encode_chunk(od, otb, kv, k, lv)
+                assert np.array_equal(e2.container(k).cpu().numpy(), oc), f"level {lv} container {k}"
+            del e2
+        for k in range(enc.n_chunks):
+            assert sizes[0][k] > sizes[1][k] > sizes[2][k], (k, sizes[0][k], sizes[1][k], sizes[2][k])
     ratio = cfg.fp16_bytes() / enc.total_bytes()
-    print(f"[fullsize] config {idx}: bit-exact on sampled chunks, compression {ratio:.3f}", flush=True)
+    print(f"[fullsize] config {idx}: all {enc.n_chunks} chunks bit-exact "
+          f"(oracle comparison {t_all:.1f} s), compression {ratio:.3f}", flush=True)
