@@ -180,8 +180,16 @@ def status_str(code: int) -> str:
 
 
 def _stream(stream: Optional[torch.cuda.Stream]) -> ctypes.c_void_p:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    """The HIP stream to launch on: `stream`, else torch's current stream.  A
+    stream other than the current one first waits for the work already
+    queued on the current stream (among it the allocation and zero-fill of
+    the tensors the launch uses)."""
+    cur = torch.cuda.current_stream()
+    if stream is None:
+        return ctypes.c_void_p(cur.cuda_stream)
+    if stream.cuda_stream != cur.cuda_stream:
+        stream.wait_stream(cur)
+    return ctypes.c_void_p(stream.cuda_stream)
 
 
 def _check(code: int, what: str) -> None:
@@ -193,8 +201,11 @@ def _dev_status(device) -> torch.Tensor:
     return torch.zeros(1, dtype=torch.int32, device=device)
 
 
-def read_status(status: torch.Tensor, what: str) -> None:
-    """Synchronize with the status word's stream and raise on a device error."""
+def read_status(status: torch.Tensor, what: str, stream=None) -> None:
+    """Wait for the launch (on `stream`, else the current stream) and raise on
+    a device error."""
+    if stream is not None:
+        stream.synchronize()
     code = int(status.item())
     if code != OK:
         raise KvcError(code, what)
@@ -226,7 +237,7 @@ def profile(desc: CodecDesc, kv_prof: torch.Tensor, stream=None, check: bool = T
     _check(L.kvc_profile(ctypes.byref(desc), _kv_ptr(kv_prof), T, tables.data_ptr(), ws.data_ptr(),
                          wsb, st.data_ptr(), _stream(stream)), "kvc_profile")
     if check:
-        read_status(st, "kvc_profile")
+        read_status(st, "kvc_profile", stream)
     return tables
 
 
@@ -292,7 +303,7 @@ def encode(desc: CodecDesc, tables: torch.Tensor, kv: torch.Tensor, levels: Sequ
     if wsp is None:
         wsp = EncodeWorkspace(desc, T, kv.device)
     encode_async(desc, tables, kv, levels, wsp, stream)
-    read_status(wsp.status, "kvc_encode")
+    read_status(wsp.status, "kvc_encode", stream)
     offs = [int(x) for x in wsp.offsets.cpu().tolist()]
     blob = wsp.out[: offs[-1]].clone()
     ntok = [min(desc.chunk_tokens, T - k * desc.chunk_tokens) for k in range(n_chunks)]
@@ -355,7 +366,7 @@ def decode(desc: CodecDesc, tables: torch.Tensor, refs: Sequence[ChunkRef], T_to
     if wsp is None:
         wsp = DecodeWorkspace(desc, len(refs), dev)
     decode_async(desc, tables, refs, out, wsp, stream)
-    read_status(wsp.status, "kvc_decode")
+    read_status(wsp.status, "kvc_decode", stream)
     return out
 
 
@@ -368,7 +379,7 @@ def decode_symbols(desc: CodecDesc, tables: torch.Tensor, refs: Sequence[ChunkRe
     _check(lib().kvc_decode_symbols(ctypes.byref(desc), tables.data_ptr(), arr, len(refs),
                                     out.data_ptr(), T_total, wsp.ws.data_ptr(), wsp.ws_bytes,
                                     wsp.status.data_ptr(), _stream(stream)), "kvc_decode_symbols")
-    read_status(wsp.status, "kvc_decode_symbols")
+    read_status(wsp.status, "kvc_decode_symbols", stream)
     return out
 
 
@@ -382,7 +393,7 @@ def decode_index(desc: CodecDesc, tables: torch.Tensor, refs: Sequence[ChunkRef]
     _check(lib().kvc_decode_index(ctypes.byref(desc), tables.data_ptr(), arr, len(refs),
                                   offs.data_ptr(), wsp.ws.data_ptr(), wsp.ws_bytes,
                                   wsp.status.data_ptr(), _stream(stream)), "kvc_decode_index")
-    read_status(wsp.status, "kvc_decode_index")
+    read_status(wsp.status, "kvc_decode_index", stream)
     return offs
 
 
@@ -498,7 +509,7 @@ def restore(desc: CodecDesc, tables: torch.Tensor, chunks: Sequence[HostChunk], 
     if rws is None:
         rws = RestoreWorkspace(desc, chunks, batch, dev)
     restore_async(desc, tables, chunks, out, rws, stream)
-    read_status(rws.status, "kvc_restore")
+    read_status(rws.status, "kvc_restore", stream)
     return out
 
 
@@ -571,4 +582,4 @@ def decode_multi(desc: CodecDesc, tables: torch.Tensor, chunks: Sequence[Request
     if wsp is None:
         wsp = DecodeWorkspace(desc, len(chunks), tables.device)
     decode_multi_async(desc, tables, chunks, wsp, stream)
-    read_status(wsp.status, "kvc_decode_multi")
+    read_status(wsp.status, "kvc_decode_multi", stream)
