@@ -193,6 +193,28 @@ kvc_status kvc_decode(const kvc_codec_desc *d, const void *tables, const kvc_chu
                       uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream);
 
 /*
+ * kvc_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without `ws` / `ws_bytes`, the same kernels and the
+ * same results.  Its scratch is a fixed array of
+ * KVC_DECODE_STATIC_SCRATCH_BYTES in the library's device memory, one per
+ * GPU (the current device's is used; `stream` must belong to that device),
+ * held from the first call on a device until the process ends.  The call
+ * allocates nothing.  Requests whose kvc_decode workspace
+ * (kvc_decode_ws_bytes(d, n_chunks)) is larger than the array return
+ * KVC_ERR_CAPACITY before anything is launched.  Every call on one GPU uses
+ * the same array: calls that overlap on that GPU (on different streams, or
+ * from different host threads without ordering) race and give undefined
+ * results; calls ordered on one stream are safe.  Nothing in the array has
+ * to start at zero: each call rewrites what it reads.
+ * Device errors: those of kvc_decode.
+ */
+#define KVC_DECODE_STATIC_SCRATCH_BYTES (32ull << 20)
+kvc_status kvc_decode_static(const kvc_codec_desc *d, const void *tables,
+                             const kvc_chunk_ref *chunks, uint32_t n_chunks, uint16_t *kv_out,
+                             uint32_t T_total, int32_t *dev_status, hipStream_t stream);
+
+/*
  * The bitstream index alone: validates the containers' headers against the
  * tables and writes offsets_out (device, [n_chunks][2LC] u32): each stream's
  * byte offset from the start of its container's payload (exclusive prefix

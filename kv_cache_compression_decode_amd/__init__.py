@@ -38,7 +38,7 @@ EXPORTED = (
     "kvc_profile_ws_bytes", "kvc_profile", "kvc_container_bound", "kvc_encode_bound",
     "kvc_encode_ws_bytes", "kvc_encode", "kvc_decode_ws_bytes", "kvc_decode",
     "kvc_decode_index", "kvc_decode_symbols", "kvc_restore_staging_bytes", "kvc_restore",
-    "kvc_plan_stream", "kvc_decode_multi",
+    "kvc_plan_stream", "kvc_decode_multi", "kvc_decode_static",
 )
 
 
@@ -166,6 +166,8 @@ def lib():
     L.kvc_restore.restype = ctypes.c_int
     L.kvc_decode_multi.argtypes = [dp, vp, vp, u32, vp, u64, vp, vp]
     L.kvc_decode_multi.restype = ctypes.c_int
+    L.kvc_decode_static.argtypes = [dp, vp, vp, u32, vp, u32, vp, vp]
+    L.kvc_decode_static.restype = ctypes.c_int
     L.kvc_plan_stream.argtypes = [vp, u32, u32, vp, u32, ctypes.c_double, ctypes.c_double, vp, vp]
     L.kvc_plan_stream.restype = ctypes.c_int
     _lib = L
@@ -368,6 +370,17 @@ def decode(desc: CodecDesc, tables: torch.Tensor, refs: Sequence[ChunkRef], T_to
     decode_async(desc, tables, refs, out, wsp, stream)
     read_status(wsp.status, "kvc_decode", stream)
     return out
+
+
+def decode_static(desc: CodecDesc, tables: torch.Tensor, refs: Sequence[ChunkRef],
+                  out: torch.Tensor, status: torch.Tensor, stream=None) -> None:
+    """kvc_decode_static: decode into out [L][2][T_total][C] using the
+    library's own fixed device scratch (no workspace, nothing allocated);
+    `status` is a caller-owned int32 device word, read after synchronizing."""
+    arr = _refs_array(refs)
+    _check(lib().kvc_decode_static(ctypes.byref(desc), tables.data_ptr(), arr, len(refs),
+                                   _kv_ptr(out), out.shape[2], status.data_ptr(),
+                                   _stream(stream)), "kvc_decode_static")
 
 
 def decode_symbols(desc: CodecDesc, tables: torch.Tensor, refs: Sequence[ChunkRef],

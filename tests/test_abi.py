@@ -210,3 +210,16 @@ def test_decode_multi_synchronous_errors(L):
     bad = chunks([(A, 100, 0)])
     bad[0].kv_out = None
     assert call(bad) == kvc.ERR_INVALID_ARG
+
+
+def test_decode_static_refuses_oversized_request_before_any_device_call(L):
+    """kvc_decode_static checks its fixed scratch against the request before
+    touching the device: an oversized request returns KVC_ERR_CAPACITY here,
+    on a host without a GPU."""
+    d = kvc.make_desc(80, 1024)
+    n = 64
+    assert L.kvc_decode_ws_bytes(ctypes.byref(d), n) > 32 << 20
+    refs = (kvc.ChunkRef * n)()
+    assert L.kvc_decode_static(ctypes.byref(d), 4096, refs, n, 4096, 1, 4096, None) == kvc.ERR_CAPACITY
+    bad = kvc.make_desc(80, 1024, delta_bits=((7, 5, 4),))
+    assert L.kvc_decode_static(ctypes.byref(bad), 4096, refs, 1, 4096, 1, 4096, None) == kvc.ERR_INVALID_ARG
