@@ -167,14 +167,18 @@ struct Stream {
 // across the branch, so nothing has to wait for the load before the block is
 // stored, a group later.
 __device__ inline void advance(Stream &s, Source &src, bool need) {
-  if (__builtin_amdgcn_ballot_w64(need) == 0) return;
-  const bool req = need && s.rem != 0;
-  const uint64_t mask = __builtin_amdgcn_ballot_w64(req);
+  const uint64_t need_mask = __builtin_amdgcn_ballot_w64(need);
+  if (need_mask == 0) return;
+  // the requesting lanes: those that need and still have a block to ask for
+  const uint64_t mask = need_mask & __builtin_amdgcn_ballot_w64(s.rem != 0);
   if (need) s.put_block();
-  const uint32_t off = src.ubase + (src.cnt + lanes_below(mask)) * kBlock;
-  s.hoff = need ? off : s.hoff;
+  // the unit's blocks handed out so far plus the requesting lanes below this one
+  const uint32_t blk = __builtin_amdgcn_mbcnt_hi(
+      (uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, src.cnt));
+  s.hoff = need ? src.ubase + blk * kBlock : s.hoff;
   s.held = __builtin_amdgcn_raw_buffer_load_b64(src.rsrc, s.hoff, 0, 0);
-  s.rem = req ? s.rem - 1u : s.rem;
+  // one block fewer to ask for (none below zero: a lane without one did not ask)
+  s.rem = need ? __builtin_elementwise_sub_sat(s.rem, 1u) : s.rem;
   src.cnt += (uint32_t)__builtin_popcountll(mask);
 }
 // At a group's anchor: a ring with at most 8 bytes left takes its block.
@@ -253,16 +257,18 @@ __device__ inline uint32_t step(Stream &x, const AnchorTop &at, uint64_t &lost_a
   if constexpr (kSymbols) {
     return kAnchor ? (uint32_t)xq >> 7 : (uint32_t)((xq >> 7) + x.M);
   } else {
-    float y;
     // 128 q is exact in binary32 and (128 q)(dl / 128) = q dl exactly, so
     // this is the single rounding of fma(q, dl, ahat)
     if constexpr (kAnchor) {
       x.ahat = __builtin_fmaf((float)xq, x.sa7, x.lo);
-      y = x.ahat;
+      // the register barrier that keeps the fma and the binary16 conversion
+      // apart (see f2h) is put on ahat itself, which stays live, so the
+      // conversion needs no copy of it
+      __asm__("" : "+v"(x.ahat));
+      return __builtin_bit_cast(uint16_t, (_Float16)x.ahat);
     } else {
-      y = __builtin_fmaf((float)xq, x.dl7, x.ahat);
+      return f2h(__builtin_fmaf((float)xq, x.dl7, x.ahat));
     }
-    return f2h(y);
   }
 }
 
