@@ -135,6 +135,18 @@ def _load():
     lib.orc_f2h_patterns.argtypes = [u32, u64, vp]
     lib.orc_set_threads.argtypes = [ctypes.c_int]
     lib.orc_get_threads.restype = ctypes.c_int
+    lib.orc_refine_quantize.argtypes = [vp, u32, u32, u32, u32, vp, vp, vp, vp, vp, vp, vp]
+    lib.orc_refine_dequantize.argtypes = [vp, vp, u32, u32, u32, u32, ctypes.c_float,
+                                          ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                          ctypes.c_float, vp]
+    lib.orc_refine_profile_id.argtypes = [vp, u32, u64, vp, vp]
+    lib.orc_refine_profile_id.restype = u64
+    lib.orc_profile_refine.argtypes = [vp, vp, u32, u32, u64, vp, vp, vp]
+    lib.orc_encode_refine_chunk.argtypes = [vp, vp, vp, u64, u64, u32, vp, u32, u32, u32, vp, u64]
+    lib.orc_encode_refine_chunk.restype = i64
+    lib.orc_decode_refined_chunk.argtypes = [vp, vp, vp, u64, vp, u64, vp, vp, u64, vp, u64,
+                                             u32, u32, u32, vp, u32]
+    lib.orc_decode_refine_symbols.argtypes = [vp, vp, vp, u64, u64, vp, u64, vp, u32, vp]
     _lib = lib
     return lib
 
@@ -418,5 +430,144 @@ def parse_header(container: np.ndarray) -> dict:
 def records(desc: Desc, container: np.ndarray) -> np.ndarray:
     """Stream records as a structured array (lo, sa, dl, nbytes)."""
     dt = np.dtype([("lo", "<f4"), ("sa", "<f4"), ("dl", "<f4"), ("nbytes", "<u4")])
+    S = desc.n_streams
+    return np.frombuffer(container[HDR_BYTES:HDR_BYTES + REC_BYTES * S].tobytes(), dt)
+
+
+# ------------------------------------------------------- refinement (R19)
+def refine_quantize(x: np.ndarray, group: int, dbits: int, ebits: int):
+    """Base quantization at dbits, then the refinement quantizer at ebits on
+    the residual against the binary32 base reconstruction (reading R19):
+    (lo, sa, dl, symbols, Da, Dd, refinement symbols)."""
+    x = np.ascontiguousarray(x, np.float32)
+    n = len(x)
+    sym = np.zeros(max(n, 1), np.int32)
+    esym = np.zeros(max(n, 1), np.int32)
+    v = [ctypes.c_float() for _ in range(5)]
+    st = _load().orc_refine_quantize(_p(x), n, group, dbits, ebits, *[ctypes.byref(t) for t in v[:3]],
+                                     _p(sym), ctypes.byref(v[3]), ctypes.byref(v[4]), _p(esym))
+    if st:
+        raise OracleError(st, "refine_quantize")
+    lo, sa, dl, Da, Dd = (np.float32(t.value) for t in v)
+    return lo, sa, dl, sym[:n], Da, Dd, esym[:n]
+
+
+def refine_dequantize(sym, esym, group: int, dbits: int, ebits: int, lo, sa, dl, Da, Dd):
+    """Refined values binary16(fma(q, D, xh)) of one stream (binary16 bits)."""
+    sym = np.ascontiguousarray(sym, np.int32)
+    esym = np.ascontiguousarray(esym, np.int32)
+    out = np.zeros(max(len(sym), 1), np.uint16)
+    f = ctypes.c_float
+    _load().orc_refine_dequantize(_p(sym), _p(esym), len(sym), group, dbits, ebits, f(lo), f(sa),
+                                  f(dl), f(Da), f(Dd), _p(out))
+    return out[: len(sym)]
+
+
+@dataclasses.dataclass
+class RefineTables:
+    """Refinement models: fEA / fED [level][m][64] (u16; anchor tokens / the
+    other tokens), their bits E, their id and the base tables' id."""
+    fEA: np.ndarray
+    fED: np.ndarray
+    ebits: int
+    refine_id: int
+    base_id: int
+
+
+def profile_refine(desc: Desc, kv_prof: np.ndarray, ebits: int, base_id: int) -> RefineTables:
+    kv = np.ascontiguousarray(kv_prof, np.uint16)
+    L, two, T, C = kv.shape
+    assert (L, two, C) == (desc.n_layers, 2, desc.n_channels)
+    S = desc.n_streams
+    fEA = np.zeros((desc.n_levels, S, DELTA_STRIDE), np.uint16)
+    fED = np.zeros((desc.n_levels, S, DELTA_STRIDE), np.uint16)
+    rid = ctypes.c_uint64()
+    st = _load().orc_profile_refine(_p(desc.words()), _p(kv), T, ebits, base_id, _p(fEA), _p(fED),
+                                    ctypes.byref(rid))
+    if st:
+        raise OracleError(st, "profile_refine")
+    return RefineTables(fEA, fED, ebits, int(rid.value), base_id)
+
+
+def refine_profile_id(desc: Desc, rt: RefineTables) -> int:
+    return int(_load().orc_refine_profile_id(_p(desc.words()), rt.ebits, rt.base_id,
+                                             _p(np.ascontiguousarray(rt.fEA, np.uint16)),
+                                             _p(np.ascontiguousarray(rt.fED, np.uint16))))
+
+
+def encode_refine_chunk(desc: Desc, rt: RefineTables, kv: np.ndarray, chunk: int,
+                        level: int) -> np.ndarray:
+    """The refinement container of chunk `chunk` over its base layer at `level`."""
+    kv = np.ascontiguousarray(kv, np.uint16)
+    T = kv.shape[2]
+    n = min(desc.chunk_tokens, T - chunk * desc.chunk_tokens)
+    cap = int(_load().orc_container_bound(_p(desc.words()), n))
+    out = np.zeros(cap, np.uint8)
+    r = _load().orc_encode_refine_chunk(_p(desc.words()), _p(rt.fEA), _p(rt.fED), rt.refine_id,
+                                        rt.base_id, rt.ebits, _p(kv), T, chunk, level, _p(out), cap)
+    if r < 0:
+        raise OracleError(int(r), "encode_refine_chunk")
+    return out[:r].copy()
+
+
+def encode_refine(desc: Desc, rt: RefineTables, kv: np.ndarray,
+                  levels: Sequence[int]) -> List[np.ndarray]:
+    T = kv.shape[2]
+    nch = (T + desc.chunk_tokens - 1) // desc.chunk_tokens
+    assert len(levels) == nch
+    return [encode_refine_chunk(desc, rt, kv, k, int(levels[k])) for k in range(nch)]
+
+
+def decode_refined_chunk_into(desc: Desc, tables: Tables, container: np.ndarray,
+                              rt: RefineTables, rcontainer: np.ndarray, first_token: int,
+                              n_tokens: int, level: int, out: np.ndarray) -> None:
+    assert out.dtype == np.uint16 and out.flags.c_contiguous
+    st = _load().orc_decode_refined_chunk(_p(desc.words()), _p(tables.fA), _p(tables.fD),
+                                          tables.profile_id, _p(container), len(container),
+                                          _p(rt.fEA), _p(rt.fED), rt.refine_id, _p(rcontainer),
+                                          len(rcontainer), first_token, n_tokens, level, _p(out),
+                                          out.shape[2])
+    if st:
+        raise OracleError(st, "decode_refined_chunk")
+
+
+def decode_refined(desc: Desc, tables: Tables, containers: Sequence[np.ndarray],
+                   rt: RefineTables, rcontainers: Sequence[np.ndarray], levels: Sequence[int],
+                   T_total: int) -> np.ndarray:
+    out = np.zeros((desc.n_layers, 2, T_total, desc.n_channels), np.uint16)
+    for k, (c, rc) in enumerate(zip(containers, rcontainers)):
+        n = min(desc.chunk_tokens, T_total - k * desc.chunk_tokens)
+        decode_refined_chunk_into(desc, tables, c, rt, rc, k * desc.chunk_tokens, n,
+                                  int(levels[k]), out)
+    return out
+
+
+def decode_refine_symbols(desc: Desc, rt: RefineTables, rcontainer: np.ndarray,
+                          ids: Sequence[int], n_tokens: int) -> np.ndarray:
+    ids = np.ascontiguousarray(ids, np.uint32)
+    syms = np.zeros((len(ids), n_tokens), np.int32)
+    st = _load().orc_decode_refine_symbols(_p(desc.words()), _p(rt.fEA), _p(rt.fED), rt.refine_id,
+                                           rt.base_id, _p(rcontainer), len(rcontainer), _p(ids),
+                                           len(ids), _p(syms))
+    if st:
+        raise OracleError(st, "decode_refine_symbols")
+    return syms
+
+
+def parse_refine_header(container: np.ndarray) -> dict:
+    b = bytes(container[:HDR_BYTES])
+    le = lambda o, n: int.from_bytes(b[o:o + n], "little")
+    return {
+        "magic": b[0:4], "version": le(4, 2), "level": b[6], "ebits": b[7],
+        "group_tokens": le(8, 2), "cdf_prec": b[10], "delta_bits": tuple(b[11:14]),
+        "n_layers": le(16, 4), "n_channels": le(20, 4), "n_tokens": le(24, 4),
+        "first_token": le(28, 4), "refine_id": le(32, 8), "payload_bytes": le(40, 8),
+        "chunk_tokens": le(48, 4), "n_streams": le(52, 4), "base_id": le(56, 8),
+    }
+
+
+def refine_records(desc: Desc, container: np.ndarray) -> np.ndarray:
+    """Refinement stream records as a structured array (Da, Dd, nbytes)."""
+    dt = np.dtype([("Da", "<f4"), ("Dd", "<f4"), ("nbytes", "<u4"), ("zero", "<u4")])
     S = desc.n_streams
     return np.frombuffer(container[HDR_BYTES:HDR_BYTES + REC_BYTES * S].tobytes(), dt)

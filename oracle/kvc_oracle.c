@@ -39,6 +39,10 @@
  *   R17 a unit's payload holds its streams' bytes cut into 8-byte blocks (the
  *      last one zero-padded), in the order in which the reference reader
  *      (unit_reader below) asks for them.
+ *   R19 incremental refinement (the page's future work: low-quality KV
+ *      first, refinement bits after): a second layer per chunk that
+ *      quantizes the residual against the base layer's binary32
+ *      reconstruction (section "refinement" at the end of this file).
  * Arithmetic: IEEE-754 binary32 with round-to-nearest-even, correctly
  * rounded division, true fused multiply-add, no flush-to-zero, no
  * contraction (build with -ffp-contract=off).
@@ -616,27 +620,26 @@ static void unit_span(const params *p, uint32_t u, uint32_t *m0, uint32_t *nv) {
  * stream does not decode to exactly its nbytes.  `order` (optional) receives
  * lane << 16 | block for every slot.
  */
-static int unit_reader(const params *p, const uint16_t *fA, const uint16_t *fD, uint32_t level,
-                       uint32_t m0, uint32_t nv, uint32_t n, const uint32_t *nb,
-                       const uint8_t *const *streams, const uint8_t *slots_in, uint64_t n_slots,
-                       uint8_t *slots_out, int32_t *sym, uint32_t *order) {
-  const uint32_t S = n_streams(p);
+/* The models one lane's stream is coded with: symbol j uses (fa, AA) when
+ * j % G == 0 and (fd, AD) otherwise. */
+typedef struct {
+  uint32_t fa[ANCHOR_ALPHA], fd[MAX_DELTA_ALPHA];
+  uint32_t AA, AD;
+} lane_models;
+
+static int unit_reader_models(const params *p, const lane_models *mods, uint32_t nv, uint32_t n,
+                              const uint32_t *nb, const uint8_t *const *streams,
+                              const uint8_t *slots_in, uint64_t n_slots, uint8_t *slots_out,
+                              int32_t *sym, uint32_t *order) {
   uint32_t nblk[UNIT_LANES], q[UNIT_LANES], W[UNIT_LANES];
   uint8_t *own[UNIT_LANES];
   const uint8_t *buf[UNIT_LANES];
   rc_dec dec[UNIT_LANES];
-  uint32_t fa[UNIT_LANES][ANCHOR_ALPHA], fd[UNIT_LANES][MAX_DELTA_ALPHA];
-  uint32_t A[UNIT_LANES];
   int err = ORC_OK;
   for (uint32_t l = 0; l < nv; ++l) {
-    const uint32_t m = m0 + l;
-    const uint32_t b = p->bits[level][third_of(m / (2 * p->C), p->L)];
     nblk[l] = (uint32_t)(pad8(nb[l]) / BLOCK);
     q[l] = 0;
     W[l] = 16;
-    A[l] = delta_alpha(b);
-    widen_freqs(fA + (size_t)m * ANCHOR_ALPHA, ANCHOR_ALPHA, fa[l]);
-    widen_freqs(fD + ((size_t)level * S + m) * MAX_DELTA_ALPHA, A[l], fd[l]);
     own[l] = NULL;
     if (streams) {
       buf[l] = streams[l];
@@ -675,8 +678,8 @@ static int unit_reader(const params *p, const uint16_t *fA, const uint16_t *fD, 
     }
     for (uint32_t l = 0; l < nv && !err; ++l) {
       int32_t s;
-      err = anchor ? rc_dec_step(&dec[l], buf[l], nb[l], fa[l], ANCHOR_ALPHA, &s)
-                   : rc_dec_step(&dec[l], buf[l], nb[l], fd[l], A[l], &s);
+      err = anchor ? rc_dec_step(&dec[l], buf[l], nb[l], mods[l].fa, mods[l].AA, &s)
+                   : rc_dec_step(&dec[l], buf[l], nb[l], mods[l].fd, mods[l].AD, &s);
       if (sym) sym[(size_t)l * n + j] = s;
     }
   }
@@ -685,6 +688,28 @@ static int unit_reader(const params *p, const uint16_t *fA, const uint16_t *fD, 
     if (dec[l].pos != nb[l]) err = ORC_ERR_CORRUPT;
   if (!err && next != n_slots) err = ORC_ERR_CORRUPT; /* every block asked for once */
   for (uint32_t l = 0; l < nv; ++l) free(own[l]);
+  return err;
+}
+
+/* The base layer's models of the unit's lanes at `level`. */
+static int unit_reader(const params *p, const uint16_t *fA, const uint16_t *fD, uint32_t level,
+                       uint32_t m0, uint32_t nv, uint32_t n, const uint32_t *nb,
+                       const uint8_t *const *streams, const uint8_t *slots_in, uint64_t n_slots,
+                       uint8_t *slots_out, int32_t *sym, uint32_t *order) {
+  const uint32_t S = n_streams(p);
+  lane_models *mods = (lane_models *)malloc(sizeof(lane_models) * UNIT_LANES);
+  if (!mods) return ORC_ERR_CAPACITY;
+  for (uint32_t l = 0; l < nv; ++l) {
+    const uint32_t m = m0 + l;
+    const uint32_t b = p->bits[level][third_of(m / (2 * p->C), p->L)];
+    mods[l].AA = ANCHOR_ALPHA;
+    mods[l].AD = delta_alpha(b);
+    widen_freqs(fA + (size_t)m * ANCHOR_ALPHA, ANCHOR_ALPHA, mods[l].fa);
+    widen_freqs(fD + ((size_t)level * S + m) * MAX_DELTA_ALPHA, mods[l].AD, mods[l].fd);
+  }
+  const int err = unit_reader_models(p, mods, nv, n, nb, streams, slots_in, n_slots, slots_out,
+                                     sym, order);
+  free(mods);
   return err;
 }
 
@@ -1077,4 +1102,517 @@ void orc_f2h_patterns(uint32_t start, uint64_t n, uint16_t *out) {
 }
 void orc_h2f_array(const uint16_t *h, float *out, uint64_t n) {
   for (uint64_t i = 0; i < n; ++i) out[i] = orc_h2f(h[i]);
+}
+
+/* =========================================================== refinement
+ * R19: incremental, SVC-like refinement (CacheGen page, 局限与 Future Work:
+ * send a low-quality version of the KV first, then refinement bits).  The
+ * page describes no scheme; the reading taken here is a two-layer successive
+ * refinement that leaves the base layer untouched:
+ *   - the base layer of a chunk is its container at the chosen level, coded
+ *     exactly as above;
+ *   - the refinement layer quantizes, per stream, the residual
+ *       e[j] = x[j] - xh[j]
+ *     against the base reconstruction in binary32, before its binary16
+ *     rounding (anchors xh = fma(qa, sa, lo); deltas xh = fma(q, dl, ahat)),
+ *     with a symmetric mid-tread quantizer of E bits (Me = 2^(E-1) - 1):
+ *     one scale over the stream's anchor tokens, Da = max |e| / Me, and one
+ *     over its other tokens, Dd = max |e| / Me (the base layer keeps anchors
+ *     and deltas apart the same way); q = D == 0 ? 0 : clamp(rint(e / D),
+ *     -Me, Me); symbol q + Me in the alphabet 2^E - 1;
+ *   - the refinement symbols are range-coded in token order with two models
+ *     per (level, layer, K/V, channel): one for anchor tokens and one for
+ *     the others, profiled and normalised like the base models;
+ *   - refined output: binary16(fma(q, D, xh)), one binary32 rounding then
+ *     one binary16 rounding.
+ * Its container ("KVCR") has the base container's layout: a 64-byte header,
+ * 2LC records {f32 Da, f32 Dd, u32 nbytes, u32 0}, then the payload in the
+ * reference reader's block order (R17). */
+
+#define REFINE_MAX_BITS 6u
+
+/* Base reconstruction of one stream in binary32 (before binary16). */
+static void base_recon(const int32_t *sym, uint32_t n, uint32_t G, uint32_t dbits, float lo,
+                       float sa, float dl, float *xh) {
+  const int32_t M = delta_m(dbits);
+  float ahat = 0.0f;
+  for (uint32_t j = 0; j < n; ++j) {
+    if (j % G == 0) {
+      ahat = fmaf((float)sym[j], sa, lo);
+      xh[j] = ahat;
+    } else {
+      xh[j] = fmaf((float)(sym[j] - M), dl, ahat);
+    }
+  }
+}
+
+/* The refinement quantizer of one stream: from x and its base
+ * reconstruction xh, the two scales and the symbols (q + Me). */
+static void refine_quantize_xh(const float *x, const float *xh, uint32_t n, uint32_t G,
+                               uint32_t ebits, float *Da_out, float *Dd_out, int32_t *esym) {
+  const int32_t Me = delta_m(ebits);
+  float amax = 0.0f, dmax = 0.0f;
+  for (uint32_t j = 0; j < n; ++j) {
+    const float a = fabsf(x[j] - xh[j]);
+    if (j % G == 0) {
+      if (a > amax) amax = a;
+    } else {
+      if (a > dmax) dmax = a;
+    }
+  }
+  const float Da = amax / (float)Me, Dd = dmax / (float)Me;
+  for (uint32_t j = 0; j < n; ++j) {
+    const float D = (j % G == 0) ? Da : Dd;
+    int q = 0;
+    if (D != 0.0f) {
+      q = (int)rintf((x[j] - xh[j]) / D);
+      if (q < -Me) q = -Me;
+      if (q > Me) q = Me;
+    }
+    esym[j] = q + Me;
+  }
+  *Da_out = Da;
+  *Dd_out = Dd;
+}
+
+/* One stream: base quantization at dbits, then the refinement quantizer at
+ * ebits.  Outputs the base side info and symbols and the refinement scales
+ * and symbols. */
+int orc_refine_quantize(const float *x, uint32_t n, uint32_t G, uint32_t dbits, uint32_t ebits,
+                        float *lo, float *sa, float *dl, int32_t *sym, float *Da, float *Dd,
+                        int32_t *esym) {
+  if (ebits < 2 || ebits > REFINE_MAX_BITS) return ORC_ERR_ARG;
+  int st = orc_quantize(x, n, G, dbits, lo, sa, dl, sym);
+  if (st) return st;
+  float *xh = (float *)malloc(sizeof(float) * (n ? n : 1));
+  if (!xh) return ORC_ERR_CAPACITY;
+  base_recon(sym, n, G, dbits, *lo, *sa, *dl, xh);
+  refine_quantize_xh(x, xh, n, G, ebits, Da, Dd, esym);
+  free(xh);
+  return ORC_OK;
+}
+
+/* Refined reconstruction of one stream: binary16(fma(q, D, xh)). */
+void orc_refine_dequantize(const int32_t *sym, const int32_t *esym, uint32_t n, uint32_t G,
+                           uint32_t dbits, uint32_t ebits, float lo, float sa, float dl, float Da,
+                           float Dd, uint16_t *out) {
+  const int32_t Me = delta_m(ebits);
+  float *xh = (float *)malloc(sizeof(float) * (n ? n : 1));
+  base_recon(sym, n, G, dbits, lo, sa, dl, xh);
+  for (uint32_t j = 0; j < n; ++j) {
+    const float D = (j % G == 0) ? Da : Dd;
+    out[j] = orc_f2h(fmaf((float)(esym[j] - Me), D, xh[j]));
+  }
+  free(xh);
+}
+
+/* Refinement profile id: FNV-1a over the descriptor, E (u32) and the base
+ * profile id (u64), then for each (layer, K/V) row the FNV-1a of that row's
+ * per-model FNV-1a values; a model's value covers, level by level, its
+ * anchor-token frequencies then its other-token frequencies (u16, LE). */
+uint64_t orc_refine_profile_id(const uint32_t *pw, uint32_t ebits, uint64_t base_id,
+                               const uint16_t *fEA, const uint16_t *fED) {
+  params p;
+  if (read_params(pw, &p)) return 0;
+  const uint32_t S = n_streams(&p);
+  const uint32_t A = delta_alpha(ebits);
+  uint64_t h = desc_hash(&p);
+  h = fnv_u32(h, ebits);
+  h = fnv_u64(h, base_id);
+  for (uint32_t row = 0; row < 2 * p.L; ++row) {
+    uint64_t hr = FNV_OFFSET;
+    for (uint32_t c = 0; c < p.C; ++c) {
+      const uint32_t m = row * p.C + c;
+      uint64_t hm = FNV_OFFSET;
+      for (uint32_t lv = 0; lv < p.nlev; ++lv) {
+        const uint16_t *fa = fEA + ((size_t)lv * S + m) * MAX_DELTA_ALPHA;
+        const uint16_t *fd = fED + ((size_t)lv * S + m) * MAX_DELTA_ALPHA;
+        for (uint32_t s = 0; s < A; ++s) hm = fnv_u16(hm, fa[s]);
+        for (uint32_t s = 0; s < A; ++s) hm = fnv_u16(hm, fd[s]);
+      }
+      hr = fnv_u64(hr, hm);
+    }
+    h = fnv_u64(h, hr);
+  }
+  return h;
+}
+
+/* Refinement profiling: over every profiling chunk, every stream and every
+ * level, count the refinement symbols of anchor tokens (fEA) and of the
+ * other tokens (fED) per (level, stream), normalise to 2^15.  Tables
+ * fEA/fED: [n_levels][2LC][64] u16 (first 2^E - 1 entries used). */
+int orc_profile_refine(const uint32_t *pw, const uint16_t *kv, uint32_t T, uint32_t ebits,
+                       uint64_t base_id, uint16_t *fEA, uint16_t *fED, uint64_t *refine_id) {
+  params p;
+  int st = read_params(pw, &p);
+  if (st) return st;
+  if (ebits < 2 || ebits > REFINE_MAX_BITS) return ORC_ERR_ARG;
+  if (T == 0) return ORC_ERR_SHAPE;
+  const uint32_t S = n_streams(&p);
+  const uint32_t A = delta_alpha(ebits);
+  const uint32_t nchunks = (T + p.chunk - 1) / p.chunk;
+  int err = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (long mm = 0; mm < (long)S; ++mm) {
+    const uint32_t m = (uint32_t)mm;
+    const uint32_t l = m / (2 * p.C);
+    float *x = (float *)malloc(sizeof(float) * p.chunk);
+    int32_t *sym = (int32_t *)malloc(sizeof(int32_t) * p.chunk);
+    int32_t *esym = (int32_t *)malloc(sizeof(int32_t) * p.chunk);
+    uint64_t ca[4][MAX_DELTA_ALPHA], cd[4][MAX_DELTA_ALPHA];
+    memset(ca, 0, sizeof ca);
+    memset(cd, 0, sizeof cd);
+    for (uint32_t k = 0; k < nchunks; ++k) {
+      const uint32_t t0 = k * p.chunk;
+      const uint32_t n = (T - t0 < p.chunk) ? T - t0 : p.chunk;
+      widen_stream(kv, &p, T, m, t0, n, x);
+      for (uint32_t lv = 0; lv < p.nlev; ++lv) {
+        float lo, sa, dl, Da, Dd;
+        if (orc_refine_quantize(x, n, p.G, p.bits[lv][third_of(l, p.L)], ebits, &lo, &sa, &dl,
+                                sym, &Da, &Dd, esym)) {
+#pragma omp atomic write
+          err = ORC_ERR_NONFINITE;
+          break;
+        }
+        for (uint32_t j = 0; j < n; ++j) {
+          if (j % p.G == 0)
+            ca[lv][esym[j]]++;
+          else
+            cd[lv][esym[j]]++;
+        }
+      }
+    }
+    uint32_t f[MAX_DELTA_ALPHA];
+    for (uint32_t lv = 0; lv < p.nlev; ++lv) {
+      uint16_t *da = fEA + ((size_t)lv * S + m) * MAX_DELTA_ALPHA;
+      uint16_t *dd = fED + ((size_t)lv * S + m) * MAX_DELTA_ALPHA;
+      orc_normalize(ca[lv], A, f);
+      for (uint32_t s = 0; s < MAX_DELTA_ALPHA; ++s) da[s] = (uint16_t)(s < A ? f[s] : 0u);
+      orc_normalize(cd[lv], A, f);
+      for (uint32_t s = 0; s < MAX_DELTA_ALPHA; ++s) dd[s] = (uint16_t)(s < A ? f[s] : 0u);
+    }
+    free(x);
+    free(sym);
+    free(esym);
+  }
+  if (err) return err;
+  *refine_id = orc_refine_profile_id(pw, ebits, base_id, fEA, fED);
+  return ORC_OK;
+}
+
+/* The refinement models of the unit's lanes at `level`. */
+static void refine_models(const params *p, const uint16_t *fEA, const uint16_t *fED,
+                          uint32_t level, uint32_t ebits, uint32_t m0, uint32_t nv,
+                          lane_models *mods) {
+  const uint32_t S = n_streams(p);
+  for (uint32_t l = 0; l < nv; ++l) {
+    const uint32_t m = m0 + l;
+    mods[l].AA = mods[l].AD = delta_alpha(ebits);
+    widen_freqs(fEA + ((size_t)level * S + m) * MAX_DELTA_ALPHA, mods[l].AA, mods[l].fa);
+    widen_freqs(fED + ((size_t)level * S + m) * MAX_DELTA_ALPHA, mods[l].AD, mods[l].fd);
+  }
+}
+
+/*
+ * The refinement layer of chunk `chunk` of kv [L][2][T][C] over its base
+ * layer at `level`, as one "KVCR" container.  Returns its size, or a
+ * negative error.
+ */
+int64_t orc_encode_refine_chunk(const uint32_t *pw, const uint16_t *fEA, const uint16_t *fED,
+                                uint64_t refine_id, uint64_t base_id, uint32_t ebits,
+                                const uint16_t *kv, uint32_t T, uint32_t chunk, uint32_t level,
+                                uint8_t *out, uint64_t cap) {
+  params p;
+  int st = read_params(pw, &p);
+  if (st) return st;
+  if (level >= p.nlev || ebits < 2 || ebits > REFINE_MAX_BITS) return ORC_ERR_ARG;
+  const uint64_t t0 = (uint64_t)chunk * p.chunk;
+  if (t0 >= T) return ORC_ERR_SHAPE;
+  const uint32_t n = (uint32_t)((T - t0 < p.chunk) ? T - t0 : p.chunk);
+  const uint32_t S = n_streams(&p);
+  const uint32_t A = delta_alpha(ebits);
+  const uint64_t slot = pad8(4u + 2u * (uint64_t)n);
+  uint8_t *scratch = (uint8_t *)calloc((size_t)S, (size_t)slot);
+  float *side = (float *)malloc(sizeof(float) * 2u * S);
+  uint32_t *nb = (uint32_t *)malloc(sizeof(uint32_t) * S);
+  if (!scratch || !side || !nb) {
+    free(scratch);
+    free(side);
+    free(nb);
+    return ORC_ERR_CAPACITY;
+  }
+  int err = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (long mm = 0; mm < (long)S; ++mm) {
+    const uint32_t m = (uint32_t)mm;
+    const uint32_t l = m / (2 * p.C);
+    float *x = (float *)malloc(sizeof(float) * n);
+    int32_t *sym = (int32_t *)malloc(sizeof(int32_t) * n);
+    int32_t *esym = (int32_t *)malloc(sizeof(int32_t) * n);
+    uint32_t fa[MAX_DELTA_ALPHA], fd[MAX_DELTA_ALPHA];
+    float lo, sa, dl;
+    widen_stream(kv, &p, T, m, (uint32_t)t0, n, x);
+    int e = orc_refine_quantize(x, n, p.G, p.bits[level][third_of(l, p.L)], ebits, &lo, &sa, &dl,
+                                sym, &side[2 * m], &side[2 * m + 1], esym);
+    if (!e) {
+      widen_freqs(fEA + ((size_t)level * S + m) * MAX_DELTA_ALPHA, A, fa);
+      widen_freqs(fED + ((size_t)level * S + m) * MAX_DELTA_ALPHA, A, fd);
+      const int64_t w =
+          orc_rc_encode(esym, n, p.G, fa, A, fd, A, scratch + (size_t)m * slot, slot);
+      if (w < 0)
+        e = (int)w;
+      else
+        nb[m] = (uint32_t)w;
+    }
+    if (e) {
+#pragma omp critical
+      err = e;
+    }
+    free(x);
+    free(sym);
+    free(esym);
+  }
+  if (err) {
+    free(scratch);
+    free(side);
+    free(nb);
+    return err;
+  }
+  uint64_t payload = 0;
+  for (uint32_t m = 0; m < S; ++m) payload += pad8(nb[m]);
+  const uint64_t total = HDR_BYTES + (uint64_t)REC_BYTES * S + payload;
+  if (total > cap) {
+    free(scratch);
+    free(side);
+    free(nb);
+    return ORC_ERR_CAPACITY;
+  }
+  memset(out, 0, (size_t)total);
+  memcpy(out, "KVCR", 4);
+  put_u16(out + 4, 1);
+  out[6] = (uint8_t)level;
+  out[7] = (uint8_t)ebits;
+  put_u16(out + 8, (uint16_t)p.G);
+  out[10] = (uint8_t)p.prec;
+  for (int j = 0; j < 3; ++j) out[11 + j] = (uint8_t)p.bits[level][j];
+  put_u32(out + 16, p.L);
+  put_u32(out + 20, p.C);
+  put_u32(out + 24, n);
+  put_u32(out + 28, (uint32_t)t0);
+  put_u64(out + 32, refine_id);
+  put_u64(out + 40, payload);
+  put_u32(out + 48, p.chunk);
+  put_u32(out + 52, S);
+  put_u64(out + 56, base_id);
+  for (uint32_t m = 0; m < S; ++m) {
+    uint8_t *rec = out + HDR_BYTES + (size_t)REC_BYTES * m;
+    put_f32(rec, side[2 * m]);
+    put_f32(rec + 4, side[2 * m + 1]);
+    put_u32(rec + 8, nb[m]);
+    put_u32(rec + 12, 0);
+  }
+  uint64_t *uoff = (uint64_t *)malloc(sizeof(uint64_t) * (n_units(&p) + 1));
+  uoff[0] = 0;
+  for (uint32_t u = 0; u < n_units(&p); ++u) {
+    uint32_t m0, nv;
+    unit_span(&p, u, &m0, &nv);
+    uint64_t sz = 0;
+    for (uint32_t l = 0; l < nv; ++l) sz += pad8(nb[m0 + l]);
+    uoff[u + 1] = uoff[u] + sz;
+  }
+  uint8_t *pay = out + HDR_BYTES + (size_t)REC_BYTES * S;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (long uu = 0; uu < (long)n_units(&p); ++uu) {
+    const uint32_t u = (uint32_t)uu;
+    uint32_t m0, nv;
+    unit_span(&p, u, &m0, &nv);
+    const uint8_t *streams[UNIT_LANES];
+    for (uint32_t l = 0; l < nv; ++l) streams[l] = scratch + (size_t)(m0 + l) * slot;
+    lane_models *mods = (lane_models *)malloc(sizeof(lane_models) * UNIT_LANES);
+    refine_models(&p, fEA, fED, level, ebits, m0, nv, mods);
+    const int e = unit_reader_models(&p, mods, nv, n, nb + m0, streams, NULL,
+                                     (uoff[u + 1] - uoff[u]) / BLOCK, pay + uoff[u], NULL, NULL);
+    free(mods);
+    if (e) {
+#pragma omp critical
+      err = e;
+    }
+  }
+  free(uoff);
+  free(scratch);
+  free(side);
+  free(nb);
+  return err ? err : (int64_t)total;
+}
+
+typedef struct {
+  uint32_t n, level, ebits;
+  uint64_t payload;
+} refine_hdr;
+
+static int check_refine_header(const params *p, uint64_t refine_id, uint64_t base_id,
+                               const uint8_t *c, uint64_t nbytes, refine_hdr *h) {
+  const uint32_t S = n_streams(p);
+  if (nbytes < HDR_BYTES + (uint64_t)REC_BYTES * S) return ORC_ERR_CORRUPT;
+  if (memcmp(c, "KVCR", 4) != 0 || get_u16(c + 4) != 1) return ORC_ERR_CORRUPT;
+  h->level = c[6];
+  h->ebits = c[7];
+  h->n = get_u32(c + 24);
+  h->payload = get_u64(c + 40);
+  if (h->level >= p->nlev || h->ebits < 2 || h->ebits > REFINE_MAX_BITS ||
+      get_u16(c + 8) != p->G || c[10] != p->prec)
+    return ORC_ERR_CORRUPT;
+  for (int j = 0; j < 3; ++j)
+    if (c[11 + j] != p->bits[h->level][j]) return ORC_ERR_CORRUPT;
+  if (get_u32(c + 16) != p->L || get_u32(c + 20) != p->C || get_u32(c + 48) != p->chunk ||
+      get_u32(c + 52) != S)
+    return ORC_ERR_CORRUPT;
+  if (h->n == 0 || h->n > p->chunk) return ORC_ERR_CORRUPT;
+  if (get_u64(c + 32) != refine_id || get_u64(c + 56) != base_id) return ORC_ERR_PROFILE;
+  if (HDR_BYTES + (uint64_t)REC_BYTES * S + h->payload != nbytes) return ORC_ERR_CORRUPT;
+  uint64_t sum = 0;
+  for (uint32_t m = 0; m < S; ++m) sum += pad8(get_u32(c + HDR_BYTES + (size_t)REC_BYTES * m + 8));
+  if (sum != h->payload) return ORC_ERR_CORRUPT;
+  return ORC_OK;
+}
+
+/*
+ * Decode a chunk's base container and its refinement container into out
+ * [L][2][T_total][C] at tokens [first_token, first_token + n_tokens): the
+ * refined values binary16(fma(q, D, xh)).  Both headers must agree with the
+ * call (level, token count) and with each other; the refinement must belong
+ * to these base tables.
+ */
+int orc_decode_refined_chunk(const uint32_t *pw, const uint16_t *fA, const uint16_t *fD,
+                             uint64_t base_id, const uint8_t *c, uint64_t nbytes,
+                             const uint16_t *fEA, const uint16_t *fED, uint64_t refine_id,
+                             const uint8_t *rc, uint64_t rbytes, uint32_t first_token,
+                             uint32_t n_tokens, uint32_t level, uint16_t *out, uint32_t T_total) {
+  params p;
+  int st = read_params(pw, &p);
+  if (st) return st;
+  chunk_hdr h;
+  st = check_header(&p, base_id, c, nbytes, &h);
+  if (st) return st;
+  refine_hdr rh;
+  st = check_refine_header(&p, refine_id, base_id, rc, rbytes, &rh);
+  if (st) return st;
+  if (h.n != n_tokens || h.level != level || rh.n != n_tokens || rh.level != level)
+    return ORC_ERR_ARG;
+  if (get_u32(c + 28) != get_u32(rc + 28)) return ORC_ERR_CORRUPT; /* same chunk */
+  if ((uint64_t)first_token + n_tokens > T_total) return ORC_ERR_SHAPE;
+  const uint32_t S = n_streams(&p);
+  uint32_t *offs = (uint32_t *)malloc(sizeof(uint32_t) * S);
+  uint32_t *roffs = (uint32_t *)malloc(sizeof(uint32_t) * S);
+  orc_stream_offsets(pw, c, nbytes, offs);
+  {
+    uint64_t acc = 0;
+    for (uint32_t m = 0; m < S; ++m) {
+      roffs[m] = (uint32_t)acc;
+      acc += pad8(get_u32(rc + HDR_BYTES + (size_t)REC_BYTES * m + 8));
+    }
+  }
+  int err = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (long uu = 0; uu < (long)n_units(&p); ++uu) {
+    const uint32_t u = (uint32_t)uu;
+    uint32_t m0, nv;
+    unit_span(&p, u, &m0, &nv);
+    int32_t *sym = (int32_t *)malloc(sizeof(int32_t) * (size_t)nv * h.n);
+    int32_t *esym = (int32_t *)malloc(sizeof(int32_t) * (size_t)nv * h.n);
+    uint16_t *vals = (uint16_t *)malloc(sizeof(uint16_t) * h.n);
+    lane_models *mods = (lane_models *)malloc(sizeof(lane_models) * UNIT_LANES);
+    int e = read_unit(&p, fA, fD, c, &h, offs, u, sym, NULL);
+    if (!e) {
+      uint32_t nb[UNIT_LANES];
+      uint64_t sz = 0;
+      for (uint32_t l = 0; l < nv; ++l) {
+        nb[l] = get_u32(rc + HDR_BYTES + (size_t)REC_BYTES * (m0 + l) + 8);
+        sz += pad8(nb[l]);
+      }
+      refine_models(&p, fEA, fED, level, rh.ebits, m0, nv, mods);
+      e = unit_reader_models(&p, mods, nv, h.n, nb, NULL,
+                             rc + HDR_BYTES + (size_t)REC_BYTES * S + roffs[m0], sz / BLOCK, NULL,
+                             esym, NULL);
+    }
+    if (e) {
+#pragma omp critical
+      err = e;
+    } else {
+      for (uint32_t l = 0; l < nv; ++l) {
+        const uint32_t m = m0 + l;
+        const uint8_t *rec = c + HDR_BYTES + (size_t)REC_BYTES * m;
+        const uint8_t *rrec = rc + HDR_BYTES + (size_t)REC_BYTES * m;
+        orc_refine_dequantize(sym + (size_t)l * h.n, esym + (size_t)l * h.n, h.n, p.G,
+                              p.bits[level][third_of(m / (2 * p.C), p.L)], rh.ebits,
+                              get_f32(rec), get_f32(rec + 4), get_f32(rec + 8), get_f32(rrec),
+                              get_f32(rrec + 4), vals);
+        const uint32_t row = m / p.C, ch = m % p.C;
+        uint16_t *dst = out + (size_t)row * T_total * p.C;
+        for (uint32_t j = 0; j < h.n; ++j) dst[(size_t)(first_token + j) * p.C + ch] = vals[j];
+      }
+    }
+    free(sym);
+    free(esym);
+    free(vals);
+    free(mods);
+  }
+  free(offs);
+  free(roffs);
+  return err;
+}
+
+/* The refinement symbols [count][n] of selected streams of a refinement
+ * container (its header checked against the ids), for checks. */
+int orc_decode_refine_symbols(const uint32_t *pw, const uint16_t *fEA, const uint16_t *fED,
+                              uint64_t refine_id, uint64_t base_id, const uint8_t *rc,
+                              uint64_t rbytes, const uint32_t *ids, uint32_t count,
+                              int32_t *esyms) {
+  params p;
+  int st = read_params(pw, &p);
+  if (st) return st;
+  refine_hdr rh;
+  st = check_refine_header(&p, refine_id, base_id, rc, rbytes, &rh);
+  if (st) return st;
+  const uint32_t S = n_streams(&p);
+  const uint32_t ncb = (p.C + UNIT_LANES - 1) / UNIT_LANES;
+  uint32_t *roffs = (uint32_t *)malloc(sizeof(uint32_t) * S);
+  uint64_t acc = 0;
+  for (uint32_t m = 0; m < S; ++m) {
+    roffs[m] = (uint32_t)acc;
+    acc += pad8(get_u32(rc + HDR_BYTES + (size_t)REC_BYTES * m + 8));
+  }
+  int32_t *usym = (int32_t *)malloc(sizeof(int32_t) * (size_t)UNIT_LANES * rh.n);
+  lane_models *mods = (lane_models *)malloc(sizeof(lane_models) * UNIT_LANES);
+  int err = ORC_OK;
+  uint32_t last = 0xFFFFFFFFu;
+  for (uint32_t i = 0; i < count && !err; ++i) {
+    if (ids[i] >= S) {
+      err = ORC_ERR_ARG;
+      break;
+    }
+    const uint32_t m = ids[i];
+    const uint32_t u = (m / p.C) * ncb + (m % p.C) / UNIT_LANES;
+    uint32_t m0, nv;
+    unit_span(&p, u, &m0, &nv);
+    if (u != last) {
+      uint32_t nb[UNIT_LANES];
+      uint64_t sz = 0;
+      for (uint32_t l = 0; l < nv; ++l) {
+        nb[l] = get_u32(rc + HDR_BYTES + (size_t)REC_BYTES * (m0 + l) + 8);
+        sz += pad8(nb[l]);
+      }
+      refine_models(&p, fEA, fED, rh.level, rh.ebits, m0, nv, mods);
+      err = unit_reader_models(&p, mods, nv, rh.n, nb, NULL,
+                               rc + HDR_BYTES + (size_t)REC_BYTES * S + roffs[m0], sz / BLOCK,
+                               NULL, usym, NULL);
+      if (err) break;
+      last = u;
+    }
+    memcpy(esyms + (size_t)i * rh.n, usym + (size_t)(m - m0) * rh.n, sizeof(int32_t) * rh.n);
+  }
+  free(usym);
+  free(mods);
+  free(roffs);
+  return err;
 }
