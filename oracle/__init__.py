@@ -568,6 +568,6 @@ def parse_refine_header(container: np.ndarray) -> dict:
 
 def refine_records(desc: Desc, container: np.ndarray) -> np.ndarray:
     """Refinement stream records as a structured array (Da, Dd, nbytes)."""
-    dt = np.dtype([("Da", "<f4"), ("Dd", "<f4"), ("nbytes", "<u4"), ("zero", "<u4")])
+    dt = np.dtype([("Da", "<f4"), ("Dd", "<f4"), ("zero", "<u4"), ("nbytes", "<u4")])
     S = desc.n_streams
     return np.frombuffer(container[HDR_BYTES:HDR_BYTES + REC_BYTES * S].tobytes(), dt)

@@ -1126,7 +1126,7 @@ void orc_h2f_array(const uint16_t *h, float *out, uint64_t n) {
  *   - refined output: binary16(fma(q, D, xh)), one binary32 rounding then
  *     one binary16 rounding.
  * Its container ("KVCR") has the base container's layout: a 64-byte header,
- * 2LC records {f32 Da, f32 Dd, u32 nbytes, u32 0}, then the payload in the
+ * 2LC records {f32 Da, f32 Dd, u32 0, u32 nbytes}, then the payload in the
  * reference reader's block order (R17). */
 
 #define REFINE_MAX_BITS 6u
@@ -1408,8 +1408,8 @@ int64_t orc_encode_refine_chunk(const uint32_t *pw, const uint16_t *fEA, const u
     uint8_t *rec = out + HDR_BYTES + (size_t)REC_BYTES * m;
     put_f32(rec, side[2 * m]);
     put_f32(rec + 4, side[2 * m + 1]);
-    put_u32(rec + 8, nb[m]);
-    put_u32(rec + 12, 0);
+    put_u32(rec + 8, 0);
+    put_u32(rec + 12, nb[m]);
   }
   uint64_t *uoff = (uint64_t *)malloc(sizeof(uint64_t) * (n_units(&p) + 1));
   uoff[0] = 0;
@@ -1471,7 +1471,7 @@ static int check_refine_header(const params *p, uint64_t refine_id, uint64_t bas
   if (get_u64(c + 32) != refine_id || get_u64(c + 56) != base_id) return ORC_ERR_PROFILE;
   if (HDR_BYTES + (uint64_t)REC_BYTES * S + h->payload != nbytes) return ORC_ERR_CORRUPT;
   uint64_t sum = 0;
-  for (uint32_t m = 0; m < S; ++m) sum += pad8(get_u32(c + HDR_BYTES + (size_t)REC_BYTES * m + 8));
+  for (uint32_t m = 0; m < S; ++m) sum += pad8(get_u32(c + HDR_BYTES + (size_t)REC_BYTES * m + 12));
   if (sum != h->payload) return ORC_ERR_CORRUPT;
   return ORC_OK;
 }
@@ -1509,7 +1509,7 @@ int orc_decode_refined_chunk(const uint32_t *pw, const uint16_t *fA, const uint1
     uint64_t acc = 0;
     for (uint32_t m = 0; m < S; ++m) {
       roffs[m] = (uint32_t)acc;
-      acc += pad8(get_u32(rc + HDR_BYTES + (size_t)REC_BYTES * m + 8));
+      acc += pad8(get_u32(rc + HDR_BYTES + (size_t)REC_BYTES * m + 12));
     }
   }
   int err = ORC_OK;
@@ -1527,7 +1527,7 @@ int orc_decode_refined_chunk(const uint32_t *pw, const uint16_t *fA, const uint1
       uint32_t nb[UNIT_LANES];
       uint64_t sz = 0;
       for (uint32_t l = 0; l < nv; ++l) {
-        nb[l] = get_u32(rc + HDR_BYTES + (size_t)REC_BYTES * (m0 + l) + 8);
+        nb[l] = get_u32(rc + HDR_BYTES + (size_t)REC_BYTES * (m0 + l) + 12);
         sz += pad8(nb[l]);
       }
       refine_models(&p, fEA, fED, level, rh.ebits, m0, nv, mods);
@@ -1580,7 +1580,7 @@ int orc_decode_refine_symbols(const uint32_t *pw, const uint16_t *fEA, const uin
   uint64_t acc = 0;
   for (uint32_t m = 0; m < S; ++m) {
     roffs[m] = (uint32_t)acc;
-    acc += pad8(get_u32(rc + HDR_BYTES + (size_t)REC_BYTES * m + 8));
+    acc += pad8(get_u32(rc + HDR_BYTES + (size_t)REC_BYTES * m + 12));
   }
   int32_t *usym = (int32_t *)malloc(sizeof(int32_t) * (size_t)UNIT_LANES * rh.n);
   lane_models *mods = (lane_models *)malloc(sizeof(lane_models) * UNIT_LANES);
@@ -1599,7 +1599,7 @@ int orc_decode_refine_symbols(const uint32_t *pw, const uint16_t *fEA, const uin
       uint32_t nb[UNIT_LANES];
       uint64_t sz = 0;
       for (uint32_t l = 0; l < nv; ++l) {
-        nb[l] = get_u32(rc + HDR_BYTES + (size_t)REC_BYTES * (m0 + l) + 8);
+        nb[l] = get_u32(rc + HDR_BYTES + (size_t)REC_BYTES * (m0 + l) + 12);
         sz += pad8(nb[l]);
       }
       refine_models(&p, fEA, fED, rh.level, rh.ebits, m0, nv, mods);
