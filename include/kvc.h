@@ -108,6 +108,19 @@ typedef struct {
   uint32_t reserved;             /* 0 */
 } kvc_host_chunk;
 
+/* One chunk's base container and its refinement container, for
+ * kvc_decode_refined. */
+typedef struct {
+  const uint8_t *container;  /* device pointer to the chunk's base container */
+  uint64_t container_bytes;  /* its size in bytes */
+  const uint8_t *refinement; /* device pointer to the chunk's refinement container */
+  uint64_t refinement_bytes; /* its size in bytes */
+  uint32_t first_token;      /* destination token offset in kv_out */
+  uint32_t n_tokens;         /* tokens in the chunk; must equal both headers */
+  uint32_t level;            /* base level; must equal both headers */
+  uint32_t reserved;         /* 0 */
+} kvc_refined_chunk_ref;
+
 /* Library version (major * 10000 + minor * 100 + patch). */
 int kvc_version(void);
 
@@ -240,6 +253,76 @@ kvc_status kvc_decode_index(const kvc_codec_desc *d, const void *tables,
 kvc_status kvc_decode_multi(const kvc_codec_desc *d, const void *tables,
                             const kvc_request_chunk *chunks, uint32_t n_chunks, void *ws,
                             uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream);
+
+/* ------------------------------------------------- incremental refinement */
+/*
+ * Incremental, SVC-like refinement (CacheGen page, 局限与 Future Work:
+ * low-quality KV first, refinement bits after).  The page gives no scheme;
+ * the one here is a second layer per chunk that leaves the base layer (the
+ * chunk's container at its level) untouched: per stream it quantizes the
+ * residual e = x - xh against the base layer's binary32 reconstruction xh
+ * (before its binary16 rounding) with E = refine_bits bits, one scale for
+ * the stream's anchor tokens and one for its other tokens (D = max |e| /
+ * (2^(E-1) - 1), q = rint(e / D) clamped), and range-codes the symbols
+ * against two models per (level, layer, K/V, channel).  A refined value is
+ * binary16(fma(q, D, xh)); it lies within D/2 (plus rounding) of the input,
+ * about 2^(1-E) of the base layer's error.  Supported: refine_bits in [2, 6].
+ */
+
+/* Size in bytes of the refinement tables blob: a 128-byte header, then the
+ * anchor-token cumulative frequencies [n_levels][2LC][64] u16, then those
+ * of the other tokens.  0 if the descriptor is invalid. */
+uint64_t kvc_refine_tables_bytes(const kvc_codec_desc *d);
+
+/* Workspace bytes needed by kvc_profile_refine. */
+uint64_t kvc_refine_profile_ws_bytes(const kvc_codec_desc *d);
+
+/*
+ * Offline profiling of the refinement models on the profiling KV
+ * [L][2][T][C] (chunked like kvc_profile, every level): writes the
+ * refinement tables blob (kvc_refine_tables_bytes) with its 64-bit id,
+ * which also covers `tables`' profile id (the base tables the refinement
+ * goes with).  Device errors: KVC_ERR_NONFINITE.
+ */
+kvc_status kvc_profile_refine(const kvc_codec_desc *d, const void *tables,
+                              const uint16_t *kv_fp16, uint32_t T, uint32_t refine_bits,
+                              void *rtables_out, void *ws, uint64_t ws_bytes, int32_t *dev_status,
+                              hipStream_t stream);
+
+/* Workspace bytes needed by kvc_encode_refine for a T-token context. */
+uint64_t kvc_encode_refine_ws_bytes(const kvc_codec_desc *d, uint32_t T);
+
+/*
+ * The refinement layer of a T-token KV cache: chunk k over its base layer at
+ * chunk_levels[k] (host array), one refinement container ("KVCR") per chunk,
+ * written back to back into `out` (device, out_cap bytes; kvc_encode_bound
+ * is enough), with chunk_offsets_out (device, n_chunks + 1 u64) as for
+ * kvc_encode.  Its payload uses the same block order as the base containers.
+ * Device errors: KVC_ERR_NONFINITE, KVC_ERR_CAPACITY,
+ * KVC_ERR_PROFILE_MISMATCH (rtables made for another descriptor or E).
+ */
+kvc_status kvc_encode_refine(const kvc_codec_desc *d, const void *rtables, uint32_t refine_bits,
+                             const uint16_t *kv_fp16, uint32_t T, const uint8_t *chunk_levels,
+                             uint8_t *out, uint64_t out_cap, uint64_t *chunk_offsets_out,
+                             void *ws, uint64_t ws_bytes, int32_t *dev_status,
+                             hipStream_t stream);
+
+/* Workspace bytes needed by kvc_decode_refined for n_chunks. */
+uint64_t kvc_decode_refined_ws_bytes(const kvc_codec_desc *d, uint32_t n_chunks);
+
+/*
+ * Decode chunks from their base and refinement containers in one launch:
+ * every lane decodes a stream's base layer and its refinement layer token by
+ * token and writes the refined binary16 values into kv_out
+ * [L][2][T_total][C].  Token ranges must be disjoint and inside T_total.
+ * Device errors: those of kvc_decode, plus KVC_ERR_PROFILE_MISMATCH for a
+ * refinement made with other tables, and KVC_ERR_CORRUPT_STREAM for a
+ * refinement of another chunk.
+ */
+kvc_status kvc_decode_refined(const kvc_codec_desc *d, const void *tables, const void *rtables,
+                              uint32_t refine_bits, const kvc_refined_chunk_ref *chunks,
+                              uint32_t n_chunks, uint16_t *kv_out, uint32_t T_total, void *ws,
+                              uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream);
 
 /* --------------------------------------------------------- streamed restore */
 /*

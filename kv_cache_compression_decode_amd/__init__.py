@@ -38,7 +38,9 @@ EXPORTED = (
     "kvc_profile_ws_bytes", "kvc_profile", "kvc_container_bound", "kvc_encode_bound",
     "kvc_encode_ws_bytes", "kvc_encode", "kvc_decode_ws_bytes", "kvc_decode",
     "kvc_decode_index", "kvc_decode_symbols", "kvc_restore_staging_bytes", "kvc_restore",
-    "kvc_plan_stream", "kvc_decode_multi", "kvc_decode_static",
+    "kvc_plan_stream", "kvc_decode_multi", "kvc_decode_static", "kvc_refine_tables_bytes",
+    "kvc_refine_profile_ws_bytes", "kvc_profile_refine", "kvc_encode_refine_ws_bytes",
+    "kvc_encode_refine", "kvc_decode_refined_ws_bytes", "kvc_decode_refined",
 )
 
 
@@ -92,6 +94,20 @@ class RequestChunk(ctypes.Structure):
         ("kv_out", ctypes.c_void_p),
         ("T_total", ctypes.c_uint32),
         ("reserved2", ctypes.c_uint32),
+    ]
+
+
+class RefinedChunkRef(ctypes.Structure):
+    """kvc_refined_chunk_ref: a chunk's base and refinement containers."""
+    _fields_ = [
+        ("container", ctypes.c_void_p),
+        ("container_bytes", ctypes.c_uint64),
+        ("refinement", ctypes.c_void_p),
+        ("refinement_bytes", ctypes.c_uint64),
+        ("first_token", ctypes.c_uint32),
+        ("n_tokens", ctypes.c_uint32),
+        ("level", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
     ]
 
 
@@ -168,6 +184,18 @@ def lib():
     L.kvc_decode_multi.restype = ctypes.c_int
     L.kvc_decode_static.argtypes = [dp, vp, vp, u32, vp, u32, vp, vp]
     L.kvc_decode_static.restype = ctypes.c_int
+    for name in ("kvc_refine_tables_bytes", "kvc_refine_profile_ws_bytes"):
+        getattr(L, name).argtypes = [dp]
+        getattr(L, name).restype = u64
+    for name in ("kvc_encode_refine_ws_bytes", "kvc_decode_refined_ws_bytes"):
+        getattr(L, name).argtypes = [dp, u32]
+        getattr(L, name).restype = u64
+    L.kvc_profile_refine.argtypes = [dp, vp, vp, u32, u32, vp, vp, u64, vp, vp]
+    L.kvc_profile_refine.restype = ctypes.c_int
+    L.kvc_encode_refine.argtypes = [dp, vp, u32, vp, u32, vp, vp, u64, vp, vp, u64, vp, vp]
+    L.kvc_encode_refine.restype = ctypes.c_int
+    L.kvc_decode_refined.argtypes = [dp, vp, vp, u32, vp, u32, vp, u32, vp, u64, vp, vp]
+    L.kvc_decode_refined.restype = ctypes.c_int
     L.kvc_plan_stream.argtypes = [vp, u32, u32, vp, u32, ctypes.c_double, ctypes.c_double, vp, vp]
     L.kvc_plan_stream.restype = ctypes.c_int
     _lib = L
@@ -596,3 +624,102 @@ def decode_multi(desc: CodecDesc, tables: torch.Tensor, chunks: Sequence[Request
         wsp = DecodeWorkspace(desc, len(chunks), tables.device)
     decode_multi_async(desc, tables, chunks, wsp, stream)
     read_status(wsp.status, "kvc_decode_multi", stream)
+
+
+# ------------------------------------------------------ incremental refinement
+def refine_tables_bytes(desc: CodecDesc) -> int:
+    return int(lib().kvc_refine_tables_bytes(ctypes.byref(desc)))
+
+
+def profile_refine(desc: CodecDesc, tables: torch.Tensor, kv_prof: torch.Tensor, refine_bits: int,
+                   stream=None, check: bool = True) -> torch.Tensor:
+    """Profile the refinement models (refine_bits bits) on kv_prof
+    [L][2][T][C] for the base `tables`; returns the refinement tables blob."""
+    L = lib()
+    nb = refine_tables_bytes(desc)
+    if nb == 0:
+        raise KvcError(ERR_INVALID_ARG, "profile_refine")
+    rtables = torch.empty(nb, dtype=torch.uint8, device=kv_prof.device)
+    wsb = int(L.kvc_refine_profile_ws_bytes(ctypes.byref(desc)))
+    ws = torch.empty(wsb, dtype=torch.uint8, device=kv_prof.device)
+    st = _dev_status(kv_prof.device)
+    _check(L.kvc_profile_refine(ctypes.byref(desc), tables.data_ptr(), _kv_ptr(kv_prof),
+                                kv_prof.shape[2], refine_bits, rtables.data_ptr(), ws.data_ptr(),
+                                wsb, st.data_ptr(), _stream(stream)), "kvc_profile_refine")
+    if check:
+        read_status(st, "kvc_profile_refine", stream)
+    return rtables
+
+
+def refine_id(rtables: torch.Tensor) -> int:
+    return int(rtables[48:56].cpu().numpy().view("<u8")[0])
+
+
+def encode_refine(desc: CodecDesc, rtables: torch.Tensor, refine_bits: int, kv: torch.Tensor,
+                  levels: Sequence[int], stream=None) -> Encoded:
+    """The refinement containers of kv [L][2][T][C] over base layers at
+    `levels` (one per chunk)."""
+    L = lib()
+    T = kv.shape[2]
+    n_chunks = (T + desc.chunk_tokens - 1) // desc.chunk_tokens
+    if len(levels) != n_chunks:
+        raise ValueError(f"{n_chunks} chunk levels expected")
+    wsb = int(L.kvc_encode_refine_ws_bytes(ctypes.byref(desc), T))
+    cap = int(L.kvc_encode_bound(ctypes.byref(desc), T))
+    ws = torch.empty(wsb, dtype=torch.uint8, device=kv.device)
+    out = torch.empty(cap, dtype=torch.uint8, device=kv.device)
+    offsets = torch.empty(n_chunks + 1, dtype=torch.int64, device=kv.device)
+    st = _dev_status(kv.device)
+    lv = (ctypes.c_uint8 * max(len(levels), 1))(*[int(x) for x in levels])
+    _check(L.kvc_encode_refine(ctypes.byref(desc), rtables.data_ptr(), refine_bits, _kv_ptr(kv), T,
+                               lv, out.data_ptr(), cap, offsets.data_ptr(), ws.data_ptr(), wsb,
+                               st.data_ptr(), _stream(stream)), "kvc_encode_refine")
+    read_status(st, "kvc_encode_refine", stream)
+    offs = [int(x) for x in offsets.cpu().tolist()]
+    ntok = [min(desc.chunk_tokens, T - k * desc.chunk_tokens) for k in range(n_chunks)]
+    return Encoded(out[: offs[-1]].clone(), offs, [int(x) for x in levels], ntok,
+                   desc.chunk_tokens)
+
+
+def refined_chunk_refs(enc: Encoded, renc: Encoded, chunks: Optional[Sequence[int]] = None,
+                       first_tokens: Optional[Sequence[int]] = None) -> List[RefinedChunkRef]:
+    """RefinedChunkRefs pairing each chunk's base container (enc) with its
+    refinement container (renc); by default each goes back to its own
+    token range."""
+    ks = list(range(enc.n_chunks)) if chunks is None else list(chunks)
+    out = []
+    for i, k in enumerate(ks):
+        r = RefinedChunkRef()
+        r.container = enc.blob.data_ptr() + enc.offsets[k]
+        r.container_bytes = enc.offsets[k + 1] - enc.offsets[k]
+        r.refinement = renc.blob.data_ptr() + renc.offsets[k]
+        r.refinement_bytes = renc.offsets[k + 1] - renc.offsets[k]
+        r.first_token = k * enc.chunk_tokens if first_tokens is None else int(first_tokens[i])
+        r.n_tokens = enc.n_tokens[k]
+        r.level = enc.levels[k]
+        r.reserved = 0
+        out.append(r)
+    return out
+
+
+def decode_refined(desc: CodecDesc, tables: torch.Tensor, rtables: torch.Tensor, refine_bits: int,
+                   refs: Sequence[RefinedChunkRef], T_total: int,
+                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode base + refinement layers into the KV cache [L][2][T_total][C]
+    (int16 bit patterns of binary16)."""
+    L = lib()
+    dev = tables.device
+    if out is None:
+        out = torch.zeros((desc.n_layers, 2, T_total, desc.n_channels), dtype=torch.int16, device=dev)
+    wsb = int(L.kvc_decode_refined_ws_bytes(ctypes.byref(desc), len(refs)))
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    st = _dev_status(dev)
+    arr = (RefinedChunkRef * max(len(refs), 1))()
+    for i, r in enumerate(refs):
+        arr[i] = r
+    _check(L.kvc_decode_refined(ctypes.byref(desc), tables.data_ptr(), rtables.data_ptr(),
+                                refine_bits, arr, len(refs), _kv_ptr(out), out.shape[2],
+                                ws.data_ptr(), wsb, st.data_ptr(), _stream(stream)),
+           "kvc_decode_refined")
+    read_status(st, "kvc_decode_refined", stream)
+    return out

@@ -35,6 +35,27 @@ size_t encode_emit_lds_bytes(uint32_t levels, uint32_t waves);
 hipError_t launch_profile(const Desc &d, const uint16_t *kv, uint32_t T, uint8_t *tables,
                           uint32_t *counts, uint64_t *model_hash, uint64_t *row_hash,
                           int32_t *status, hipStream_t stream);
+hipError_t launch_profile_refine(const Desc &d, uint32_t ebits, const uint16_t *kv, uint32_t T,
+                                 const uint8_t *base_tables, uint8_t *rtables, uint32_t *counts,
+                                 uint64_t *model_hash, uint64_t *row_hash, int32_t *status,
+                                 hipStream_t stream);
+size_t refine_count_lds_bytes(const Desc &d);
+uint32_t refine_emit_lane_bytes(uint32_t chunk);
+hipError_t launch_encode_refine(const Desc &d, uint32_t ebits, const uint8_t *rtables,
+                                const uint16_t *kv, uint32_t T, const ChunkInfo *dev_chunks,
+                                uint32_t n_chunks, uint32_t stat_blocks, uint32_t emit_blocks,
+                                float *side, uint8_t *records, uint64_t *row_sums,
+                                uint32_t *flags, uint32_t *offsets, uint8_t *valid,
+                                uint64_t *payload, uint64_t *chunk_off_ws, uint32_t *fits,
+                                uint32_t *spare, uint8_t *scratch, uint8_t *out, uint64_t out_cap,
+                                uint64_t *chunk_off_out, int32_t *status, hipStream_t stream);
+size_t decode_refined_lds_bytes(uint32_t waves);
+hipError_t launch_decode_refined(const Desc &d, uint32_t ebits, const ChunkInfo *dev_chunks,
+                                 const ChunkInfo *dev_rchunks, const DecodeGroup *groups,
+                                 uint32_t n_groups, uint32_t waves, const uint8_t *valid,
+                                 const uint8_t *rvalid, const uint32_t *offsets,
+                                 const uint32_t *roffsets, const uint8_t *tables,
+                                 const uint8_t *rtables, int32_t *status, hipStream_t stream);
 }  // namespace kvc
 
 using namespace kvc;
@@ -285,6 +306,49 @@ struct RestoreEvents {
   }
 };
 
+// ---------------------------------------------------------- refinement
+constexpr uint32_t kRefineMinBits = 2, kRefineMaxBits = 6;
+bool refine_bits_ok(uint32_t e) { return e >= kRefineMinBits && e <= kRefineMaxBits; }
+
+// Refinement encode: one wave per (chunk, unit) item; the emit waves share
+// at most this much scratch.
+constexpr uint64_t kRefineScratchCap = 256ull << 20;
+uint32_t refine_items(const Desc &d, uint32_t K) {
+  return K * 2u * d.L * ((d.C + kWave - 1) / kWave);
+}
+uint32_t refine_emit_blocks(const Desc &d, uint32_t K) {
+  const uint64_t per = (uint64_t)kWave * refine_emit_lane_bytes(d.chunk);
+  const uint64_t cap = std::max<uint64_t>(1, kRefineScratchCap / per);
+  return (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>({cap, 2048, refine_items(d, K)}));
+}
+uint32_t refine_stat_blocks(const Desc &d, uint32_t K) {
+  return std::max<uint32_t>(1, std::min<uint32_t>(4096, refine_items(d, K)));
+}
+
+struct RefineEncodeWs {
+  uint64_t chunks, rows, hdr, valid, payload, offsets, records, side, chunk_off, fits, spare,
+      scratch, total;
+};
+RefineEncodeWs refine_encode_ws(const Desc &d, uint32_t K) {
+  const uint64_t S = n_streams(d);
+  RefineEncodeWs w;
+  w.chunks = 0;
+  w.rows = align256((uint64_t)K * sizeof(ChunkInfo));
+  w.hdr = align256(w.rows + (uint64_t)K * 2 * d.L * 8);
+  w.valid = align256(w.hdr + (uint64_t)K * 4);
+  w.payload = align256(w.valid + K);
+  w.offsets = align256(w.payload + (uint64_t)K * 8);
+  w.records = align256(w.offsets + (uint64_t)K * S * 4);
+  w.side = align256(w.records + (uint64_t)K * S * kRecBytes);
+  w.chunk_off = align256(w.side + (uint64_t)K * S * 16);
+  w.fits = align256(w.chunk_off + (uint64_t)(K + 1) * 8);
+  w.spare = align256(w.fits + 4);
+  w.scratch = align256(w.spare + 4);
+  w.total = align256(w.scratch + (uint64_t)refine_emit_blocks(d, K) * kWave *
+                                     refine_emit_lane_bytes(d.chunk));
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -494,6 +558,223 @@ kvc_status kvc_decode_multi(const kvc_codec_desc *d, const void *tables,
   }
   return decode_chunks(d, tables, v.data(), n_chunks, ws, ws_bytes, dev_status, stream, 0,
                        nullptr);
+}
+
+// ---------------------------------------------------------- refinement
+uint64_t kvc_refine_tables_bytes(const kvc_codec_desc *dd) {
+  if (!desc_ok(dd)) return 0;
+  const uint64_t S = 2ull * dd->n_layers * dd->n_channels;
+  return kTablesHdr + 2ull * dd->n_levels * S * kDeltaStride * 2;
+}
+
+uint64_t kvc_refine_profile_ws_bytes(const kvc_codec_desc *dd) {
+  if (!desc_ok(dd)) return 0;
+  const uint64_t S = 2ull * dd->n_layers * dd->n_channels;
+  const uint64_t counts = S * 2ull * dd->n_levels * kDeltaStride * 4;
+  return align256(counts) + align256(S * 8) + align256(2ull * dd->n_layers * 8);
+}
+
+kvc_status kvc_profile_refine(const kvc_codec_desc *dd, const void *tables,
+                              const uint16_t *kv_fp16, uint32_t T, uint32_t refine_bits,
+                              void *rtables_out, void *ws, uint64_t ws_bytes, int32_t *dev_status,
+                              hipStream_t stream) {
+  if (!desc_ok(dd) || !refine_bits_ok(refine_bits)) return KVC_ERR_INVALID_ARG;
+  if (!tables || !aligned(tables, 16) || !kv_fp16 || !aligned(kv_fp16, 2) || !rtables_out ||
+      !aligned(rtables_out, 16) || !ws || !aligned(ws, 256) || !dev_status ||
+      !aligned(dev_status, 4))
+    return KVC_ERR_INVALID_ARG;
+  if (T < 1) return KVC_ERR_SHAPE;
+  if (ws_bytes < kvc_refine_profile_ws_bytes(dd)) return KVC_ERR_CAPACITY;
+  const Desc d = to_desc(dd);
+  const uint64_t S = n_streams(d);
+  if (refine_count_lds_bytes(d) > 64 * 1024) return KVC_ERR_INVALID_ARG;
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  const uint64_t counts_bytes = S * 2ull * d.nlev * kDeltaStride * 4;
+  uint32_t *counts = reinterpret_cast<uint32_t *>(base);
+  uint64_t *model_hash = reinterpret_cast<uint64_t *>(base + align256(counts_bytes));
+  uint64_t *row_hash = reinterpret_cast<uint64_t *>(base + align256(counts_bytes) + align256(S * 8));
+  hipError_t e = launch_reset_status(dev_status, stream);
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  e = launch_profile_refine(d, refine_bits, kv_fp16, T, static_cast<const uint8_t *>(tables),
+                            static_cast<uint8_t *>(rtables_out), counts, model_hash, row_hash,
+                            dev_status, stream);
+  return hip_status(e);
+}
+
+uint64_t kvc_encode_refine_ws_bytes(const kvc_codec_desc *dd, uint32_t T) {
+  if (!desc_ok(dd)) return 0;
+  const Desc d = to_desc(dd);
+  const uint32_t K = (uint32_t)((T + (uint64_t)d.chunk - 1) / d.chunk);
+  return refine_encode_ws(d, K).total;
+}
+
+kvc_status kvc_encode_refine(const kvc_codec_desc *dd, const void *rtables, uint32_t refine_bits,
+                             const uint16_t *kv_fp16, uint32_t T, const uint8_t *chunk_levels,
+                             uint8_t *out, uint64_t out_cap, uint64_t *chunk_offsets_out,
+                             void *ws, uint64_t ws_bytes, int32_t *dev_status,
+                             hipStream_t stream) {
+  if (!desc_ok(dd) || !refine_bits_ok(refine_bits)) return KVC_ERR_INVALID_ARG;
+  const Desc d = to_desc(dd);
+  if (!rtables || !aligned(rtables, 16) || !kv_fp16 || !aligned(kv_fp16, 2) || !chunk_levels ||
+      !out || !aligned(out, 4) || !chunk_offsets_out || !aligned(chunk_offsets_out, 8) || !ws ||
+      !aligned(ws, 256) || !dev_status || !aligned(dev_status, 4))
+    return KVC_ERR_INVALID_ARG;
+  if (T < 1) return KVC_ERR_SHAPE;
+  const uint64_t K64 = (T + (uint64_t)d.chunk - 1) / d.chunk;
+  if (K64 > 65535) return KVC_ERR_SHAPE;
+  const uint32_t K = (uint32_t)K64;
+  const uint64_t S = n_streams(d);
+  if (S * pad8(4ull + 2ull * d.chunk) > 0xFFFFFFFFull) return KVC_ERR_SHAPE;
+  const RefineEncodeWs w = refine_encode_ws(d, K);
+  if (ws_bytes < w.total) return KVC_ERR_CAPACITY;
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  std::vector<ChunkInfo> info(K);
+  for (uint32_t k = 0; k < K; ++k) {
+    if (chunk_levels[k] >= d.nlev) return KVC_ERR_INVALID_ARG;
+    const uint64_t t0 = (uint64_t)k * d.chunk;
+    info[k].cont = nullptr;
+    info[k].records = base + w.records + (uint64_t)k * S * kRecBytes;
+    info[k].cont_bytes = 0;
+    info[k].first_token = (uint32_t)t0;
+    info[k].n_tokens = (uint32_t)std::min<uint64_t>(d.chunk, T - t0);
+    info[k].level = chunk_levels[k];
+    info[k].out_tokens = 0;
+    info[k].out = nullptr;
+  }
+  hipError_t e = launch_reset_status(dev_status, stream);
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  ChunkInfo *dch = reinterpret_cast<ChunkInfo *>(base + w.chunks);
+  e = launch_load_chunks(info.data(), K, dch, reinterpret_cast<uint32_t *>(base + w.hdr), stream);
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  e = launch_encode_refine(d, refine_bits, static_cast<const uint8_t *>(rtables), kv_fp16, T, dch,
+                           K, refine_stat_blocks(d, K), refine_emit_blocks(d, K),
+                           reinterpret_cast<float *>(base + w.side), base + w.records,
+                           reinterpret_cast<uint64_t *>(base + w.rows),
+                           reinterpret_cast<uint32_t *>(base + w.hdr),
+                           reinterpret_cast<uint32_t *>(base + w.offsets), base + w.valid,
+                           reinterpret_cast<uint64_t *>(base + w.payload),
+                           reinterpret_cast<uint64_t *>(base + w.chunk_off),
+                           reinterpret_cast<uint32_t *>(base + w.fits),
+                           reinterpret_cast<uint32_t *>(base + w.spare), base + w.scratch, out,
+                           out_cap, chunk_offsets_out, dev_status, stream);
+  return hip_status(e);
+}
+
+uint64_t kvc_decode_refined_ws_bytes(const kvc_codec_desc *dd, uint32_t n_chunks) {
+  if (!desc_ok(dd)) return 0;
+  return 2 * ws_layout(to_desc(dd), n_chunks, false).total;
+}
+
+kvc_status kvc_decode_refined(const kvc_codec_desc *dd, const void *tables, const void *rtables,
+                              uint32_t refine_bits, const kvc_refined_chunk_ref *chunks,
+                              uint32_t n_chunks, uint16_t *kv_out, uint32_t T_total, void *ws,
+                              uint64_t ws_bytes, int32_t *dev_status, hipStream_t stream) {
+  if (!desc_ok(dd) || !refine_bits_ok(refine_bits)) return KVC_ERR_INVALID_ARG;
+  const Desc d = to_desc(dd);
+  if (!tables || !aligned(tables, 16) || !rtables || !aligned(rtables, 16) || !dev_status ||
+      !aligned(dev_status, 4))
+    return KVC_ERR_INVALID_ARG;
+  if (n_chunks > 65535) return KVC_ERR_SHAPE;
+  if (n_chunks && (!chunks || !kv_out || !aligned(kv_out, 2))) return KVC_ERR_INVALID_ARG;
+  const WsLayout w = ws_layout(d, n_chunks, false);
+  if (n_chunks && (!ws || !aligned(ws, 256))) return KVC_ERR_INVALID_ARG;
+  if (ws_bytes < 2 * w.total) return KVC_ERR_CAPACITY;
+  const uint64_t S = n_streams(d);
+  std::vector<std::pair<ChunkInfo, ChunkInfo>> info(n_chunks);
+  std::vector<std::pair<uint32_t, uint32_t>> ranges(n_chunks);
+  for (uint32_t k = 0; k < n_chunks; ++k) {
+    const kvc_refined_chunk_ref &c = chunks[k];
+    if (!c.container || !aligned(c.container, 4) || !c.refinement || !aligned(c.refinement, 4))
+      return KVC_ERR_INVALID_ARG;
+    if (c.level >= d.nlev || c.reserved != 0) return KVC_ERR_INVALID_ARG;
+    if (c.n_tokens < 1 || c.n_tokens > d.chunk) return KVC_ERR_SHAPE;
+    if ((uint64_t)c.first_token + c.n_tokens > T_total) return KVC_ERR_SHAPE;
+    for (const uint64_t nb : {c.container_bytes, c.refinement_bytes})
+      if (nb < kHdrBytes + kRecBytes * S || nb > 0xFFFFFFFFull) return KVC_ERR_SHAPE;
+    ChunkInfo b{}, r{};
+    b.cont = c.container;
+    b.records = c.container + kHdrBytes;
+    b.cont_bytes = c.container_bytes;
+    r.cont = c.refinement;
+    r.records = c.refinement + kHdrBytes;
+    r.cont_bytes = c.refinement_bytes;
+    b.first_token = r.first_token = c.first_token;
+    b.n_tokens = r.n_tokens = c.n_tokens;
+    b.level = r.level = c.level;
+    b.out_tokens = r.out_tokens = T_total;
+    b.out = r.out = kv_out;
+    info[k] = {b, r};
+    ranges[k] = {c.first_token, c.first_token + c.n_tokens};
+  }
+  std::sort(ranges.begin(), ranges.end());
+  for (uint32_t k = 1; k < n_chunks; ++k)
+    if (ranges[k].first < ranges[k - 1].second) return KVC_ERR_SHAPE;
+  // groups hold chunks of one level: the chunk table is ordered by level and
+  // each level's chunks split into groups of at most wmax * kMaxRounds
+  std::stable_sort(info.begin(), info.end(),
+                   [](const std::pair<ChunkInfo, ChunkInfo> &a,
+                      const std::pair<ChunkInfo, ChunkInfo> &b) { return a.first.level < b.first.level; });
+  constexpr uint32_t kMaxRounds = 4;
+  constexpr size_t kRefinedLdsBudget = 160u * 1024u;
+  uint32_t wmax = 1;
+  for (uint32_t wv = kDecodeMaxWaves; wv >= 1; --wv)
+    if (decode_refined_lds_bytes(wv) <= kRefinedLdsBudget) {
+      wmax = wv;
+      break;
+    }
+  std::vector<DecodeGroup> groups;
+  uint32_t waves = 1;
+  for (uint32_t a = 0; a < n_chunks;) {
+    uint32_t b = a;
+    while (b < n_chunks && info[b].first.level == info[a].first.level) ++b;
+    const uint32_t cnt = b - a;
+    const uint32_t ng = (cnt + wmax * kMaxRounds - 1) / (wmax * kMaxRounds);
+    for (uint32_t gi = 0; gi < ng; ++gi) {
+      DecodeGroup g{};
+      g.start = a + (uint32_t)((uint64_t)cnt * gi / ng);
+      g.count = a + (uint32_t)((uint64_t)cnt * (gi + 1) / ng) - g.start;
+      g.level = 1u << info[a].first.level;
+      waves = std::max<uint32_t>(waves, std::min<uint32_t>(wmax, g.count));
+      groups.push_back(g);
+    }
+    a = b;
+  }
+  hipError_t e = launch_reset_status(dev_status, stream);
+  if (e != hipSuccess || n_chunks == 0) return hip_status(e);
+  std::vector<ChunkInfo> bi(n_chunks), ri(n_chunks);
+  for (uint32_t k = 0; k < n_chunks; ++k) {
+    bi[k] = info[k].first;
+    ri[k] = info[k].second;
+  }
+  uint8_t *wb = static_cast<uint8_t *>(ws), *wr = wb + w.total;
+  ChunkInfo *dbch = reinterpret_cast<ChunkInfo *>(wb + w.chunks);
+  ChunkInfo *drch = reinterpret_cast<ChunkInfo *>(wr + w.chunks);
+  e = launch_load_chunks(bi.data(), n_chunks, dbch, reinterpret_cast<uint32_t *>(wb + w.hdr), stream);
+  if (e == hipSuccess)
+    e = launch_load_chunks(ri.data(), n_chunks, drch, reinterpret_cast<uint32_t *>(wr + w.hdr), stream);
+  if (e == hipSuccess)
+    e = launch_index(d, dbch, n_chunks, reinterpret_cast<uint64_t *>(wb + w.rows),
+                     reinterpret_cast<uint32_t *>(wb + w.hdr),
+                     reinterpret_cast<uint32_t *>(wb + w.offsets), wb + w.valid,
+                     reinterpret_cast<uint64_t *>(wb + w.payload),
+                     static_cast<const uint8_t *>(tables), 1, dev_status, stream);
+  if (e == hipSuccess)
+    e = launch_index(d, drch, n_chunks, reinterpret_cast<uint64_t *>(wr + w.rows),
+                     reinterpret_cast<uint32_t *>(wr + w.hdr),
+                     reinterpret_cast<uint32_t *>(wr + w.offsets), wr + w.valid,
+                     reinterpret_cast<uint64_t *>(wr + w.payload),
+                     static_cast<const uint8_t *>(rtables), 2, dev_status, stream);
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  DecodeGroup *dgr = reinterpret_cast<DecodeGroup *>(wb + w.groups);
+  e = launch_load_groups(groups.data(), (uint32_t)groups.size(), dgr, stream);
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  e = launch_decode_refined(d, refine_bits, dbch, drch, dgr, (uint32_t)groups.size(), waves,
+                            wb + w.valid, wr + w.valid,
+                            reinterpret_cast<uint32_t *>(wb + w.offsets),
+                            reinterpret_cast<uint32_t *>(wr + w.offsets),
+                            static_cast<const uint8_t *>(tables),
+                            static_cast<const uint8_t *>(rtables), dev_status, stream);
+  return hip_status(e);
 }
 
 uint64_t kvc_restore_staging_bytes(const kvc_host_chunk *chunks, uint32_t n_chunks,

@@ -166,7 +166,8 @@ struct Stream {
 // others load their held block again.  No lane keeps its old register value
 // across the branch, so nothing has to wait for the load before the block is
 // stored, a group later.
-__device__ inline void advance(Stream &s, Source &src, bool need) {
+template <class St>
+__device__ inline void advance(St &s, Source &src, bool need) {
   const uint64_t need_mask = __builtin_amdgcn_ballot_w64(need);
   if (need_mask == 0) return;
   // the requesting lanes: those that need and still have a block to ask for
@@ -182,12 +183,14 @@ __device__ inline void advance(Stream &s, Source &src, bool need) {
   src.cnt += (uint32_t)__builtin_popcountll(mask);
 }
 // At a group's anchor: a ring with at most 8 bytes left takes its block.
-__device__ inline void refill(Stream &s, Source &src) {
+template <class St>
+__device__ inline void refill(St &s, Source &src) {
   advance(s, src, (int32_t)(s.nrpos - s.nwlim) <= 48);
 }
 // Before every other token: a ring with fewer than 2 bytes left takes its
 // block (rare).
-__device__ inline void ensure(Stream &s, Source &src) { advance(s, src, s.nrpos < s.nwlim); }
+template <class St>
+__device__ inline void ensure(St &s, Source &src) { advance(s, src, s.nrpos < s.nwlim); }
 
 // Keeps the instruction scheduler from moving code across this point: each
 // binary-search probe is read, then compared, with nothing hoisted between.
@@ -206,7 +209,7 @@ struct AnchorTop {
 // [0, 2^kSteps), and delta entries past an alphabet are staged as 2^15 so
 // that no product can wrap and a valid code never selects them.  Returns the
 // value to store (binary16 bits, or the symbol).
-template <bool kSymbols, bool kAnchor, uint32_t kSteps>
+template <bool kSymbols, bool kAnchor, uint32_t kSteps, bool kF32 = false>
 __device__ inline uint32_t step(Stream &x, const AnchorTop &at, uint64_t &lost_anchor) {
   // the next four stream bytes, most significant first
   const lds_u32 *rd =
@@ -256,6 +259,15 @@ __device__ inline uint32_t step(Stream &x, const AnchorTop &at, uint64_t &lost_a
   x.nrpos -= sh;
   if constexpr (kSymbols) {
     return kAnchor ? (uint32_t)xq >> 7 : (uint32_t)((xq >> 7) + x.M);
+  } else if constexpr (kF32) {
+    // the reconstruction in binary32, before its binary16 rounding (the
+    // value the refinement layer refines)
+    if constexpr (kAnchor) {
+      x.ahat = __builtin_fmaf((float)xq, x.sa7, x.lo);
+      return __builtin_bit_cast(uint32_t, x.ahat);
+    } else {
+      return __builtin_bit_cast(uint32_t, __builtin_fmaf((float)xq, x.dl7, x.ahat));
+    }
   } else {
     // 128 q is exact in binary32 and (128 q)(dl / 128) = q dl exactly, so
     // this is the single rounding of fma(q, dl, ahat)
@@ -347,6 +359,90 @@ __device__ inline void stream_dispatch(uint32_t steps, Stream &s, const AnchorTo
     case 4: stream_run<kSymbols, 4>(s, at, src, ob, ld, loff, n, G, lost_anchor); break;
     case 5: stream_run<kSymbols, 5>(s, at, src, ob, ld, loff, n, G, lost_anchor); break;
     default: stream_run<kSymbols, 6>(s, at, src, ob, ld, loff, n, G, lost_anchor); break;
+  }
+}
+
+// ------------------------------------------------------------ refinement
+// A lane's refinement stream (the second layer of its chunk): the same byte
+// ring and block source as a base stream, and its two models (anchor tokens,
+// other tokens), both E-bit alphabets staged like the delta models.
+struct RStream {
+  lds_u32 *ring;
+  uint32_t code, range;
+  uint32_t nrpos, nwlim;
+  u32x2 held;
+  uint32_t rem, hoff, wbase, wsum;
+  uint32_t tab[2];   // LDS byte address of this lane's row 0: anchor tokens, other tokens
+  uint32_t tabM[2];  // tab + Me rows: (addr - tabM) is 128 q
+  float D7[2];       // Da / 128, Dd / 128 (exact: D is 0 or above 2^-100)
+
+  // as Stream::put_block: the held block, byte-reversed, into the free half
+  __device__ inline void put_block() {
+    lds_u32 *w = (lds_u32 *)(uintptr_t)wbase;
+    const uint32_t lo = __builtin_bswap32(held[0]);
+    w[0] = lo;
+    w[4] = lo;
+    w[3] = __builtin_bswap32(held[1]);
+    wbase = wsum - wbase;
+    nwlim -= 64;
+  }
+};
+
+// One token of a lane's refinement stream: the symbol q + Me (binary search
+// over 2^E entries, `top` = 2^(E-1) rows), then binary16(fma(q, D, xh)).
+template <bool kAnchor>
+__device__ inline uint32_t rstep(RStream &e, uint32_t top, float xh) {
+  const lds_u32 *rd =
+      (const lds_u32 *)(uintptr_t)(lds_addr(e.ring) + (dword_of(e.nrpos) << 2));
+  const uint32_t in = __builtin_amdgcn_alignbit(rd[1], rd[0], e.nrpos);
+  const uint32_t r = e.range >> kPrec;
+  constexpr uint32_t kind = kAnchor ? 0 : 1;
+  uint32_t a = e.tab[kind];
+  for (uint32_t sz = top * kRowBytes; sz >= kRowBytes; sz >>= 1) {
+    const uint32_t probe = lds_read_u16(a + sz);
+    if (__umul24(r, probe) <= e.code) a += sz;
+  }
+  const uint32_t cs = lds_read_u16(a);
+  const uint32_t cn = lds_read_u16(a + kRowBytes);
+  const int32_t xq = (int32_t)(a - e.tabM[kind]);
+  e.code -= __umul24(r, cs);
+  const uint32_t range = __umul24(r, cn - cs);
+  const uint32_t sh = ffbh(range) & 24u;
+  e.range = range << sh;
+  e.code = (uint32_t)((((uint64_t)e.code << 32) | in) << sh >> 32);
+  e.nrpos -= sh;
+  return f2h(__builtin_fmaf((float)xq, e.D7[kind], xh));
+}
+
+// Every token of a lane's base and refinement streams, group by group; the
+// two streams follow the same reading rule, each over its own container.
+template <uint32_t kSteps>
+__device__ inline void refined_run(Stream &s, RStream &e, const AnchorTop &at, Source &src,
+                                   Source &rsrc, gbyte *ob, uint64_t ld, uint32_t &loff,
+                                   uint32_t n, uint32_t G, uint32_t etop, uint64_t &lost_anchor) {
+  for (uint32_t j = 0; j < n;) {
+    refill(s, src);
+    refill(e, rsrc);
+    {
+      const float xh =
+          __builtin_bit_cast(float, step<false, true, 8, true>(s, at, lost_anchor));
+      put<false>(ob, loff, rstep<true>(e, etop, xh));
+      ob += ld;
+    }
+    const uint32_t jend = j + G < n ? j + G : n;
+    const uint32_t count = jend - j - 1;
+    for (uint32_t i = 0; i < count; ++i) {
+      // the first three deltas after an anchor's refill cannot run low
+      if (i >= 3) {
+        ensure(s, src);
+        ensure(e, rsrc);
+      }
+      const float xh =
+          __builtin_bit_cast(float, step<false, false, kSteps, true>(s, at, lost_anchor));
+      put<false>(ob, loff, rstep<false>(e, etop, xh));
+      ob += ld;
+    }
+    j = jend;
   }
 }
 
@@ -508,6 +604,243 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
     if (s.range == 0 || s.nrpos != 0u - 8 * nbytes || s.rem != 0 || ((lost_anchor >> lane) & 1))
       set_status(status, KVC_ERR_CORRUPT_STREAM);
   }
+}
+
+// Decode of base and refinement layers in one launch: the same work
+// decomposition as k_decode; each lane decodes its base stream and its
+// refinement stream token by token and stores binary16(fma(q, D, xh)).
+// Groups hold chunks of one level (the host forms them so), whose base delta
+// models and two refinement models are staged beside the anchor models.
+__global__ __launch_bounds__(kMaxWaves *kWave) void k_decode_refined(
+    Desc d, uint32_t ebits, const ChunkInfo *__restrict__ ci, const ChunkInfo *__restrict__ rci,
+    const DecodeGroup *__restrict__ groups, uint32_t n_groups, uint32_t n_units,
+    const uint8_t *__restrict__ valid, const uint8_t *__restrict__ rvalid,
+    const uint32_t *__restrict__ offsets, const uint32_t *__restrict__ roffsets,
+    const uint8_t *__restrict__ tables, const uint8_t *__restrict__ rtables, int32_t *status) {
+  const uint32_t id = blockIdx.x;
+  const uint32_t local = id / kXcds;
+  const uint32_t unit = (local / n_groups) * kXcds + id % kXcds;
+  const uint32_t grp = local % n_groups;
+  if (unit >= n_units) return;
+  const uint32_t ncb = (d.C + kWave - 1) / kWave;
+  const uint32_t row = unit / ncb, cb = unit % ncb;
+  const uint32_t c0 = cb * kWave;
+  const uint32_t nv = d.C - c0 < kWave ? d.C - c0 : kWave;
+  const uint32_t m0 = row * d.C + c0;
+  const uint32_t S = n_streams(d);
+  const DecodeGroup gp = groups[grp];
+  const uint32_t lv = 31u - __builtin_clz(gp.level);  // the group's one level
+  const uint32_t n_waves = blockDim.x / kWave;
+  // the refinement tables were made for this descriptor, E and these base
+  // tables (their base id is the base tables' profile id)
+  if (!refine_tables_match(d, ebits, rtables) ||
+      *reinterpret_cast<const uint64_t *>(rtables + 56) !=
+          *reinterpret_cast<const uint64_t *>(tables + 48)) {
+    if (threadIdx.x == 0) set_status(status, KVC_ERR_PROFILE_MISMATCH);
+    return;
+  }
+
+  extern __shared__ uint32_t lds_raw[];
+  lds_u32 *lds = (lds_u32 *)lds_raw;
+  lds_u32 *sA = lds;                          // [kARows][64] anchor cum
+  lds_u32 *sD = sA + kARows * kWave / 2;      // [kDRows][64] base delta cum of level lv
+  lds_u32 *sE = sD + kDRows * kWave / 2;      // [2][kDRows][64] refinement cum
+  lds_u32 *sR = sE + 2 * kDRows * kWave / 2;  // [waves][64][2][kRing] rings
+  lds_u16 *hA = (lds_u16 *)sA;
+
+  const uint32_t tid = threadIdx.x;
+  {
+    const uint32_t *gA = reinterpret_cast<const uint32_t *>(tables + kTablesHdr) +
+                         (uint64_t)m0 * (kAnchorStride / 2);
+    for (uint32_t i = tid; i < nv * (kARows / 2); i += blockDim.x) {
+      const uint32_t w = i / nv, l = i % nv;
+      const uint32_t v = gA[(uint64_t)l * (kAnchorStride / 2) + w];
+      hA[(2 * w) * kWave + lane_col(l)] = (uint16_t)v;
+      hA[(2 * w + 1) * kWave + lane_col(l)] = (uint16_t)(v >> 16);
+    }
+    // three 64-entry tables: base deltas of level lv, refinement anchor
+    // tokens and other tokens of level lv; entries past an alphabet
+    // (0xFFFF pads) become 2^15 = cum[A]
+    const uint32_t *src3[3] = {
+        reinterpret_cast<const uint32_t *>(tables + kTablesHdr + (uint64_t)S * kAnchorStride * 2) +
+            ((uint64_t)lv * S + m0) * (kDeltaStride / 2),
+        reinterpret_cast<const uint32_t *>(rtables + kTablesHdr) +
+            ((uint64_t)lv * S + m0) * (kDeltaStride / 2),
+        reinterpret_cast<const uint32_t *>(rtables + kTablesHdr) +
+            (((uint64_t)d.nlev + lv) * S + m0) * (kDeltaStride / 2)};
+    for (uint32_t t = 0; t < 3; ++t) {
+      lds_u16 *dst = (lds_u16 *)(t == 0 ? sD : sE) + (t == 2 ? kDRows * kWave : 0);
+      for (uint32_t i = tid; i < nv * (kDRows / 2); i += blockDim.x) {
+        const uint32_t w = i / nv, l = i % nv;
+        const uint32_t v =
+            w < kDeltaStride / 2 ? src3[t][(uint64_t)l * (kDeltaStride / 2) + w] : 0xFFFFFFFFu;
+        const uint32_t e0 = v & 0xFFFFu, e1 = v >> 16;
+        dst[(2 * w) * kWave + lane_col(l)] = (uint16_t)(e0 == 0xFFFFu ? kTot : e0);
+        dst[(2 * w + 1) * kWave + lane_col(l)] = (uint16_t)(e1 == 0xFFFFu ? kTot : e1);
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t lane = tid % kWave;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  if (lane >= nv) return;
+
+  AnchorTop at;
+  at.base = lds_addr(sA) + 2 * lane_col(lane);
+  at.mid = at.base + 128 * kRowBytes;
+  at.c1 = lds_read_u16(at.mid);
+  at.c2lo = lds_read_u16(at.base + 64 * kRowBytes);
+  at.c2hi = lds_read_u16(at.base + 192 * kRowBytes);
+  const uint32_t third = third_of(row >> 1, d.L);
+  const uint64_t ld = (uint64_t)d.C * 2u;
+  const uint32_t m = m0 + lane;
+  const int32_t Me = (1 << (ebits - 1)) - 1;
+  const uint32_t etop = 1u << (ebits - 1);
+  uint32_t ring_addr = lds_addr(sR + ((wave * kWave + lane) * 2) * kRing + kRingLead);
+  __asm__ volatile("" : "+v"(ring_addr));
+  const uint32_t rring_addr = ring_addr + kRing * 4;
+  uint32_t loff = lane * 2u;
+  __asm__ volatile("" : "+v"(loff));
+
+  for (uint32_t i = wave; i < gp.count; i += n_waves) {
+    const uint32_t k = gp.start + i;
+    if (!valid[k] || !rvalid[k]) continue;
+    const ChunkInfo c = ci[k];
+    const ChunkInfo rc = rci[k];
+    // the refinement must be of the base container's chunk (both headers
+    // were checked by the index; the token each was encoded from is at 28)
+    if (*reinterpret_cast<const uint32_t *>(c.cont + 28) !=
+        *reinterpret_cast<const uint32_t *>(rc.cont + 28)) {
+      set_status(status, KVC_ERR_CORRUPT_STREAM);
+      continue;
+    }
+    // ---- the base stream, as in k_decode
+    Stream s;
+    s.ring = (lds_u32 *)(uintptr_t)ring_addr;
+    s.dbase = lds_addr(sD) + 2 * lane_col(lane);
+    const uint32_t b = __builtin_amdgcn_readfirstlane(d.bits[c.level][third]);
+    s.M = (1 << (b - 1)) - 1;
+    s.dbaseM = s.dbase + (uint32_t)s.M * kRowBytes;
+    s.dmid = s.dbase + (1u << (b - 1)) * kRowBytes;
+    s.d1 = lds_read_u16(s.dmid);
+    s.d2lo = lds_read_u16(s.dbase + (1u << (b - 2)) * kRowBytes);
+    s.d2hi = lds_read_u16(s.dbase + 3u * (1u << (b - 2)) * kRowBytes);
+    const uint32_t *rec = reinterpret_cast<const uint32_t *>(c.records + (uint64_t)m * kRecBytes);
+    s.lo = __builtin_bit_cast(float, rec[0]);
+    s.sa7 = __builtin_bit_cast(float, rec[1]) * 0.0078125f;
+    s.dl7 = __builtin_bit_cast(float, rec[2]) * 0.0078125f;
+    const uint32_t nblk = (uint32_t)(pad8(rec[3]) / kBlock);
+    Source src;
+    src.rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)c.cont, (short)0,
+                                                 (int)(uint32_t)c.cont_bytes, kBufferWord3);
+    src.ubase = (uint32_t)(kHdrBytes + (uint64_t)kRecBytes * S) + offsets[(uint64_t)k * S + m0];
+    src.cnt = 0;
+    s.ahat = 0.0f;
+    // ---- the refinement stream
+    RStream e;
+    e.ring = (lds_u32 *)(uintptr_t)rring_addr;
+    e.tab[0] = lds_addr(sE) + 2 * lane_col(lane);
+    e.tab[1] = e.tab[0] + kDRows * kRowBytes;
+    e.tabM[0] = e.tab[0] + (uint32_t)Me * kRowBytes;
+    e.tabM[1] = e.tab[1] + (uint32_t)Me * kRowBytes;
+    const uint32_t *rrec = reinterpret_cast<const uint32_t *>(rc.records + (uint64_t)m * kRecBytes);
+    e.D7[0] = __builtin_bit_cast(float, rrec[0]) * 0.0078125f;
+    e.D7[1] = __builtin_bit_cast(float, rrec[1]) * 0.0078125f;
+    const uint32_t rnblk = (uint32_t)(pad8(rrec[3]) / kBlock);
+    Source rsrc;
+    rsrc.rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)rc.cont, (short)0,
+                                                  (int)(uint32_t)rc.cont_bytes, kBufferWord3);
+    rsrc.ubase = (uint32_t)(kHdrBytes + (uint64_t)kRecBytes * S) + roffsets[(uint64_t)k * S + m0];
+    rsrc.cnt = 0;
+    // start of the reading rule for both: blocks 0, 1 and 2 of every lane
+    // (block outer, lane inner); 0 and 1 fill the ring, 2 is held
+    uint32_t blk[3][2], rblk[3][2];
+#pragma unroll
+    for (uint32_t q = 0; q < 3; ++q) {
+      const uint64_t mask = __builtin_amdgcn_ballot_w64(q < nblk);
+      const uint32_t pos = src.cnt + lanes_below(mask);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(src.rsrc, src.ubase + pos * kBlock, 0, 0);
+      blk[q][0] = v[0];
+      blk[q][1] = v[1];
+      if (q == 2) s.hoff = src.ubase + pos * kBlock;
+      src.cnt += (uint32_t)__builtin_popcountll(mask);
+      const uint64_t rmask = __builtin_amdgcn_ballot_w64(q < rnblk);
+      const uint32_t rpos = rsrc.cnt + lanes_below(rmask);
+      const auto rv =
+          __builtin_amdgcn_raw_buffer_load_b64(rsrc.rsrc, rsrc.ubase + rpos * kBlock, 0, 0);
+      rblk[q][0] = rv[0];
+      rblk[q][1] = rv[1];
+      if (q == 2) e.hoff = rsrc.ubase + rpos * kBlock;
+      rsrc.cnt += (uint32_t)__builtin_popcountll(rmask);
+    }
+    s.rem = nblk < 3 ? 0u : nblk - 3;
+    s.ring[4] = __builtin_bswap32(blk[0][0]);
+    s.ring[3] = __builtin_bswap32(blk[0][1]);
+    s.ring[2] = __builtin_bswap32(blk[1][0]);
+    s.ring[1] = __builtin_bswap32(blk[1][1]);
+    s.ring[0] = __builtin_bswap32(blk[0][0]);
+    s.held[0] = blk[2][0];
+    s.held[1] = blk[2][1];
+    s.nwlim = 0u - (128 - 16);
+    s.wbase = ring_addr;
+    s.wsum = 2u * ring_addr - 8u;
+    s.code = bswap32(blk[0][0]);
+    s.nrpos = 0u - 32;
+    s.range = 0xFFFFFFFFu;
+    e.rem = rnblk < 3 ? 0u : rnblk - 3;
+    e.ring[4] = __builtin_bswap32(rblk[0][0]);
+    e.ring[3] = __builtin_bswap32(rblk[0][1]);
+    e.ring[2] = __builtin_bswap32(rblk[1][0]);
+    e.ring[1] = __builtin_bswap32(rblk[1][1]);
+    e.ring[0] = __builtin_bswap32(rblk[0][0]);
+    e.held[0] = rblk[2][0];
+    e.held[1] = rblk[2][1];
+    e.nwlim = 0u - (128 - 16);
+    e.wbase = rring_addr;
+    e.wsum = 2u * rring_addr - 8u;
+    e.code = bswap32(rblk[0][0]);
+    e.nrpos = 0u - 32;
+    e.range = 0xFFFFFFFFu;
+
+    gbyte *ob = uniform_ptr((gbyte *)c.out +
+                            (((uint64_t)row * c.out_tokens + c.first_token) * d.C + c0) * 2u);
+    uint64_t lost_anchor = 0;
+    switch (b) {
+      case 2: refined_run<2>(s, e, at, src, rsrc, ob, ld, loff, c.n_tokens, d.G, etop, lost_anchor); break;
+      case 3: refined_run<3>(s, e, at, src, rsrc, ob, ld, loff, c.n_tokens, d.G, etop, lost_anchor); break;
+      case 4: refined_run<4>(s, e, at, src, rsrc, ob, ld, loff, c.n_tokens, d.G, etop, lost_anchor); break;
+      case 5: refined_run<5>(s, e, at, src, rsrc, ob, ld, loff, c.n_tokens, d.G, etop, lost_anchor); break;
+      default: refined_run<6>(s, e, at, src, rsrc, ob, ld, loff, c.n_tokens, d.G, etop, lost_anchor); break;
+    }
+    const uint32_t nbytes =
+        reinterpret_cast<const uint32_t *>(ci[k].records + (uint64_t)m * kRecBytes)[3];
+    const uint32_t rnbytes =
+        reinterpret_cast<const uint32_t *>(rci[k].records + (uint64_t)m * kRecBytes)[3];
+    if (s.range == 0 || s.nrpos != 0u - 8 * nbytes || s.rem != 0 || ((lost_anchor >> lane) & 1) ||
+        e.range == 0 || e.nrpos != 0u - 8 * rnbytes || e.rem != 0)
+      set_status(status, KVC_ERR_CORRUPT_STREAM);
+  }
+}
+
+size_t decode_refined_lds_bytes(uint32_t waves) {
+  return (size_t)kARows * kRowBytes + (size_t)3 * kDRows * kRowBytes +
+         sizeof(uint32_t) * (size_t)waves * kWave * 2 * kRing;
+}
+
+hipError_t launch_decode_refined(const Desc &d, uint32_t ebits, const ChunkInfo *dev_chunks,
+                                 const ChunkInfo *dev_rchunks, const DecodeGroup *groups,
+                                 uint32_t n_groups, uint32_t waves, const uint8_t *valid,
+                                 const uint8_t *rvalid, const uint32_t *offsets,
+                                 const uint32_t *roffsets, const uint8_t *tables,
+                                 const uint8_t *rtables, int32_t *status, hipStream_t stream) {
+  const uint32_t ncb = (d.C + kWave - 1) / kWave;
+  const uint32_t n_units = 2u * d.L * ncb;
+  const uint64_t blocks = (uint64_t)((n_units + kXcds - 1) / kXcds) * kXcds * n_groups;
+  hipLaunchKernelGGL(k_decode_refined, dim3((uint32_t)blocks), dim3(waves * kWave),
+                     decode_refined_lds_bytes(waves), stream, d, ebits, dev_chunks, dev_rchunks,
+                     groups, n_groups, n_units, valid, rvalid, offsets, roffsets, tables, rtables,
+                     status);
+  return hipGetLastError();
 }
 
 size_t decode_lds_bytes(uint32_t levels, uint32_t waves) {

@@ -675,6 +675,17 @@ __global__ void k_encode_header(Desc d, const ChunkInfo *__restrict__ ci, uint32
   }
 }
 
+// Container start offsets and the capacity check (shared with the
+// refinement encoder).
+hipError_t launch_encode_layout(const Desc &d, uint32_t n_chunks, const uint64_t *payload,
+                                uint64_t *chunk_off_ws, uint64_t *chunk_off_out, uint64_t out_cap,
+                                uint32_t *fits, uint32_t *redo, int32_t *status,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(k_encode_layout, dim3(1), dim3(64), 0, stream, d, n_chunks, payload,
+                     chunk_off_ws, chunk_off_out, out_cap, fits, redo, status);
+  return hipGetLastError();
+}
+
 hipError_t launch_index(const Desc &d, const ChunkInfo *dev_chunks, uint32_t n_chunks,
                         uint64_t *row_sums, uint32_t *flags, uint32_t *offsets, uint8_t *valid,
                         uint64_t *payload, const uint8_t *tables, int check_header_flag,

@@ -65,6 +65,30 @@ __device__ int32_t check_header(const Desc &d, const ChunkInfo &ci, const uint8_
   return KVC_OK;
 }
 
+// A refinement container ("KVCR") against the descriptor and the refinement
+// tables (its E, its id and the base profile id they were made for).
+__device__ int32_t check_refine_header(const Desc &d, const ChunkInfo &ci, const uint8_t *rtables) {
+  const uint8_t *h = ci.cont;
+  if (ld_u32(h) != kRefineContainerMagic) return KVC_ERR_CORRUPT_STREAM;
+  const uint32_t w1 = ld_u32(h + 4);  // version u16, level u8, E u8
+  if ((w1 & 0xFFFFu) != kRefineVersion) return KVC_ERR_CORRUPT_STREAM;
+  const uint32_t level = (w1 >> 16) & 0xFFu;
+  if (level != ci.level || level >= d.nlev) return KVC_ERR_CORRUPT_STREAM;
+  if (((w1 >> 24) & 0xFFu) != ld_u32(rtables + 24)) return KVC_ERR_CORRUPT_STREAM;
+  const uint32_t w2 = ld_u32(h + 8);
+  const uint32_t w3 = ld_u32(h + 12);
+  if ((w2 & 0xFFFFu) != d.G || ((w2 >> 16) & 0xFFu) != kPrec) return KVC_ERR_CORRUPT_STREAM;
+  if (((w2 >> 24) & 0xFFu) != d.bits[level][0] || (w3 & 0xFFu) != d.bits[level][1] ||
+      ((w3 >> 8) & 0xFFu) != d.bits[level][2])
+    return KVC_ERR_CORRUPT_STREAM;
+  if (ld_u32(h + 16) != d.L || ld_u32(h + 20) != d.C) return KVC_ERR_CORRUPT_STREAM;
+  if (ld_u32(h + 24) != ci.n_tokens) return KVC_ERR_CORRUPT_STREAM;
+  if (ld_u32(h + 48) != d.chunk || ld_u32(h + 52) != n_streams(d)) return KVC_ERR_CORRUPT_STREAM;
+  if (ld_u64(h + 32) != ld_u64(rtables + 48) || ld_u64(h + 56) != ld_u64(rtables + 56))
+    return KVC_ERR_PROFILE_MISMATCH;
+  return KVC_OK;
+}
+
 __global__ __launch_bounds__(256) void k_index_rows(Desc d, const ChunkInfo *__restrict__ ci,
                                                     uint64_t *__restrict__ row_sums,
                                                     uint32_t *__restrict__ flags,
@@ -96,7 +120,10 @@ __global__ __launch_bounds__(256) void k_index_rows(Desc d, const ChunkInfo *__r
   if (threadIdx.x == 0) {
     row_sums[(uint64_t)k * nrows + row] = red[0];
     if (row == 0 && check_header_flag) {
-      const int32_t st = check_header(d, c, tables);
+      // 1: a base container against the tables; 2: a refinement container
+      // against the refinement tables
+      const int32_t st =
+          check_header_flag == 2 ? check_refine_header(d, c, tables) : check_header(d, c, tables);
       if (st != KVC_OK) {
         atomicOr(&flags[k], kFlagHeader);
         set_status(status, st);

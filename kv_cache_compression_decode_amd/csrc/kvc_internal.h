@@ -35,6 +35,10 @@ constexpr uint32_t kContainerMagic = 0x3143564Bu;  // "KVC1"
 constexpr uint32_t kTablesMagic = 0x5443564Bu;     // "KVCT"
 constexpr uint32_t kFormatVersion = 2;  // containers: block-interleaved unit payloads
 constexpr uint32_t kTablesVersion = 1;
+// Refinement layer: its tables blob ("KVRT") and containers ("KVCR").
+constexpr uint32_t kRefineTablesMagic = 0x5452564Bu;     // "KVRT"
+constexpr uint32_t kRefineContainerMagic = 0x5243564Bu;  // "KVCR"
+constexpr uint32_t kRefineVersion = 1;
 
 // Per-chunk description kept in the workspace.
 struct ChunkInfo {
@@ -312,6 +316,46 @@ __device__ inline bool stream_stats(Column &x, uint32_t n, uint32_t G, float &lo
   sa_out = sa;
   maxabs_out = maxabs;
   return finite;
+}
+
+// counts -> frequencies (floor of 1, remainder to the most frequent symbol,
+// lowest index on ties); writes cum[0..A] and pads 0xFFFF; returns the FNV
+// state after hashing the frequencies.
+__device__ inline uint64_t normalize_one(const uint32_t *cnt, uint32_t A, uint16_t *cum,
+                                         uint32_t stride_entries, uint64_t h) {
+  uint64_t N = 0;
+  uint32_t arg = 0;
+  for (uint32_t s = 0; s < A; ++s) {
+    N += cnt[s];
+    if (cnt[s] > cnt[arg]) arg = s;
+  }
+  uint32_t sum = 0;
+  if (N != 0) {
+    for (uint32_t s = 0; s < A; ++s) sum += 1u + (uint32_t)(((uint64_t)cnt[s] * (kTot - A)) / N);
+  }
+  uint32_t acc = 0;
+  for (uint32_t s = 0; s < A; ++s) {
+    uint32_t f;
+    if (N == 0) {
+      f = kTot / A + (s < kTot % A ? 1u : 0u);
+    } else {
+      f = 1u + (uint32_t)(((uint64_t)cnt[s] * (kTot - A)) / N);
+      if (s == arg) f += kTot - sum;
+    }
+    cum[s] = (uint16_t)acc;
+    acc += f;
+    h = fnv_u16(h, f);
+  }
+  cum[A] = (uint16_t)acc;  // == 2^15
+  for (uint32_t s = A + 1; s < stride_entries; ++s) cum[s] = 0xFFFFu;
+  return h;
+}
+
+// The refinement tables blob was made for this descriptor and E.
+__device__ inline bool refine_tables_match(const Desc &d, uint32_t ebits, const uint8_t *rt) {
+  const uint32_t *w = reinterpret_cast<const uint32_t *>(rt);
+  return w[0] == kRefineTablesMagic && w[1] == kRefineVersion && w[2] == d.L && w[3] == d.C &&
+         w[4] == d.G && w[5] == d.chunk && w[6] == ebits && w[7] == d.nlev && w[8] == kPrec;
 }
 
 // Workspace layout helpers.

@@ -82,39 +82,6 @@ __global__ __launch_bounds__(64) void k_profile_count(Desc d, const uint16_t *__
   }
 }
 
-// counts -> frequencies (floor of 1, remainder to the most frequent symbol,
-// lowest index on ties); writes cum[0..A] and pads 0xFFFF; returns the FNV
-// state after hashing the frequencies.
-__device__ inline uint64_t normalize_one(const uint32_t *cnt, uint32_t A, uint16_t *cum,
-                                         uint32_t stride_entries, uint64_t h) {
-  uint64_t N = 0;
-  uint32_t arg = 0;
-  for (uint32_t s = 0; s < A; ++s) {
-    N += cnt[s];
-    if (cnt[s] > cnt[arg]) arg = s;
-  }
-  uint32_t sum = 0;
-  if (N != 0) {
-    for (uint32_t s = 0; s < A; ++s) sum += 1u + (uint32_t)(((uint64_t)cnt[s] * (kTot - A)) / N);
-  }
-  uint32_t acc = 0;
-  for (uint32_t s = 0; s < A; ++s) {
-    uint32_t f;
-    if (N == 0) {
-      f = kTot / A + (s < kTot % A ? 1u : 0u);
-    } else {
-      f = 1u + (uint32_t)(((uint64_t)cnt[s] * (kTot - A)) / N);
-      if (s == arg) f += kTot - sum;
-    }
-    cum[s] = (uint16_t)acc;
-    acc += f;
-    h = fnv_u16(h, f);
-  }
-  cum[A] = (uint16_t)acc;  // == 2^15
-  for (uint32_t s = A + 1; s < stride_entries; ++s) cum[s] = 0xFFFFu;
-  return h;
-}
-
 __global__ __launch_bounds__(64) void k_profile_normalize(Desc d, const uint32_t *__restrict__ counts,
                                                           uint8_t *__restrict__ tables,
                                                           uint64_t *__restrict__ model_hash) {
@@ -181,6 +148,15 @@ __global__ void k_profile_final(Desc d, const uint64_t *__restrict__ row_hash,
   q[4] = q[3] + (uint64_t)d.nlev * S * kDeltaStride * 2;  // 80: total bytes
   for (uint32_t off = 88; off < kTablesHdr; off += 8)
     *reinterpret_cast<uint64_t *>(tables + off) = 0;
+}
+
+// Per (layer, K/V) row, FNV-1a over the row's model hashes (shared with the
+// refinement profile).
+hipError_t launch_rowhash(const Desc &d, const uint64_t *model_hash, uint64_t *row_hash,
+                          hipStream_t stream) {
+  hipLaunchKernelGGL(k_profile_rowhash, dim3((2u * d.L + 63) / 64), dim3(64), 0, stream, d,
+                     model_hash, row_hash);
+  return hipGetLastError();
 }
 
 hipError_t launch_profile(const Desc &d, const uint16_t *kv, uint32_t T, uint8_t *tables,

@@ -223,3 +223,24 @@ def test_decode_static_refuses_oversized_request_before_any_device_call(L):
     assert L.kvc_decode_static(ctypes.byref(d), 4096, refs, n, 4096, 1, 4096, None) == kvc.ERR_CAPACITY
     bad = kvc.make_desc(80, 1024, delta_bits=((7, 5, 4),))
     assert L.kvc_decode_static(ctypes.byref(bad), 4096, refs, 1, 4096, 1, 4096, None) == kvc.ERR_INVALID_ARG
+
+
+def test_refinement_size_queries_and_argument_errors(L):
+    d = kvc.make_desc(80, 1024, delta_bits=((6, 5, 4), (5, 4, 3), (4, 3, 2)))
+    S = 2 * 80 * 1024
+    assert L.kvc_refine_tables_bytes(ctypes.byref(d)) == 128 + 2 * 3 * S * 128
+    assert L.kvc_refine_profile_ws_bytes(ctypes.byref(d)) >= S * 2 * 3 * 64 * 4
+    assert L.kvc_decode_refined_ws_bytes(ctypes.byref(d), 11) >= 2 * 11 * S * 4
+    assert L.kvc_encode_refine_ws_bytes(ctypes.byref(d), 16000) >= 11 * S * 32
+    for bad_bits in (0, 1, 7):
+        assert L.kvc_profile_refine(ctypes.byref(d), 4096, 4096, 10, bad_bits, 4096, 4096, 1 << 40,
+                                    4096, None) == kvc.ERR_INVALID_ARG
+        assert L.kvc_decode_refined(ctypes.byref(d), 4096, 4096, bad_bits, None, 0, None, 0, None,
+                                    0, 4096, None) == kvc.ERR_INVALID_ARG
+    refs = (kvc.RefinedChunkRef * 1)()
+    refs[0].container = 4096
+    refs[0].refinement = 0  # missing refinement container
+    refs[0].container_bytes = refs[0].refinement_bytes = 64 + 16 * S
+    refs[0].n_tokens = 10
+    assert L.kvc_decode_refined(ctypes.byref(d), 4096, 4096, 4, refs, 1, 4096, 16000, 4096,
+                                1 << 40, 4096, None) == kvc.ERR_INVALID_ARG
