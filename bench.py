@@ -332,6 +332,54 @@ def measure_multi(kvc, d, tables, kv_dev, cfg, n_req: int = 8, req_tokens: int =
     return res
 
 
+def measure_refine(kvc, d, tables, rtables, ebits, enc, kv_dev, base_out, cfg, levels,
+                   reps: int = 5) -> dict:
+    """The refinement layer (ebits bits) over the same chunks: its containers'
+    size, the refined decode (base + refinement streams in one launch) timed
+    like the base decode, and the mean |error| of both decodes against the
+    input."""
+    import torch
+
+    dev = tables.device
+    renc = kvc.encode_refine(d, rtables, ebits, kv_dev, levels)
+    refs = kvc.refined_chunk_refs(enc, renc)
+    out = torch.zeros_like(kv_dev)
+    wsp = kvc.RefinedDecodeWorkspace(d, len(refs), dev)
+    for _ in range(2):
+        kvc.decode_refined_async(d, tables, rtables, ebits, refs, out, wsp)
+    kvc.read_status(wsp.status, "kvc_decode_refined")
+    ms = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        kvc.decode_refined_async(d, tables, rtables, ebits, refs, out, wsp)
+        b.record()
+        b.synchronize()
+        ms.append(a.elapsed_time(b))
+    kvc.read_status(wsp.status, "kvc_decode_refined")
+    err_b = err_r = 0.0
+    for t0 in range(0, cfg.n_tokens, 1500):
+        x = kv_dev[:, :, t0:t0 + 1500].view(torch.float16).float()
+        err_b += float((base_out[:, :, t0:t0 + 1500].view(torch.float16).float() - x).abs().sum())
+        err_r += float((out[:, :, t0:t0 + 1500].view(torch.float16).float() - x).abs().sum())
+        del x
+    med = statistics.median(ms)
+    fp16_bytes = cfg.fp16_bytes()
+    res = {
+        "refine_bits": ebits,
+        "refinement_bytes": renc.total_bytes(),
+        "base_bytes": enc.total_bytes(),
+        "ms": round(med, 3),
+        "decoded_GBps": round(fp16_bytes / (med * 1e-3) / 1e9, 2),
+        "algorithmic_GBps": round((fp16_bytes + enc.total_bytes() + renc.total_bytes())
+                                  / (med * 1e-3) / 1e9, 2),
+        "mean_abs_error_base": err_b / (fp16_bytes // 2),
+        "mean_abs_error_refined": err_r / (fp16_bytes // 2),
+    }
+    log(f"refinement: {res}")
+    return res, renc, out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -375,6 +423,8 @@ def main() -> int:
     kv_dev = torch.from_numpy(kv.view(np.int16)).to(dev)
     kvp_dev = torch.from_numpy(kvp.view(np.int16)).to(dev)
     tables = kvc.profile(d, kvp_dev)
+    refine_bits = 4
+    rtables = None if args.decode_only else kvc.profile_refine(d, tables, kvp_dev, refine_bits)
     del kvp_dev
     torch.cuda.synchronize()
 
@@ -452,8 +502,11 @@ def main() -> int:
     copy_gbs = copy_rate(out)
     torch.cuda.synchronize()
 
-    restore = controller = multi = None
+    restore = controller = multi = refine = None
+    renc = refined_out = None
     if not args.decode_only:
+        refine, renc, refined_out = measure_refine(kvc, d, tables, rtables, refine_bits, enc,
+                                                   kv_dev, out, cfg, levels)
         restore = measure_restore(kvc, d, tables, enc, cfg, out)
         controller = measure_controller(kvc, d, tables, kv_dev, cfg)
         multi = measure_multi(kvc, d, tables, kv_dev, cfg)
@@ -533,6 +586,7 @@ def main() -> int:
         "restore": restore,
         "level_controller": controller,
         "multi_request": multi,
+        "refinement": refine,
         "sha256": {"kv_fp16": sha256_of(kv), "profile_kv_fp16": sha256_of(kvp)},
     }
     props = torch.cuda.get_device_properties(dev)
@@ -576,6 +630,22 @@ def main() -> int:
                       f"{sample_bytes / 1e9:.2f} GB of binary16) in {cpu_s:.2f} s",
         }
         log(f"oracle decode {sample_bytes / 1e9:.2f} GB in {cpu_s:.1f} s; bit_exact={exact}")
+        if renc is not None:
+            # the refinement layer: tables id, first and last chunk's refinement
+            # container and refined KV against the oracle's
+            ort = oracle.profile_refine(od, kvp, refine_bits, otb.profile_id)
+            rexact = ort.refine_id == kvc.refine_id(rtables)
+            for k in sorted({0, cfg.n_chunks - 1}):
+                oc = conts[k] if k < len(conts) else oracle.encode_chunk(od, otb, kv, k, levels[k])
+                orc = oracle.encode_refine_chunk(od, ort, kv, k, levels[k])
+                rexact = rexact and np.array_equal(renc.container(k).cpu().numpy(), orc)
+                n = cfg.chunk_tokens(k)
+                oo = np.zeros((cfg.n_layers, 2, n, cfg.n_channels), np.uint16)
+                oracle.decode_refined_chunk_into(od, otb, oc, ort, orc, 0, n, levels[k], oo)
+                got = refined_out[:, :, 1500 * k:1500 * k + n].cpu().numpy().view(np.uint16)
+                rexact = rexact and np.array_equal(got, oo)
+            result["refinement"]["bit_exact_first_last_chunk"] = bool(rexact)
+            log(f"refinement bit_exact (chunks 0 and last) = {rexact}")
         # the same oracle on one core, on its first chunk
         threads = oracle.get_threads()
         oracle.set_threads(1)

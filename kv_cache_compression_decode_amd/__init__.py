@@ -702,24 +702,40 @@ def refined_chunk_refs(enc: Encoded, renc: Encoded, chunks: Optional[Sequence[in
     return out
 
 
-def decode_refined(desc: CodecDesc, tables: torch.Tensor, rtables: torch.Tensor, refine_bits: int,
-                   refs: Sequence[RefinedChunkRef], T_total: int,
-                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Decode base + refinement layers into the KV cache [L][2][T_total][C]
-    (int16 bit patterns of binary16)."""
-    L = lib()
-    dev = tables.device
-    if out is None:
-        out = torch.zeros((desc.n_layers, 2, T_total, desc.n_channels), dtype=torch.int16, device=dev)
-    wsb = int(L.kvc_decode_refined_ws_bytes(ctypes.byref(desc), len(refs)))
-    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
-    st = _dev_status(dev)
+class RefinedDecodeWorkspace:
+    """Reusable workspace + status word of kvc_decode_refined for up to n_chunks."""
+
+    def __init__(self, desc: CodecDesc, n_chunks: int, device):
+        self.ws_bytes = int(lib().kvc_decode_refined_ws_bytes(ctypes.byref(desc), n_chunks))
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+        self.status = _dev_status(device)
+        self.n_chunks = n_chunks
+
+
+def decode_refined_async(desc: CodecDesc, tables: torch.Tensor, rtables: torch.Tensor,
+                         refine_bits: int, refs: Sequence[RefinedChunkRef], out: torch.Tensor,
+                         wsp: RefinedDecodeWorkspace, stream=None) -> None:
+    """Launch kvc_decode_refined into out [L][2][T_total][C] (no sync)."""
     arr = (RefinedChunkRef * max(len(refs), 1))()
     for i, r in enumerate(refs):
         arr[i] = r
-    _check(L.kvc_decode_refined(ctypes.byref(desc), tables.data_ptr(), rtables.data_ptr(),
-                                refine_bits, arr, len(refs), _kv_ptr(out), out.shape[2],
-                                ws.data_ptr(), wsb, st.data_ptr(), _stream(stream)),
-           "kvc_decode_refined")
-    read_status(st, "kvc_decode_refined", stream)
+    _check(lib().kvc_decode_refined(ctypes.byref(desc), tables.data_ptr(), rtables.data_ptr(),
+                                    refine_bits, arr, len(refs), _kv_ptr(out), out.shape[2],
+                                    wsp.ws.data_ptr(), wsp.ws_bytes, wsp.status.data_ptr(),
+                                    _stream(stream)), "kvc_decode_refined")
+
+
+def decode_refined(desc: CodecDesc, tables: torch.Tensor, rtables: torch.Tensor, refine_bits: int,
+                   refs: Sequence[RefinedChunkRef], T_total: int,
+                   out: Optional[torch.Tensor] = None, stream=None,
+                   wsp: Optional[RefinedDecodeWorkspace] = None) -> torch.Tensor:
+    """Decode base + refinement layers into the KV cache [L][2][T_total][C]
+    (int16 bit patterns of binary16)."""
+    dev = tables.device
+    if out is None:
+        out = torch.zeros((desc.n_layers, 2, T_total, desc.n_channels), dtype=torch.int16, device=dev)
+    if wsp is None:
+        wsp = RefinedDecodeWorkspace(desc, len(refs), dev)
+    decode_refined_async(desc, tables, rtables, refine_bits, refs, out, wsp, stream)
+    read_status(wsp.status, "kvc_decode_refined", stream)
     return out

@@ -49,10 +49,11 @@ hipError_t launch_encode_refine(const Desc &d, uint32_t ebits, const uint8_t *rt
                                 uint64_t *payload, uint64_t *chunk_off_ws, uint32_t *fits,
                                 uint32_t *spare, uint8_t *scratch, uint8_t *out, uint64_t out_cap,
                                 uint64_t *chunk_off_out, int32_t *status, hipStream_t stream);
-size_t decode_refined_lds_bytes(uint32_t waves);
+size_t decode_refined_lds_bytes(uint32_t levels, uint32_t ebits, uint32_t waves);
 hipError_t launch_decode_refined(const Desc &d, uint32_t ebits, const ChunkInfo *dev_chunks,
                                  const ChunkInfo *dev_rchunks, const DecodeGroup *groups,
-                                 uint32_t n_groups, uint32_t waves, const uint8_t *valid,
+                                 uint32_t n_groups, uint32_t levels, uint32_t waves,
+                                 const uint8_t *valid,
                                  const uint8_t *rvalid, const uint32_t *offsets,
                                  const uint32_t *roffsets, const uint8_t *tables,
                                  const uint8_t *rtables, int32_t *status, hipStream_t stream);
@@ -709,35 +710,38 @@ kvc_status kvc_decode_refined(const kvc_codec_desc *dd, const void *tables, cons
   std::sort(ranges.begin(), ranges.end());
   for (uint32_t k = 1; k < n_chunks; ++k)
     if (ranges[k].first < ranges[k - 1].second) return KVC_ERR_SHAPE;
-  // groups hold chunks of one level: the chunk table is ordered by level and
-  // each level's chunks split into groups of at most wmax * kMaxRounds
+  // decode groups as in kvc_decode: the chunk table ordered by level, split
+  // into near-equal groups (one workgroup per (row, channel block) and group,
+  // each wave taking at most kMaxRounds chunks); a workgroup stages, for
+  // every level its group holds, the base delta models and both refinement
+  // models
   std::stable_sort(info.begin(), info.end(),
                    [](const std::pair<ChunkInfo, ChunkInfo> &a,
                       const std::pair<ChunkInfo, ChunkInfo> &b) { return a.first.level < b.first.level; });
   constexpr uint32_t kMaxRounds = 4;
   constexpr size_t kRefinedLdsBudget = 160u * 1024u;
+  uint32_t all_levels = 0;
+  for (const auto &c : info) all_levels |= 1u << c.first.level;
+  const uint32_t lv_all = (uint32_t)__builtin_popcount(all_levels);
   uint32_t wmax = 1;
   for (uint32_t wv = kDecodeMaxWaves; wv >= 1; --wv)
-    if (decode_refined_lds_bytes(wv) <= kRefinedLdsBudget) {
+    if (decode_refined_lds_bytes(lv_all, refine_bits, wv) <= kRefinedLdsBudget) {
       wmax = wv;
       break;
     }
   std::vector<DecodeGroup> groups;
-  uint32_t waves = 1;
-  for (uint32_t a = 0; a < n_chunks;) {
-    uint32_t b = a;
-    while (b < n_chunks && info[b].first.level == info[a].first.level) ++b;
-    const uint32_t cnt = b - a;
-    const uint32_t ng = (cnt + wmax * kMaxRounds - 1) / (wmax * kMaxRounds);
-    for (uint32_t gi = 0; gi < ng; ++gi) {
-      DecodeGroup g{};
-      g.start = a + (uint32_t)((uint64_t)cnt * gi / ng);
-      g.count = a + (uint32_t)((uint64_t)cnt * (gi + 1) / ng) - g.start;
-      g.level = 1u << info[a].first.level;
-      waves = std::max<uint32_t>(waves, std::min<uint32_t>(wmax, g.count));
-      groups.push_back(g);
-    }
-    a = b;
+  uint32_t levels = 1, waves = 1;
+  const uint32_t ng = (n_chunks + wmax * kMaxRounds - 1) / (wmax * kMaxRounds);
+  for (uint32_t gi = 0; gi < ng; ++gi) {
+    const uint32_t a = (uint32_t)((uint64_t)n_chunks * gi / ng);
+    const uint32_t b = (uint32_t)((uint64_t)n_chunks * (gi + 1) / ng);
+    DecodeGroup g{};
+    g.start = a;
+    g.count = b - a;
+    for (uint32_t i = a; i < b; ++i) g.level |= 1u << info[i].first.level;
+    levels = std::max<uint32_t>(levels, (uint32_t)__builtin_popcount(g.level));
+    waves = std::max<uint32_t>(waves, std::min<uint32_t>(wmax, g.count));
+    groups.push_back(g);
   }
   hipError_t e = launch_reset_status(dev_status, stream);
   if (e != hipSuccess || n_chunks == 0) return hip_status(e);
@@ -768,7 +772,8 @@ kvc_status kvc_decode_refined(const kvc_codec_desc *dd, const void *tables, cons
   DecodeGroup *dgr = reinterpret_cast<DecodeGroup *>(wb + w.groups);
   e = launch_load_groups(groups.data(), (uint32_t)groups.size(), dgr, stream);
   if (e != hipSuccess) return KVC_ERR_HIP;
-  e = launch_decode_refined(d, refine_bits, dbch, drch, dgr, (uint32_t)groups.size(), waves,
+  e = launch_decode_refined(d, refine_bits, dbch, drch, dgr, (uint32_t)groups.size(), levels,
+                            waves,
                             wb + w.valid, wr + w.valid,
                             reinterpret_cast<uint32_t *>(wb + w.offsets),
                             reinterpret_cast<uint32_t *>(wr + w.offsets),

@@ -58,6 +58,8 @@ namespace {
 constexpr uint32_t kMaxWaves = kDecodeMaxWaves;  // waves per workgroup (host picks W <= this)
 constexpr uint32_t kARows = 258;    // staged anchor model rows: cum[0..256] + pad
 constexpr uint32_t kDRows = 66;     // staged delta model rows: cum[0..63] + 2 pads
+// staged refinement model rows for E bits: cum[0..2^E] and one pad, even
+__host__ __device__ constexpr uint32_t refine_rows(uint32_t ebits) { return (1u << ebits) + 2u; }
 constexpr uint32_t kRowBytes = 2 * kWave;  // one u16 entry for each of the 64 lanes
 constexpr uint32_t kRing = 7;       // dwords per lane ring: 2 spare, 16 bytes, mirror of bytes 0..3
 constexpr uint32_t kRingLead = 2;   // spare dwords before the ring's byte 0
@@ -209,7 +211,7 @@ struct AnchorTop {
 // [0, 2^kSteps), and delta entries past an alphabet are staged as 2^15 so
 // that no product can wrap and a valid code never selects them.  Returns the
 // value to store (binary16 bits, or the symbol).
-template <bool kSymbols, bool kAnchor, uint32_t kSteps, bool kF32 = false>
+template <bool kSymbols, bool kAnchor, uint32_t kSteps>
 __device__ inline uint32_t step(Stream &x, const AnchorTop &at, uint64_t &lost_anchor) {
   // the next four stream bytes, most significant first
   const lds_u32 *rd =
@@ -259,15 +261,6 @@ __device__ inline uint32_t step(Stream &x, const AnchorTop &at, uint64_t &lost_a
   x.nrpos -= sh;
   if constexpr (kSymbols) {
     return kAnchor ? (uint32_t)xq >> 7 : (uint32_t)((xq >> 7) + x.M);
-  } else if constexpr (kF32) {
-    // the reconstruction in binary32, before its binary16 rounding (the
-    // value the refinement layer refines)
-    if constexpr (kAnchor) {
-      x.ahat = __builtin_fmaf((float)xq, x.sa7, x.lo);
-      return __builtin_bit_cast(uint32_t, x.ahat);
-    } else {
-      return __builtin_bit_cast(uint32_t, __builtin_fmaf((float)xq, x.dl7, x.ahat));
-    }
   } else {
     // 128 q is exact in binary32 and (128 q)(dl / 128) = q dl exactly, so
     // this is the single rounding of fma(q, dl, ahat)
@@ -373,7 +366,9 @@ struct RStream {
   u32x2 held;
   uint32_t rem, hoff, wbase, wsum;
   uint32_t tab[2];   // LDS byte address of this lane's row 0: anchor tokens, other tokens
+  uint32_t mid[2];   // tab + 2^(E-1) rows: the search's first step taken
   uint32_t tabM[2];  // tab + Me rows: (addr - tabM) is 128 q
+  uint32_t c1[2], c2lo[2], c2hi[2];  // cum[2^(E-1)], cum[2^(E-2)], cum[3 2^(E-2)]
   float D7[2];       // Da / 128, Dd / 128 (exact: D is 0 or above 2^-100)
 
   // as Stream::put_block: the held block, byte-reversed, into the free half
@@ -388,47 +383,95 @@ struct RStream {
   }
 };
 
-// One token of a lane's refinement stream: the symbol q + Me (binary search
-// over 2^E entries, `top` = 2^(E-1) rows), then binary16(fma(q, D, xh)).
-template <bool kAnchor>
-__device__ inline uint32_t rstep(RStream &e, uint32_t top, float xh) {
-  const lds_u32 *rd =
-      (const lds_u32 *)(uintptr_t)(lds_addr(e.ring) + (dword_of(e.nrpos) << 2));
-  const uint32_t in = __builtin_amdgcn_alignbit(rd[1], rd[0], e.nrpos);
-  const uint32_t r = e.range >> kPrec;
+// Range-decoder state update once a search has ended on the interval
+// [cs, cn): the Stream::step arithmetic.  Returns whether the code is past
+// the interval (code - r cs >= r (cn - cs)), which only a lost anchor shows.
+template <class St>
+__device__ inline bool rc_consume(St &x, uint32_t r, uint32_t cs, uint32_t cn, uint32_t in) {
+  x.code -= __umul24(r, cs);
+  const uint32_t range = __umul24(r, cn - cs);
+  const bool past = x.code >= range;
+  const uint32_t sh = ffbh(range) & 24u;
+  x.range = range << sh;
+  x.code = (uint32_t)((((uint64_t)x.code << 32) | in) << sh >> 32);
+  x.nrpos -= sh;
+  return past;
+}
+
+// One token of a lane's base and refinement streams together: both symbols
+// (the base search over kSteps levels, the refinement search over E levels,
+// their LDS probes issued side by side so that the two dependent chains
+// overlap), then the base value xh in binary32 and binary16(fma(q, D, xh)).
+template <bool kAnchor, uint32_t kSteps, uint32_t kE>
+__device__ inline uint32_t rstep(Stream &x, RStream &e, const AnchorTop &at,
+                                 uint64_t &lost_anchor) {
   constexpr uint32_t kind = kAnchor ? 0 : 1;
-  uint32_t a = e.tab[kind];
-  for (uint32_t sz = top * kRowBytes; sz >= kRowBytes; sz >>= 1) {
-    const uint32_t probe = lds_read_u16(a + sz);
-    if (__umul24(r, probe) <= e.code) a += sz;
+  const lds_u32 *rd =
+      (const lds_u32 *)(uintptr_t)(lds_addr(x.ring) + (dword_of(x.nrpos) << 2));
+  const uint32_t in = __builtin_amdgcn_alignbit(rd[1], rd[0], x.nrpos);
+  const lds_u32 *erd =
+      (const lds_u32 *)(uintptr_t)(lds_addr(e.ring) + (dword_of(e.nrpos) << 2));
+  const uint32_t ein = __builtin_amdgcn_alignbit(erd[1], erd[0], e.nrpos);
+  const uint32_t r = x.range >> kPrec;
+  const uint32_t er = e.range >> kPrec;
+  // the first two levels of both searches from registers
+  constexpr uint32_t kTop = 1u << (kSteps - 1);
+  constexpr uint32_t kETop = 1u << (kE - 1);
+  const bool upper = __umul24(r, kAnchor ? at.c1 : x.d1) <= x.code;
+  uint32_t a = upper ? (kAnchor ? at.mid : x.dmid) : (kAnchor ? at.base : x.dbase);
+  const uint32_t p2 = upper ? (kAnchor ? at.c2hi : x.d2hi) : (kAnchor ? at.c2lo : x.d2lo);
+  if (__umul24(r, p2) <= x.code) a += (kTop / 2) * kRowBytes;
+  const bool eupper = __umul24(er, e.c1[kind]) <= e.code;
+  uint32_t ea = eupper ? e.mid[kind] : e.tab[kind];
+  const uint32_t ep2 = eupper ? e.c2hi[kind] : e.c2lo[kind];
+  if (__umul24(er, ep2) <= e.code) ea += (kETop / 2) * kRowBytes;
+  SEARCH_BARRIER();
+  // the LDS levels, in lockstep while both searches have one
+  constexpr uint32_t kLv = kSteps - 2, kELv = kE - 2;
+  constexpr uint32_t kMaxLv = kLv > kELv ? kLv : kELv;
+#pragma unroll
+  for (uint32_t i = 0; i < kMaxLv; ++i) {
+    const uint32_t sz = (kTop / 4) >> i, esz = (kETop / 4) >> i;
+    uint32_t probe = 0, eprobe = 0;
+    if (i < kLv) probe = lds_read_u16(a + sz * kRowBytes);
+    if (i < kELv) eprobe = lds_read_u16(ea + esz * kRowBytes);
+    SEARCH_BARRIER();
+    if (i < kLv && __umul24(r, probe) <= x.code) a += sz * kRowBytes;
+    if (i < kELv && __umul24(er, eprobe) <= e.code) ea += esz * kRowBytes;
+    SEARCH_BARRIER();
   }
   const uint32_t cs = lds_read_u16(a);
   const uint32_t cn = lds_read_u16(a + kRowBytes);
-  const int32_t xq = (int32_t)(a - e.tabM[kind]);
-  e.code -= __umul24(r, cs);
-  const uint32_t range = __umul24(r, cn - cs);
-  const uint32_t sh = ffbh(range) & 24u;
-  e.range = range << sh;
-  e.code = (uint32_t)((((uint64_t)e.code << 32) | in) << sh >> 32);
-  e.nrpos -= sh;
-  return f2h(__builtin_fmaf((float)xq, e.D7[kind], xh));
+  const uint32_t ecs = lds_read_u16(ea);
+  const uint32_t ecn = lds_read_u16(ea + kRowBytes);
+  SEARCH_BARRIER();
+  // base: as Stream::step (a lost anchor is recorded the same way)
+  const int32_t xq = kAnchor ? (int32_t)(a - at.base) : (int32_t)(a - x.dbaseM);
+  const bool past = rc_consume(x, r, cs, cn, in);
+  if constexpr (kAnchor) lost_anchor |= __builtin_amdgcn_ballot_w64(past);
+  const int32_t eq = (int32_t)(ea - e.tabM[kind]);
+  rc_consume(e, er, ecs, ecn, ein);
+  float xh;
+  if constexpr (kAnchor) {
+    x.ahat = __builtin_fmaf((float)xq, x.sa7, x.lo);
+    xh = x.ahat;
+  } else {
+    xh = __builtin_fmaf((float)xq, x.dl7, x.ahat);
+  }
+  return f2h(__builtin_fmaf((float)eq, e.D7[kind], xh));
 }
 
 // Every token of a lane's base and refinement streams, group by group; the
 // two streams follow the same reading rule, each over its own container.
-template <uint32_t kSteps>
+template <uint32_t kSteps, uint32_t kE>
 __device__ inline void refined_run(Stream &s, RStream &e, const AnchorTop &at, Source &src,
                                    Source &rsrc, gbyte *ob, uint64_t ld, uint32_t &loff,
-                                   uint32_t n, uint32_t G, uint32_t etop, uint64_t &lost_anchor) {
+                                   uint32_t n, uint32_t G, uint64_t &lost_anchor) {
   for (uint32_t j = 0; j < n;) {
     refill(s, src);
     refill(e, rsrc);
-    {
-      const float xh =
-          __builtin_bit_cast(float, step<false, true, 8, true>(s, at, lost_anchor));
-      put<false>(ob, loff, rstep<true>(e, etop, xh));
-      ob += ld;
-    }
+    put<false>(ob, loff, rstep<true, 8, kE>(s, e, at, lost_anchor));
+    ob += ld;
     const uint32_t jend = j + G < n ? j + G : n;
     const uint32_t count = jend - j - 1;
     for (uint32_t i = 0; i < count; ++i) {
@@ -437,12 +480,24 @@ __device__ inline void refined_run(Stream &s, RStream &e, const AnchorTop &at, S
         ensure(s, src);
         ensure(e, rsrc);
       }
-      const float xh =
-          __builtin_bit_cast(float, step<false, false, kSteps, true>(s, at, lost_anchor));
-      put<false>(ob, loff, rstep<false>(e, etop, xh));
+      put<false>(ob, loff, rstep<false, kSteps, kE>(s, e, at, lost_anchor));
       ob += ld;
     }
     j = jend;
+  }
+}
+
+template <uint32_t kE>
+__device__ inline void refined_run_b(uint32_t b, Stream &s, RStream &e, const AnchorTop &at,
+                                     Source &src, Source &rsrc, gbyte *ob, uint64_t ld,
+                                     uint32_t &loff, uint32_t n, uint32_t G,
+                                     uint64_t &lost_anchor) {
+  switch (b) {
+    case 2: refined_run<2, kE>(s, e, at, src, rsrc, ob, ld, loff, n, G, lost_anchor); break;
+    case 3: refined_run<3, kE>(s, e, at, src, rsrc, ob, ld, loff, n, G, lost_anchor); break;
+    case 4: refined_run<4, kE>(s, e, at, src, rsrc, ob, ld, loff, n, G, lost_anchor); break;
+    case 5: refined_run<5, kE>(s, e, at, src, rsrc, ob, ld, loff, n, G, lost_anchor); break;
+    default: refined_run<6, kE>(s, e, at, src, rsrc, ob, ld, loff, n, G, lost_anchor); break;
   }
 }
 
@@ -629,8 +684,10 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode_refined(
   const uint32_t m0 = row * d.C + c0;
   const uint32_t S = n_streams(d);
   const DecodeGroup gp = groups[grp];
-  const uint32_t lv = 31u - __builtin_clz(gp.level);  // the group's one level
+  const uint32_t level_mask = gp.level;  // bit l: the group has chunks of level l
   const uint32_t n_waves = blockDim.x / kWave;
+  const uint32_t erows = refine_rows(ebits);
+  const uint32_t slot_rows = kDRows + 2 * erows;
   // the refinement tables were made for this descriptor, E and these base
   // tables (their base id is the base tables' profile id)
   if (!refine_tables_match(d, ebits, rtables) ||
@@ -642,10 +699,12 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode_refined(
 
   extern __shared__ uint32_t lds_raw[];
   lds_u32 *lds = (lds_u32 *)lds_raw;
-  lds_u32 *sA = lds;                          // [kARows][64] anchor cum
-  lds_u32 *sD = sA + kARows * kWave / 2;      // [kDRows][64] base delta cum of level lv
-  lds_u32 *sE = sD + kDRows * kWave / 2;      // [2][kDRows][64] refinement cum
-  lds_u32 *sR = sE + 2 * kDRows * kWave / 2;  // [waves][64][2][kRing] rings
+  // [kARows][64] anchor cum, then one slot per level the group uses: base
+  // delta cum [kDRows][64], refinement cum of anchor tokens and of the other
+  // tokens [erows][64] each; then the rings [waves][64][2][kRing]
+  lds_u32 *sA = lds;
+  lds_u32 *sL = sA + kARows * kWave / 2;
+  lds_u32 *sR = sL + __builtin_popcount(level_mask) * slot_rows * kWave / 2;
   lds_u16 *hA = (lds_u16 *)sA;
 
   const uint32_t tid = threadIdx.x;
@@ -658,26 +717,33 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode_refined(
       hA[(2 * w) * kWave + lane_col(l)] = (uint16_t)v;
       hA[(2 * w + 1) * kWave + lane_col(l)] = (uint16_t)(v >> 16);
     }
-    // three 64-entry tables: base deltas of level lv, refinement anchor
-    // tokens and other tokens of level lv; entries past an alphabet
-    // (0xFFFF pads) become 2^15 = cum[A]
-    const uint32_t *src3[3] = {
-        reinterpret_cast<const uint32_t *>(tables + kTablesHdr + (uint64_t)S * kAnchorStride * 2) +
-            ((uint64_t)lv * S + m0) * (kDeltaStride / 2),
-        reinterpret_cast<const uint32_t *>(rtables + kTablesHdr) +
-            ((uint64_t)lv * S + m0) * (kDeltaStride / 2),
-        reinterpret_cast<const uint32_t *>(rtables + kTablesHdr) +
-            (((uint64_t)d.nlev + lv) * S + m0) * (kDeltaStride / 2)};
-    for (uint32_t t = 0; t < 3; ++t) {
-      lds_u16 *dst = (lds_u16 *)(t == 0 ? sD : sE) + (t == 2 ? kDRows * kWave : 0);
-      for (uint32_t i = tid; i < nv * (kDRows / 2); i += blockDim.x) {
-        const uint32_t w = i / nv, l = i % nv;
-        const uint32_t v =
-            w < kDeltaStride / 2 ? src3[t][(uint64_t)l * (kDeltaStride / 2) + w] : 0xFFFFFFFFu;
-        const uint32_t e0 = v & 0xFFFFu, e1 = v >> 16;
-        dst[(2 * w) * kWave + lane_col(l)] = (uint16_t)(e0 == 0xFFFFu ? kTot : e0);
-        dst[(2 * w + 1) * kWave + lane_col(l)] = (uint16_t)(e1 == 0xFFFFu ? kTot : e1);
+    // per level: the base deltas, the refinement of anchor tokens and of the
+    // other tokens; entries past an alphabet (0xFFFF pads) become 2^15 = cum[A]
+    uint32_t slot = 0;
+    for (uint32_t lv = 0; lv < d.nlev; ++lv) {
+      if (!((level_mask >> lv) & 1u)) continue;
+      const uint32_t *src3[3] = {
+          reinterpret_cast<const uint32_t *>(tables + kTablesHdr +
+                                             (uint64_t)S * kAnchorStride * 2) +
+              ((uint64_t)lv * S + m0) * (kDeltaStride / 2),
+          reinterpret_cast<const uint32_t *>(rtables + kTablesHdr) +
+              ((uint64_t)lv * S + m0) * (kDeltaStride / 2),
+          reinterpret_cast<const uint32_t *>(rtables + kTablesHdr) +
+              (((uint64_t)d.nlev + lv) * S + m0) * (kDeltaStride / 2)};
+      lds_u16 *sbase = (lds_u16 *)(sL + slot * slot_rows * kWave / 2);
+      for (uint32_t t = 0; t < 3; ++t) {
+        const uint32_t rows = t == 0 ? kDRows : erows;
+        lds_u16 *dst = sbase + (t == 0 ? 0u : (kDRows + (t - 1) * erows) * kWave);
+        for (uint32_t i = tid; i < nv * (rows / 2); i += blockDim.x) {
+          const uint32_t w = i / nv, l = i % nv;
+          const uint32_t v =
+              w < kDeltaStride / 2 ? src3[t][(uint64_t)l * (kDeltaStride / 2) + w] : 0xFFFFFFFFu;
+          const uint32_t e0 = v & 0xFFFFu, e1 = v >> 16;
+          dst[(2 * w) * kWave + lane_col(l)] = (uint16_t)(e0 == 0xFFFFu ? kTot : e0);
+          dst[(2 * w + 1) * kWave + lane_col(l)] = (uint16_t)(e1 == 0xFFFFu ? kTot : e1);
+        }
       }
+      ++slot;
     }
   }
   __syncthreads();
@@ -717,7 +783,9 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode_refined(
     // ---- the base stream, as in k_decode
     Stream s;
     s.ring = (lds_u32 *)(uintptr_t)ring_addr;
-    s.dbase = lds_addr(sD) + 2 * lane_col(lane);
+    const uint32_t lslot = __builtin_popcount(level_mask & ((1u << c.level) - 1u));
+    const uint32_t slot_addr = lds_addr(sL) + lslot * slot_rows * kRowBytes + 2 * lane_col(lane);
+    s.dbase = slot_addr;
     const uint32_t b = __builtin_amdgcn_readfirstlane(d.bits[c.level][third]);
     s.M = (1 << (b - 1)) - 1;
     s.dbaseM = s.dbase + (uint32_t)s.M * kRowBytes;
@@ -739,10 +807,15 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode_refined(
     // ---- the refinement stream
     RStream e;
     e.ring = (lds_u32 *)(uintptr_t)rring_addr;
-    e.tab[0] = lds_addr(sE) + 2 * lane_col(lane);
-    e.tab[1] = e.tab[0] + kDRows * kRowBytes;
-    e.tabM[0] = e.tab[0] + (uint32_t)Me * kRowBytes;
-    e.tabM[1] = e.tab[1] + (uint32_t)Me * kRowBytes;
+    e.tab[0] = slot_addr + kDRows * kRowBytes;
+    e.tab[1] = e.tab[0] + erows * kRowBytes;
+    for (uint32_t t = 0; t < 2; ++t) {
+      e.tabM[t] = e.tab[t] + (uint32_t)Me * kRowBytes;
+      e.mid[t] = e.tab[t] + etop * kRowBytes;
+      e.c1[t] = lds_read_u16(e.mid[t]);
+      e.c2lo[t] = lds_read_u16(e.tab[t] + (etop / 2) * kRowBytes);
+      e.c2hi[t] = lds_read_u16(e.tab[t] + 3u * (etop / 2) * kRowBytes);
+    }
     const uint32_t *rrec = reinterpret_cast<const uint32_t *>(rc.records + (uint64_t)m * kRecBytes);
     e.D7[0] = __builtin_bit_cast(float, rrec[0]) * 0.0078125f;
     e.D7[1] = __builtin_bit_cast(float, rrec[1]) * 0.0078125f;
@@ -805,12 +878,12 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode_refined(
     gbyte *ob = uniform_ptr((gbyte *)c.out +
                             (((uint64_t)row * c.out_tokens + c.first_token) * d.C + c0) * 2u);
     uint64_t lost_anchor = 0;
-    switch (b) {
-      case 2: refined_run<2>(s, e, at, src, rsrc, ob, ld, loff, c.n_tokens, d.G, etop, lost_anchor); break;
-      case 3: refined_run<3>(s, e, at, src, rsrc, ob, ld, loff, c.n_tokens, d.G, etop, lost_anchor); break;
-      case 4: refined_run<4>(s, e, at, src, rsrc, ob, ld, loff, c.n_tokens, d.G, etop, lost_anchor); break;
-      case 5: refined_run<5>(s, e, at, src, rsrc, ob, ld, loff, c.n_tokens, d.G, etop, lost_anchor); break;
-      default: refined_run<6>(s, e, at, src, rsrc, ob, ld, loff, c.n_tokens, d.G, etop, lost_anchor); break;
+    switch (ebits) {
+      case 2: refined_run_b<2>(b, s, e, at, src, rsrc, ob, ld, loff, c.n_tokens, d.G, lost_anchor); break;
+      case 3: refined_run_b<3>(b, s, e, at, src, rsrc, ob, ld, loff, c.n_tokens, d.G, lost_anchor); break;
+      case 4: refined_run_b<4>(b, s, e, at, src, rsrc, ob, ld, loff, c.n_tokens, d.G, lost_anchor); break;
+      case 5: refined_run_b<5>(b, s, e, at, src, rsrc, ob, ld, loff, c.n_tokens, d.G, lost_anchor); break;
+      default: refined_run_b<6>(b, s, e, at, src, rsrc, ob, ld, loff, c.n_tokens, d.G, lost_anchor); break;
     }
     const uint32_t nbytes =
         reinterpret_cast<const uint32_t *>(ci[k].records + (uint64_t)m * kRecBytes)[3];
@@ -822,14 +895,15 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode_refined(
   }
 }
 
-size_t decode_refined_lds_bytes(uint32_t waves) {
-  return (size_t)kARows * kRowBytes + (size_t)3 * kDRows * kRowBytes +
+size_t decode_refined_lds_bytes(uint32_t levels, uint32_t ebits, uint32_t waves) {
+  return (size_t)kARows * kRowBytes +
+         (size_t)levels * (kDRows + 2 * refine_rows(ebits)) * kRowBytes +
          sizeof(uint32_t) * (size_t)waves * kWave * 2 * kRing;
 }
 
 hipError_t launch_decode_refined(const Desc &d, uint32_t ebits, const ChunkInfo *dev_chunks,
                                  const ChunkInfo *dev_rchunks, const DecodeGroup *groups,
-                                 uint32_t n_groups, uint32_t waves, const uint8_t *valid,
+                                 uint32_t n_groups, uint32_t levels, uint32_t waves, const uint8_t *valid,
                                  const uint8_t *rvalid, const uint32_t *offsets,
                                  const uint32_t *roffsets, const uint8_t *tables,
                                  const uint8_t *rtables, int32_t *status, hipStream_t stream) {
@@ -837,7 +911,7 @@ hipError_t launch_decode_refined(const Desc &d, uint32_t ebits, const ChunkInfo 
   const uint32_t n_units = 2u * d.L * ncb;
   const uint64_t blocks = (uint64_t)((n_units + kXcds - 1) / kXcds) * kXcds * n_groups;
   hipLaunchKernelGGL(k_decode_refined, dim3((uint32_t)blocks), dim3(waves * kWave),
-                     decode_refined_lds_bytes(waves), stream, d, ebits, dev_chunks, dev_rchunks,
+                     decode_refined_lds_bytes(levels, ebits, waves), stream, d, ebits, dev_chunks, dev_rchunks,
                      groups, n_groups, n_units, valid, rvalid, offsets, roffsets, tables, rtables,
                      status);
   return hipGetLastError();

@@ -155,3 +155,89 @@ def test_full_size_config(idx):
     ratio = cfg.fp16_bytes() / enc.total_bytes()
     print(f"[fullsize] config {idx}: all {enc.n_chunks} chunks bit-exact "
           f"(oracle comparison {t_all:.1f} s), compression {ratio:.3f}", flush=True)
+
+
+@pytest.mark.timeout(900)
+def test_full_size_refinement():
+    """The refinement layer (4 bits) over the 70B-shaped workload's mixed
+    levels: the refinement tables completely, the refinement containers and
+    the refined KV of the first, middle and last chunks against the oracle,
+    and on every element the half-refinement-step bound, evaluated on the
+    GPU; the refined mean error is far below the base layer's."""
+    cfg = synth.CONFIGS[4]
+    E = 4
+    print(f"\n[fullsize refine] {cfg.name}: generating", flush=True)
+    p = synth.params(cfg)
+    kv = synth.make_kv(cfg, p=p)
+    kvp = synth.make_profile_kv(cfg, p=p)
+    levels = cfg.chunk_levels()
+    d = kvc.make_desc(cfg.n_layers, cfg.n_channels, cfg.delta_bits)
+    od = oracle.desc_for(cfg)
+
+    print("[fullsize refine] gpu profile / encode / decode", flush=True)
+    kv_dev = _t(kv)
+    kvp_dev = _t(kvp)
+    tables = kvc.profile(d, kvp_dev)
+    rtables = kvc.profile_refine(d, tables, kvp_dev, E)
+    del kvp_dev
+    enc = kvc.encode(d, tables, kv_dev, levels)
+    renc = kvc.encode_refine(d, rtables, E, kv_dev, levels)
+    base = kvc.decode(d, tables, kvc.chunk_refs(enc), cfg.n_tokens)
+    ref = kvc.decode_refined(d, tables, rtables, E, kvc.refined_chunk_refs(enc, renc), cfg.n_tokens)
+    torch.cuda.synchronize()
+
+    print("[fullsize refine] oracle profiles", flush=True)
+    otb = oracle.profile(od, kvp)
+    ort = oracle.profile_refine(od, kvp, E, otb.profile_id)
+    del kvp
+    S = d.n_streams
+    A = (1 << E) - 1
+    blob = rtables.cpu().numpy()
+    sec = blob[128:].view(np.uint16).reshape(2, d.n_levels, S, 64)
+    for kind, want in ((0, ort.fEA), (1, ort.fED)):
+        got = np.diff(sec[kind][:, :, :A + 1].astype(np.int32), axis=2)
+        np.testing.assert_array_equal(got, want[:, :, :A].astype(np.int32))
+    assert kvc.refine_id(rtables) == ort.refine_id
+
+    print("[fullsize refine] half-refinement-step bound on every element", flush=True)
+    L, C = cfg.n_layers, cfg.n_channels
+    err_b = err_r = 0.0
+    for k in range(renc.n_chunks):
+        n = renc.n_tokens[k]
+        t0 = 1500 * k
+        rec = renc.container(k)[64:64 + 16 * S].view(torch.float32).view(S, 4)
+        Da = rec[:, 0].reshape(L, 2, 1, C).double()
+        Dd = rec[:, 1].reshape(L, 2, 1, C).double()
+        is_anchor = (torch.arange(n, device=DEV) % 10 == 0).view(1, 1, n, 1)
+        D = torch.where(is_anchor, Da, Dd)
+        x = kv_dev[:, :, t0:t0 + n].view(torch.float16).double()
+        y = ref[:, :, t0:t0 + n].view(torch.float16).double()
+        xb = base[:, :, t0:t0 + n].view(torch.float16).double()
+        assert torch.isfinite(y).all()
+        _, e16 = torch.frexp(y.abs())
+        ulp16 = torch.clamp(torch.ldexp(torch.ones_like(y), e16 - 11), min=2.0 ** -24)
+        big = x.abs() + 8 * D + xb.abs()
+        _, e32 = torch.frexp(big)
+        ulp32 = torch.clamp(torch.ldexp(torch.ones_like(big), e32 - 24), min=2.0 ** -149)
+        bound = D / 2 + D * 2.0 ** -14 + ulp16 / 2 + 4 * ulp32
+        bad = (x - y).abs() > bound
+        assert not bad.any(), (k, int(bad.sum()))
+        err_b += float((x - xb).abs().sum())
+        err_r += float((x - y).abs().sum())
+        del x, y, xb, big, bound, bad, D
+    assert err_r < err_b / 5, (err_r, err_b)
+
+    for k in _sample_chunks(cfg):
+        print(f"[fullsize refine] oracle chunk {k} (level {levels[k]})", flush=True)
+        oc = oracle.encode_chunk(od, otb, kv, k, levels[k])
+        orc = oracle.encode_refine_chunk(od, ort, kv, k, levels[k])
+        assert np.array_equal(renc.container(k).cpu().numpy(), orc), f"refinement container {k}"
+        n = renc.n_tokens[k]
+        oo = np.zeros((cfg.n_layers, 2, n, cfg.n_channels), np.uint16)
+        oracle.decode_refined_chunk_into(od, otb, oc, ort, orc, 0, n, levels[k], oo)
+        got = ref[:, :, 1500 * k:1500 * k + n].cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(got, oo)
+        del oc, orc, oo, got
+    print(f"[fullsize refine] refinement {renc.total_bytes() / 1e9:.3f} GB over base "
+          f"{enc.total_bytes() / 1e9:.3f} GB; mean |error| {err_b / kv.size:.3e} -> "
+          f"{err_r / kv.size:.3e}", flush=True)

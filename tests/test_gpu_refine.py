@@ -41,6 +41,10 @@ CASES = {
     "E2_one_level": (3, 64, 1600, 10, 1500, ((5, 4, 3),), [0, 0], 2, 82),
     "E6_every_token_anchor": (2, 70, 900, 1, 400, ((6, 5, 4), (4, 3, 2)), [1, 0, 1], 6, 83),
     "E5_groups_of_7": (3, 130, 2100, 7, 1000, ((4, 3, 2), (6, 6, 6)), [1, 0, 1], 5, 84),
+    # 60 chunks of 50 tokens: several workgroup chunk groups, each over
+    # three levels
+    "E6_many_small_chunks": (2, 64, 3000, 10, 50, ((6, 5, 4), (5, 4, 3), (4, 3, 2)),
+                             [(7 * i) % 3 for i in range(60)], 6, 85),
 }
 
 
