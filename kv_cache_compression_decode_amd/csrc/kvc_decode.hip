@@ -35,7 +35,9 @@
 //    32..63 the high halves, so a half-wave never collides on an LDS bank;
 //  * stream bytes are staged per lane in a 16-byte LDS ring (stored
 //    byte-reversed, so the next four bytes are one funnel shift of two
-//    aligned dwords) fed in 8-byte blocks: a lane stores the block it loaded
+//    aligned dwords; ring dword k of a wave's lane l is the wave's LDS dword
+//    64 k + l, so whatever ring positions the lanes are at, the 64 lanes of
+//    a read touch 64 different banks) fed in 8-byte blocks: a lane stores the block it loaded
 //    earlier only when its ring runs low (at most 8 bytes left at a group's
 //    anchor, fewer than 2 before any other token) and then asks for its next
 //    one, so a load has about a group of tokens to arrive;
@@ -63,6 +65,7 @@ __host__ __device__ constexpr uint32_t refine_rows(uint32_t ebits) { return (1u 
 constexpr uint32_t kRowBytes = 2 * kWave;  // one u16 entry for each of the 64 lanes
 constexpr uint32_t kRing = 7;       // dwords per lane ring: 2 spare, 16 bytes, mirror of bytes 0..3
 constexpr uint32_t kRingLead = 2;   // spare dwords before the ring's byte 0
+constexpr uint32_t kRingStride = 4 * kWave;  // LDS bytes from a lane's ring dword k to k + 1
 constexpr uint32_t kXcds = 8;
 
 // Explicit address spaces for the LDS tables / rings and the output, so that
@@ -118,9 +121,11 @@ struct Source {
 // most significant first, and that dword lies inside the two aligned dwords
 // at (-p mod 16) & 12: one paired LDS read and one funnel shift whose shift
 // count is the bit position itself.  Two spare dwords precede the ring, so
-// that both halves are written by the same three stores (below).
+// that both halves are written by the same three stores (below).  A lane's
+// ring dwords are kRingStride bytes apart (the wave's 64 rings interleaved
+// dword by dword).
 struct Stream {
-  lds_u32 *ring;        // this lane's ring in LDS (20 bytes)
+  lds_u32 *ring;        // this lane's ring dword 0 in LDS
   uint32_t code, range;
   uint32_t nrpos;       // -(bits consumed) mod 2^32 (a multiple of 8)
   uint32_t nwlim;       // -(bits written to the ring, less 16): past it fewer
@@ -130,7 +135,7 @@ struct Stream {
   uint32_t rem;         // the stream's blocks the lane has not asked for
   uint32_t hoff;        // byte offset of the held block in the container
   uint32_t wbase;       // LDS address the next block is written from: ring
-                        // byte 0, or 8 bytes before it (alternating)
+                        // dword 0, or two ring dwords before it (alternating)
   uint32_t wsum;        // the sum of those two addresses
   int32_t M;
   uint32_t dbase;       // LDS byte address of this lane's delta row 0
@@ -141,16 +146,16 @@ struct Stream {
 
   // The held block, byte-reversed, into the free half of the ring: its
   // first stream byte is a multiple of 16 (dwords 4, 3 and the mirror 0) or
-  // 8 past one (dwords 2, 1).  Written from w = ring byte 0 or 8 bytes before
-  // it, the same three stores do both: dwords w+0 and w+4 take the block's
-  // first four bytes (the mirror and dword 4, or a spare dword and dword 2),
-  // dword w+3 the other four (dword 3, or dword 1).
+  // 8 past one (dwords 2, 1).  Written from w = ring dword 0 or two ring
+  // dwords before it, the same three stores do both: ring dwords w+0 and w+4
+  // take the block's first four bytes (the mirror and dword 4, or a spare
+  // dword and dword 2), dword w+3 the other four (dword 3, or dword 1).
   __device__ inline void put_block() {
     lds_u32 *w = (lds_u32 *)(uintptr_t)wbase;
     const uint32_t lo = __builtin_bswap32(held[0]);
     w[0] = lo;
-    w[4] = lo;
-    w[3] = __builtin_bswap32(held[1]);
+    w[4 * kWave] = lo;
+    w[3 * kWave] = __builtin_bswap32(held[1]);
     wbase = wsum - wbase;
     nwlim -= 64;
   }
@@ -215,8 +220,8 @@ template <bool kSymbols, bool kAnchor, uint32_t kSteps>
 __device__ inline uint32_t step(Stream &x, const AnchorTop &at, uint64_t &lost_anchor) {
   // the next four stream bytes, most significant first
   const lds_u32 *rd =
-      (const lds_u32 *)(uintptr_t)(lds_addr(x.ring) + (dword_of(x.nrpos) << 2));
-  const uint32_t in = __builtin_amdgcn_alignbit(rd[1], rd[0], x.nrpos);
+      (const lds_u32 *)(uintptr_t)(lds_addr(x.ring) + dword_of(x.nrpos) * kRingStride);
+  const uint32_t in = __builtin_amdgcn_alignbit(rd[kWave], rd[0], x.nrpos);
   const uint32_t r = x.range >> kPrec;
   // binary search; the entries of its first two steps are fixed for the
   // whole stream and held in registers, the rest are read from LDS
@@ -376,8 +381,8 @@ struct RStream {
     lds_u32 *w = (lds_u32 *)(uintptr_t)wbase;
     const uint32_t lo = __builtin_bswap32(held[0]);
     w[0] = lo;
-    w[4] = lo;
-    w[3] = __builtin_bswap32(held[1]);
+    w[4 * kWave] = lo;
+    w[3 * kWave] = __builtin_bswap32(held[1]);
     wbase = wsum - wbase;
     nwlim -= 64;
   }
@@ -407,11 +412,11 @@ __device__ inline uint32_t rstep(Stream &x, RStream &e, const AnchorTop &at,
                                  uint64_t &lost_anchor) {
   constexpr uint32_t kind = kAnchor ? 0 : 1;
   const lds_u32 *rd =
-      (const lds_u32 *)(uintptr_t)(lds_addr(x.ring) + (dword_of(x.nrpos) << 2));
-  const uint32_t in = __builtin_amdgcn_alignbit(rd[1], rd[0], x.nrpos);
+      (const lds_u32 *)(uintptr_t)(lds_addr(x.ring) + dword_of(x.nrpos) * kRingStride);
+  const uint32_t in = __builtin_amdgcn_alignbit(rd[kWave], rd[0], x.nrpos);
   const lds_u32 *erd =
-      (const lds_u32 *)(uintptr_t)(lds_addr(e.ring) + (dword_of(e.nrpos) << 2));
-  const uint32_t ein = __builtin_amdgcn_alignbit(erd[1], erd[0], e.nrpos);
+      (const lds_u32 *)(uintptr_t)(lds_addr(e.ring) + dword_of(e.nrpos) * kRingStride);
+  const uint32_t ein = __builtin_amdgcn_alignbit(erd[kWave], erd[0], e.nrpos);
   const uint32_t r = x.range >> kPrec;
   const uint32_t er = e.range >> kPrec;
   // the first two levels of both searches from registers
@@ -530,7 +535,7 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
   lds_u32 *lds = (lds_u32 *)lds_raw;
   lds_u32 *sA = lds;                                    // [kARows][64] u16 anchor cum
   lds_u32 *sD = sA + kARows * kWave / 2;                // [levels used][kDRows][64] u16 delta cum
-  lds_u32 *sR = sD + nlev_used * kDRows * kWave / 2;    // [waves][64][kRing] rings
+  lds_u32 *sR = sD + nlev_used * kDRows * kWave / 2;    // [waves][kRing][64] rings
   lds_u16 *hA = (lds_u16 *)sA;
   lds_u16 *hD = (lds_u16 *)sD;
 
@@ -584,7 +589,7 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
   const uint32_t m = m0 + lane;
   // this wave's ring (one register holds its address, so that a ring read
   // is one bit-field extract and one shift-add)
-  uint32_t ring_addr = lds_addr(sR + (wave * kWave + lane) * kRing + kRingLead);
+  uint32_t ring_addr = lds_addr(sR + (wave * kRing + kRingLead) * kWave + lane);
   __asm__ volatile("" : "+v"(ring_addr));
   uint32_t loff = lane * esz;
   __asm__ volatile("" : "+v"(loff));
@@ -637,16 +642,16 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode(
       src.cnt += (uint32_t)__builtin_popcountll(mask);
     }
     s.rem = nblk < 3 ? 0u : nblk - 3;
-    s.ring[4] = __builtin_bswap32(blk[0][0]);
-    s.ring[3] = __builtin_bswap32(blk[0][1]);
-    s.ring[2] = __builtin_bswap32(blk[1][0]);
-    s.ring[1] = __builtin_bswap32(blk[1][1]);
+    s.ring[4 * kWave] = __builtin_bswap32(blk[0][0]);
+    s.ring[3 * kWave] = __builtin_bswap32(blk[0][1]);
+    s.ring[2 * kWave] = __builtin_bswap32(blk[1][0]);
+    s.ring[1 * kWave] = __builtin_bswap32(blk[1][1]);
     s.ring[0] = __builtin_bswap32(blk[0][0]);
     s.held[0] = blk[2][0];
     s.held[1] = blk[2][1];
     s.nwlim = 0u - (128 - 16);
     s.wbase = ring_addr;  // block 2 goes to dwords 4, 3 and the mirror
-    s.wsum = 2u * ring_addr - 8u;
+    s.wsum = 2u * ring_addr - 2u * kRingStride;
     s.code = bswap32(blk[0][0]);
     s.nrpos = 0u - 32;
     s.range = 0xFFFFFFFFu;
@@ -701,7 +706,7 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode_refined(
   lds_u32 *lds = (lds_u32 *)lds_raw;
   // [kARows][64] anchor cum, then one slot per level the group uses: base
   // delta cum [kDRows][64], refinement cum of anchor tokens and of the other
-  // tokens [erows][64] each; then the rings [waves][64][2][kRing]
+  // tokens [erows][64] each; then the rings [waves][2][kRing][64]
   lds_u32 *sA = lds;
   lds_u32 *sL = sA + kARows * kWave / 2;
   lds_u32 *sR = sL + __builtin_popcount(level_mask) * slot_rows * kWave / 2;
@@ -762,9 +767,9 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode_refined(
   const uint32_t m = m0 + lane;
   const int32_t Me = (1 << (ebits - 1)) - 1;
   const uint32_t etop = 1u << (ebits - 1);
-  uint32_t ring_addr = lds_addr(sR + ((wave * kWave + lane) * 2) * kRing + kRingLead);
+  uint32_t ring_addr = lds_addr(sR + (2 * wave * kRing + kRingLead) * kWave + lane);
   __asm__ volatile("" : "+v"(ring_addr));
-  const uint32_t rring_addr = ring_addr + kRing * 4;
+  const uint32_t rring_addr = ring_addr + kRing * kRingStride;
   uint32_t loff = lane * 2u;
   __asm__ volatile("" : "+v"(loff));
 
@@ -847,30 +852,30 @@ __global__ __launch_bounds__(kMaxWaves *kWave) void k_decode_refined(
       rsrc.cnt += (uint32_t)__builtin_popcountll(rmask);
     }
     s.rem = nblk < 3 ? 0u : nblk - 3;
-    s.ring[4] = __builtin_bswap32(blk[0][0]);
-    s.ring[3] = __builtin_bswap32(blk[0][1]);
-    s.ring[2] = __builtin_bswap32(blk[1][0]);
-    s.ring[1] = __builtin_bswap32(blk[1][1]);
+    s.ring[4 * kWave] = __builtin_bswap32(blk[0][0]);
+    s.ring[3 * kWave] = __builtin_bswap32(blk[0][1]);
+    s.ring[2 * kWave] = __builtin_bswap32(blk[1][0]);
+    s.ring[1 * kWave] = __builtin_bswap32(blk[1][1]);
     s.ring[0] = __builtin_bswap32(blk[0][0]);
     s.held[0] = blk[2][0];
     s.held[1] = blk[2][1];
     s.nwlim = 0u - (128 - 16);
     s.wbase = ring_addr;
-    s.wsum = 2u * ring_addr - 8u;
+    s.wsum = 2u * ring_addr - 2u * kRingStride;
     s.code = bswap32(blk[0][0]);
     s.nrpos = 0u - 32;
     s.range = 0xFFFFFFFFu;
     e.rem = rnblk < 3 ? 0u : rnblk - 3;
-    e.ring[4] = __builtin_bswap32(rblk[0][0]);
-    e.ring[3] = __builtin_bswap32(rblk[0][1]);
-    e.ring[2] = __builtin_bswap32(rblk[1][0]);
-    e.ring[1] = __builtin_bswap32(rblk[1][1]);
+    e.ring[4 * kWave] = __builtin_bswap32(rblk[0][0]);
+    e.ring[3 * kWave] = __builtin_bswap32(rblk[0][1]);
+    e.ring[2 * kWave] = __builtin_bswap32(rblk[1][0]);
+    e.ring[1 * kWave] = __builtin_bswap32(rblk[1][1]);
     e.ring[0] = __builtin_bswap32(rblk[0][0]);
     e.held[0] = rblk[2][0];
     e.held[1] = rblk[2][1];
     e.nwlim = 0u - (128 - 16);
     e.wbase = rring_addr;
-    e.wsum = 2u * rring_addr - 8u;
+    e.wsum = 2u * rring_addr - 2u * kRingStride;
     e.code = bswap32(rblk[0][0]);
     e.nrpos = 0u - 32;
     e.range = 0xFFFFFFFFu;
