@@ -384,7 +384,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--oracle-chunks", type=int, default=11,
                     help="chunks decoded by the CPU oracle for the baseline and the bit-exact check")
@@ -392,6 +392,8 @@ def main() -> int:
     ap.add_argument("--decode-only", action="store_true",
                     help="skip the restore, level-choice and multi-request measurements "
                          "(profiler passes of the decode kernel)")
+    ap.add_argument("--with-refinement", action="store_true",
+                    help="with --decode-only: still measure the refinement layer")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer three times (HBM counter calibration)")
     args = ap.parse_args()
@@ -424,7 +426,8 @@ def main() -> int:
     kvp_dev = torch.from_numpy(kvp.view(np.int16)).to(dev)
     tables = kvc.profile(d, kvp_dev)
     refine_bits = 4
-    rtables = None if args.decode_only else kvc.profile_refine(d, tables, kvp_dev, refine_bits)
+    do_refine = args.with_refinement or not args.decode_only
+    rtables = kvc.profile_refine(d, tables, kvp_dev, refine_bits) if do_refine else None
     del kvp_dev
     torch.cuda.synchronize()
 
@@ -504,9 +507,10 @@ def main() -> int:
 
     restore = controller = multi = refine = None
     renc = refined_out = None
-    if not args.decode_only:
+    if do_refine:
         refine, renc, refined_out = measure_refine(kvc, d, tables, rtables, refine_bits, enc,
                                                    kv_dev, out, cfg, levels)
+    if not args.decode_only:
         restore = measure_restore(kvc, d, tables, enc, cfg, out)
         controller = measure_controller(kvc, d, tables, kv_dev, cfg)
         multi = measure_multi(kvc, d, tables, kv_dev, cfg)
