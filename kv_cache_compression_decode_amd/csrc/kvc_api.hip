@@ -312,15 +312,15 @@ constexpr uint32_t kRefineMinBits = 2, kRefineMaxBits = 6;
 bool refine_bits_ok(uint32_t e) { return e >= kRefineMinBits && e <= kRefineMaxBits; }
 
 // Refinement encode: one wave per (chunk, unit) item; the emit waves share
-// at most this much scratch.
-constexpr uint64_t kRefineScratchCap = 256ull << 20;
+// at most this much scratch (about 14 waves per CU at 1,500-token chunks).
+constexpr uint64_t kRefineScratchCap = 1ull << 30;
 uint32_t refine_items(const Desc &d, uint32_t K) {
   return K * 2u * d.L * ((d.C + kWave - 1) / kWave);
 }
 uint32_t refine_emit_blocks(const Desc &d, uint32_t K) {
   const uint64_t per = (uint64_t)kWave * refine_emit_lane_bytes(d.chunk);
   const uint64_t cap = std::max<uint64_t>(1, kRefineScratchCap / per);
-  return (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>({cap, 2048, refine_items(d, K)}));
+  return (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>({cap, 4096, refine_items(d, K)}));
 }
 uint32_t refine_stat_blocks(const Desc &d, uint32_t K) {
   return std::max<uint32_t>(1, std::min<uint32_t>(4096, refine_items(d, K)));

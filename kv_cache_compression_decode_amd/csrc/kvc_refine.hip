@@ -69,6 +69,21 @@ __device__ inline const uint16_t *refine_cum(const uint8_t *rtables, const Desc 
          (((uint64_t)kind * d.nlev + lv) * S + m) * kDeltaStride;
 }
 
+// A lane's two refinement tables (cum[0..A], A = 2^E - 1) copied to its
+// column of a wave's LDS copy [2][64 entries][64 lanes], read back by the
+// same lane only (so no barrier): the coder's per-token lookups then wait on
+// LDS, not on memory.
+struct RefineCumLds {
+  uint16_t e[2][kDeltaStride][kWave];
+};
+__device__ inline void stage_refine_cum(RefineCumLds &t, const uint16_t *ca, const uint16_t *cd,
+                                        uint32_t A, uint32_t lane) {
+  for (uint32_t i = 0; i <= A; ++i) {
+    t.e[0][i][lane] = ca[i];
+    t.e[1][i][lane] = cd[i];
+  }
+}
+
 // One stream's base side information at Mb = 2^(b-1) - 1 and the maxima of
 // |x - xh| over its anchor tokens and its other tokens.  Returns false if a
 // value is not finite.
@@ -256,6 +271,7 @@ __global__ __launch_bounds__(kWave) void k_refine_stats(
     if (blockIdx.x == 0 && lane == 0) set_status(status, KVC_ERR_PROFILE_MISMATCH);
     return;
   }
+  __shared__ RefineCumLds cum_lds;
   for (uint32_t item = blockIdx.x; item < n_items; item += gridDim.x) {
     const RefineItem it = refine_item(d, item);
     if (lane >= it.nv) continue;
@@ -269,12 +285,13 @@ __global__ __launch_bounds__(kWave) void k_refine_stats(
     if (!refine_scan(x, c.n_tokens, d.G, Mb, lo, sa, dl, amax, dmax))
       set_status(status, KVC_ERR_NONFINITE);
     const float Da = amax / (float)Me, Dd = dmax / (float)Me;
-    const uint16_t *ca = refine_cum(rtables, d, c.level, 0, m);
-    const uint16_t *cd = refine_cum(rtables, d, c.level, 1, m);
+    stage_refine_cum(cum_lds, refine_cum(rtables, d, c.level, 0, m),
+                     refine_cum(rtables, d, c.level, 1, m), 2u * (uint32_t)Me + 1u, lane);
     uint32_t range = 0xFFFFFFFFu, shifts = 0;
     refine_symbols(x, c.n_tokens, d.G, Mb, Me, lo, sa, dl, Da, Dd, [&](uint32_t s, bool anchor) {
-      const uint16_t *cum = anchor ? ca : cd;
-      range = __umul24(range >> kPrec, (uint32_t)cum[s + 1] - cum[s]);
+      const uint32_t kind = anchor ? 0u : 1u;
+      range = __umul24(range >> kPrec,
+                       (uint32_t)cum_lds.e[kind][s + 1][lane] - cum_lds.e[kind][s][lane]);
       const uint32_t sh = ffbh32(range) & 24u;
       range <<= sh;
       shifts += sh >> 3;
@@ -306,8 +323,15 @@ __global__ __launch_bounds__(kWave) void k_refine_emit(
   const uint32_t S = n_streams(d);
   const int32_t Me = (1 << (ebits - 1)) - 1;
   const uint32_t cap = (uint32_t)pad8(4u + 2u * d.chunk);
-  uint8_t *buf = scratch + ((uint64_t)blockIdx.x * kWave + lane) * lane_stride;
-  uint8_t *shifts = buf + cap;
+  // the wave's scratch, lanes interleaved dword by dword: byte p of lane l at
+  // (p / 4) * 256 + 4 l + p % 4, so the 64 lanes' stores at nearby stream
+  // positions share a few cache lines; the bytes first, then the shifts
+  uint8_t *wbuf = scratch + (uint64_t)blockIdx.x * kWave * lane_stride;
+  uint8_t *wshifts = wbuf + (uint64_t)kWave * cap;
+  __shared__ RefineCumLds cum_lds;
+  auto at = [&](uint8_t *base, uint32_t p) -> uint8_t & {
+    return base[(uint64_t)(p >> 2) * (4 * kWave) + 4 * lane + (p & 3u)];
+  };
   for (uint32_t item = blockIdx.x; item < n_items; item += gridDim.x) {
     const RefineItem it = refine_item(d, item);
     if (lane >= it.nv) continue;
@@ -327,52 +351,87 @@ __global__ __launch_bounds__(kWave) void k_refine_emit(
     rout[1] = rin[1];
     rout[2] = 0;
     rout[3] = nbytes;
-    const uint16_t *ca = refine_cum(rtables, d, c.level, 0, m);
-    const uint16_t *cd = refine_cum(rtables, d, c.level, 1, m);
+    stage_refine_cum(cum_lds, refine_cum(rtables, d, c.level, 0, m),
+                     refine_cum(rtables, d, c.level, 1, m), 2u * (uint32_t)Me + 1u, lane);
     Column x{reinterpret_cast<const uint8_t *>(kv + ((uint64_t)it.row * T + c.first_token) * d.C +
                                                it.c0),
              2ull * d.C, 2 * lane};
-    // the stream's bytes, carries added into the bytes already there
-    uint64_t low = 0;
-    uint32_t range = 0xFFFFFFFFu, pos = 0, j = 0;
+    // the stream's bytes: the newest (up to 8) held in `win`, newest lowest,
+    // where a carry is one add; older bytes leave to the scratch four at a
+    // time (positions pos - nwin.. are held, so pos - nwin stays a multiple
+    // of 4); a carry through all held bytes goes on into the scratch
+    uint64_t low = 0, win = 0;
+    uint32_t range = 0xFFFFFFFFu, pos = 0, nwin = 0, j = 0, shw = 0;
     bool bad = false;
+    auto put_dword = [&](uint8_t *base, uint32_t p, uint32_t v) {
+      *reinterpret_cast<uint32_t *>(&at(base, p)) = v;
+    };
+    auto push = [&](uint32_t byte) {
+      if (nwin == 8) {
+        // the oldest four held bytes, oldest first in memory
+        if (pos - 8u + 4u <= cap) put_dword(wbuf, pos - 8u, __builtin_bswap32((uint32_t)(win >> 32)));
+        else bad = true;
+        win &= 0xFFFFFFFFull;
+        nwin = 4;
+      }
+      win = (win << 8) | byte;
+      ++nwin;
+      ++pos;
+    };
     refine_symbols(x, n, d.G, Mb, Me, sd[0], sd[1], sd[2], Da, Dd, [&](uint32_t s, bool anchor) {
-      const uint16_t *cum = anchor ? ca : cd;
-      const uint32_t cs = cum[s], f = (uint32_t)cum[s + 1] - cs;
+      const uint32_t kind = anchor ? 0u : 1u;
+      const uint32_t cs = cum_lds.e[kind][s][lane];
+      const uint32_t f = (uint32_t)cum_lds.e[kind][s + 1][lane] - cs;
       const uint32_t r = range >> kPrec;
       // (HIP's __umul24 returns int: widen the product through uint32_t)
       low += (uint64_t)(uint32_t)__umul24(r, cs);
       range = __umul24(r, f);
       if (low >> 32) {
         low &= 0xFFFFFFFFull;
-        uint32_t p = pos;
-        for (;;) {
-          if (p == 0) {  // a carry past the first byte: impossible for valid models
-            bad = true;
-            break;
+        const uint64_t w1 = win + 1u;
+        const bool out = nwin == 8 ? w1 == 0 : (w1 >> (8u * nwin)) != 0;
+        win = nwin == 8 ? w1 : w1 & ((1ull << (8u * nwin)) - 1u);
+        if (out) {  // every held byte was 0xFF: on into the scratch (rare)
+          uint32_t p = pos - nwin;
+          for (;;) {
+            if (p == 0) {  // a carry past the first byte: impossible for valid models
+              bad = true;
+              break;
+            }
+            --p;
+            const uint8_t nb = (uint8_t)(at(wbuf, p) + 1u);
+            at(wbuf, p) = nb;
+            if (nb != 0) break;
           }
-          --p;
-          const uint8_t nb = (uint8_t)(buf[p] + 1u);
-          buf[p] = nb;
-          if (nb != 0) break;
         }
       }
       const uint32_t sh = ffbh32(range) & 24u;
       for (uint32_t t = 0; t < sh; t += 8) {
-        if (pos < cap) buf[pos] = (uint8_t)(low >> 24); else bad = true;
-        ++pos;
+        push((uint32_t)(low >> 24) & 0xFFu);
         low = (low << 8) & 0xFFFFFFFFull;
       }
       range <<= sh;
-      shifts[j++] = (uint8_t)(sh >> 3);
+      // the shift counts (bytes per token), four tokens to a dword
+      shw |= (sh >> 3) << (8u * (j & 3u));
+      if ((j & 3u) == 3u) {
+        put_dword(wshifts, j & ~3u, shw);
+        shw = 0;
+      }
+      ++j;
     });
+    if (j & 3u) put_dword(wshifts, j & ~3u, shw);
     for (uint32_t t = 0; t < 4; ++t) {
-      if (pos < cap) buf[pos] = (uint8_t)(low >> 24); else bad = true;
-      ++pos;
+      push((uint32_t)(low >> 24) & 0xFFu);
       low = (low << 8) & 0xFFFFFFFFull;
     }
+    // the held bytes, then zeros to the block end
+    for (uint32_t i = 0; i < nwin; ++i) {
+      const uint32_t p = pos - nwin + i;
+      if (p < cap) at(wbuf, p) = (uint8_t)(win >> (8u * (nwin - 1u - i)));
+      else bad = true;
+    }
     bad = bad || pos != nbytes;
-    for (uint32_t p = pos; p < cap && (p & 7u) != 0; ++p) buf[p] = 0;
+    for (uint32_t p = pos; p < cap && (p & 7u) != 0; ++p) at(wbuf, p) = 0;
 
     // the reading rule: a lane's i-th request takes the unit's next payload
     // block, requests of one step in lane order
@@ -380,10 +439,9 @@ __global__ __launch_bounds__(kWave) void k_refine_emit(
     uint8_t *pay = cont + kHdrBytes + (uint64_t)kRecBytes * S +
                    offsets[(uint64_t)it.k * S + it.row * d.C + it.c0];
     auto copy_block = [&](uint32_t blk, uint32_t slot) {
-      const uint32_t *src = reinterpret_cast<const uint32_t *>(buf + (uint64_t)blk * kBlock);
       uint32_t *dst = reinterpret_cast<uint32_t *>(pay + (uint64_t)slot * kBlock);
-      dst[0] = src[0];
-      dst[1] = src[1];
+      dst[0] = *reinterpret_cast<const uint32_t *>(&at(wbuf, blk * kBlock));
+      dst[1] = *reinterpret_cast<const uint32_t *>(&at(wbuf, blk * kBlock + 4));
     };
     uint32_t cnt = 0, R = 4, W = 16, q = 0;
     for (uint32_t blk = 0; blk < 3; ++blk) {
@@ -407,7 +465,7 @@ __global__ __launch_bounds__(kWave) void k_refine_emit(
       }
       if (need) W += kBlock;
       cnt += (uint32_t)__builtin_popcountll(mask);
-      R += shifts[jj];
+      R += at(wshifts, jj);
       g = g + 1 == d.G ? 0 : g + 1;
     }
     if (bad || R != nbytes || q != nblk) set_status(status, KVC_ERR_CORRUPT_STREAM);
