@@ -315,9 +315,14 @@ uint64_t kvc_decode_refined_ws_bytes(const kvc_codec_desc *d, uint32_t n_chunks)
  * every lane decodes a stream's base layer and its refinement layer token by
  * token and writes the refined binary16 values into kv_out
  * [L][2][T_total][C].  Token ranges must be disjoint and inside T_total.
- * Device errors: those of kvc_decode, plus KVC_ERR_PROFILE_MISMATCH for a
- * refinement made with other tables, and KVC_ERR_CORRUPT_STREAM for a
- * refinement of another chunk.
+ * Device errors: those of kvc_decode, plus KVC_ERR_PROFILE_MISMATCH for
+ * refinement tables made for another descriptor or E or for other base
+ * tables (their base id is not `tables`' profile id) and for a refinement
+ * container made with other refinement tables, and KVC_ERR_CORRUPT_STREAM
+ * for a refinement of another chunk (the token it was encoded from differs
+ * from its base container's) or a damaged refinement stream.  Chunks are
+ * grouped by level as in kvc_decode; each workgroup also stages the two
+ * refinement models of every level it decodes.
  */
 kvc_status kvc_decode_refined(const kvc_codec_desc *d, const void *tables, const void *rtables,
                               uint32_t refine_bits, const kvc_refined_chunk_ref *chunks,
