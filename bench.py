@@ -37,7 +37,9 @@ COPY_CALIBRATION_BYTES = 1 << 30
 # workload; its figures are reported only for that workload, and only while the
 # kernel sources still hash to the value recorded there.
 COUNTERS_MD = os.path.join(ROOT, "profiles", "k_decode_70b-gqa-16K_hbm_counters.md")
-COUNTERS_WORKLOAD = "llama-70b-gqa-shape-16K"
+# the workload the metric is quoted on, and the one the committed counters cover
+DEFAULT_WORKLOAD = "llama-70b-gqa-shape-16K"
+COUNTERS_WORKLOAD = DEFAULT_WORKLOAD
 DECODE_SOURCES = [os.path.join(ROOT, "kv_cache_compression_decode_amd", "csrc", f)
                   for f in ("kvc_decode.hip", "kvc_internal.h")]
 METRIC = "decoded KV GB/s on 1 MI355X (+% HBM roofline), bit-exact vs oracle; compression ratio"
@@ -385,7 +387,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="a workload of synth.WORKLOADS, by name")
     ap.add_argument("--oracle-chunks", type=int, default=11,
                     help="chunks decoded by the CPU oracle for the baseline and the bit-exact check")
     ap.add_argument("--no-oracle", action="store_true")
@@ -412,7 +415,7 @@ def main() -> int:
     import synth
 
     dev = torch.device("cuda:0")
-    cfg = synth.CONFIGS[args.config]
+    cfg = synth.WORKLOADS[args.workload]
     levels = cfg.chunk_levels()
     log(f"workload {cfg.name}: generating {cfg.fp16_bytes() / 1e9:.2f} GB of binary16 KV")
     t0 = time.time()

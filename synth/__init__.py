@@ -40,7 +40,7 @@ N_PROFILE_CHUNKS = 3
 
 @dataclasses.dataclass(frozen=True)
 class Config:
-    index: int
+    seed_index: int  # offset of this workload's seeds from SEED_BASE
     name: str
     n_layers: int
     n_channels: int  # per K and per V: kv_heads * head_dim
@@ -56,7 +56,7 @@ class Config:
 
     @property
     def seed(self) -> int:
-        return SEED_BASE + self.index
+        return SEED_BASE + self.seed_index
 
     @property
     def n_chunks(self) -> int:
@@ -76,7 +76,7 @@ class Config:
         if self.schedule == "level1":
             return [1] * self.n_chunks
         if self.schedule == "mixed":
-            return levels_sequence(SEED_BASE + LEVEL_SEED_OFFSET + self.index,
+            return levels_sequence(SEED_BASE + LEVEL_SEED_OFFSET + self.seed_index,
                                    self.n_chunks, self.n_levels)
         raise ValueError(self.schedule)
 
@@ -87,28 +87,30 @@ class Config:
         return 2 * self.n_layers * self.n_channels * self.n_tokens * 2
 
 
-CONFIGS = {
-    0: Config(0, "tiny-4L-512ch-1.5K", 4, 512, 1500, 0, 0.9, 0.9, 0.0, 8.0, 1,
-              "level0", "4 layers, 8 heads x 64, one 1,500-token chunk, no outliers"),
-    1: Config(1, "llama2-7b-shape-9K", 32, 4096, 9000, 0, 0.9, 0.9, 0.01, 8.0, 1,
-              "level0", "32 layers, 32 heads x 128, 6 chunks of 1,500 tokens"),
-    2: Config(2, "llama2-13b-shape-16K", 40, 5120, 16000, 0, 0.9, 0.9, 0.01, 8.0, 3,
-              "level1", "40 layers, 40 heads x 128, 16,000 tokens, 3 levels, decode the middle one"),
-    3: Config(3, "34b-gqa-shape-80K", 48, 1024, 80000, 1, 0.8, 0.97, 0.01, 8.0, 1,
-              "level0", "48 layers, 8 KV heads x 128, 80,000 tokens, rho ~ U(0.8, 0.97)"),
-    4: Config(4, "llama-70b-gqa-shape-16K", 80, 1024, 16000, 0, 0.9, 0.9, 0.01, 8.0, 3,
-              "mixed", "80 layers, 8 KV heads x 128, 16,000 tokens, seeded mixed levels"),
-}
+TINY = Config(0, "tiny-4L-512ch-1.5K", 4, 512, 1500, 0, 0.9, 0.9, 0.0, 8.0, 1,
+              "level0", "4 layers, 8 heads x 64, one 1,500-token chunk, no outliers")
+SHAPE_7B_9K = Config(1, "llama2-7b-shape-9K", 32, 4096, 9000, 0, 0.9, 0.9, 0.01, 8.0, 1,
+                     "level0", "32 layers, 32 heads x 128, 6 chunks of 1,500 tokens")
+SHAPE_13B_16K = Config(2, "llama2-13b-shape-16K", 40, 5120, 16000, 0, 0.9, 0.9, 0.01, 8.0, 3,
+                       "level1",
+                       "40 layers, 40 heads x 128, 16,000 tokens, 3 levels, decode the middle one")
+SHAPE_34B_GQA_80K = Config(3, "34b-gqa-shape-80K", 48, 1024, 80000, 1, 0.8, 0.97, 0.01, 8.0, 1,
+                           "level0", "48 layers, 8 KV heads x 128, 80,000 tokens, rho ~ U(0.8, 0.97)")
+SHAPE_70B_GQA_16K = Config(4, "llama-70b-gqa-shape-16K", 80, 1024, 16000, 0, 0.9, 0.9, 0.01, 8.0, 3,
+                           "mixed", "80 layers, 8 KV heads x 128, 16,000 tokens, seeded mixed levels")
+# the workloads by name
+WORKLOADS = {w.name: w for w in (TINY, SHAPE_7B_9K, SHAPE_13B_16K, SHAPE_34B_GQA_80K,
+                                 SHAPE_70B_GQA_16K)}
 
 
 def small_config(n_layers: int, n_channels: int, n_tokens: int, n_levels: int = 3,
-                 schedule: str = "mixed", index: int = 90, rho_mode: int = 0,
+                 schedule: str = "mixed", seed_index: int = 90, rho_mode: int = 0,
                  outlier_frac: float = 0.01, rho: Optional[float] = None) -> Config:
     """A reduced configuration with the same value model, for quick tests
     (`rho` overrides the constant AR(1) coefficient, e.g. 0 for white noise)."""
     lo = 0.8 if rho_mode else (0.9 if rho is None else rho)
     hi = 0.97 if rho_mode else lo
-    return Config(index, f"small-{n_layers}L-{n_channels}ch-{n_tokens}", n_layers,
+    return Config(seed_index, f"small-{n_layers}L-{n_channels}ch-{n_tokens}", n_layers,
                   n_channels, n_tokens, rho_mode, lo, hi, outlier_frac, 8.0, n_levels, schedule,
                   "reduced test configuration")
 

@@ -45,8 +45,8 @@ def record(cfg, levels):
 def main():
     data = {
         "note": "oracle outputs on seeded synthetic KV; regression fixture written by make_golden.py",
-        "tiny": record(synth.CONFIGS[0], synth.CONFIGS[0].chunk_levels()),
-        "mixed_small": record(synth.small_config(6, 96, 3700, n_levels=3, schedule="mixed", index=91),
+        "tiny": record(synth.TINY, synth.TINY.chunk_levels()),
+        "mixed_small": record(synth.small_config(6, 96, 3700, n_levels=3, schedule="mixed", seed_index=91),
                               [0, 2, 1]),
     }
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "oracle_tiny.json")

@@ -17,11 +17,11 @@ def _load():
 
 def test_tiny_fixture():
     want = _load()["tiny"]
-    got = record(synth.CONFIGS[0], synth.CONFIGS[0].chunk_levels())
+    got = record(synth.TINY, synth.TINY.chunk_levels())
     assert got == want
 
 
 def test_mixed_small_fixture():
     want = _load()["mixed_small"]
-    got = record(synth.small_config(6, 96, 3700, n_levels=3, schedule="mixed", index=91), [0, 2, 1])
+    got = record(synth.small_config(6, 96, 3700, n_levels=3, schedule="mixed", seed_index=91), [0, 2, 1])
     assert got == want

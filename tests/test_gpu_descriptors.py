@@ -33,7 +33,7 @@ def _t(a):
 def test_descriptor_bit_exact(name):
     L, C, T, G, chunk, bits, levels, index = CASES[name]
     print(f"\n[gpu descriptor] {name}", flush=True)
-    cfg = synth.small_config(L, C, T, n_levels=len(bits), index=index)
+    cfg = synth.small_config(L, C, T, n_levels=len(bits), seed_index=index)
     kv = synth.make_kv(cfg)
     kvp = synth.make_profile_kv(cfg)
     od = oracle.Desc(L, C, G, chunk, 8, tuple(tuple(b) for b in bits), 15)
@@ -58,7 +58,7 @@ def test_many_chunks_in_one_call():
     chunks in reverse order through kvc_decode_multi."""
     L, C, T, G, chunk = 2, 64, 1400, 5, 10
     print("\n[gpu descriptor] 140 chunks", flush=True)
-    cfg = synth.small_config(L, C, T, n_levels=3, index=78)
+    cfg = synth.small_config(L, C, T, n_levels=3, seed_index=78)
     kv = synth.make_kv(cfg)
     kvp = synth.make_profile_kv(cfg)
     bits = ((6, 5, 4), (5, 4, 3), (4, 3, 2))

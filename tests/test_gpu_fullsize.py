@@ -1,4 +1,5 @@
-"""GPU parity at the full workload sizes (configurations 1-4), through the C ABI.
+"""GPU parity at the full workload sizes (the 7B-, 13B-, 34B-GQA- and 70B-GQA-shaped
+workloads), through the C ABI.
 
 Against the oracle, chunk by chunk (one chunk's oracle container and
 decoded KV in host memory at a time):
@@ -89,10 +90,11 @@ def _sample_chunks(cfg):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("idx", [1, 2, 3, 4])
-def test_full_size_config(idx):
-    cfg = synth.CONFIGS[idx]
-    print(f"\n[fullsize] config {idx} {cfg.name}: generating", flush=True)
+@pytest.mark.parametrize("name", [synth.SHAPE_7B_9K.name, synth.SHAPE_13B_16K.name,
+                                  synth.SHAPE_34B_GQA_80K.name, synth.SHAPE_70B_GQA_16K.name])
+def test_full_size_workload(name):
+    cfg = synth.WORKLOADS[name]
+    print(f"\n[fullsize] {cfg.name}: generating", flush=True)
     p = synth.params(cfg)
     kv = synth.make_kv(cfg, p=p)
     kvp = synth.make_profile_kv(cfg, p=p)
@@ -153,7 +155,7 @@ def test_full_size_config(idx):
         for k in range(enc.n_chunks):
             assert sizes[0][k] > sizes[1][k] > sizes[2][k], (k, sizes[0][k], sizes[1][k], sizes[2][k])
     ratio = cfg.fp16_bytes() / enc.total_bytes()
-    print(f"[fullsize] config {idx}: all {enc.n_chunks} chunks bit-exact "
+    print(f"[fullsize] {cfg.name}: all {enc.n_chunks} chunks bit-exact "
           f"(oracle comparison {t_all:.1f} s), compression {ratio:.3f}", flush=True)
 
 
@@ -164,7 +166,7 @@ def test_full_size_refinement():
     the refined KV of the first, middle and last chunks against the oracle,
     and on every element the half-refinement-step bound, evaluated on the
     GPU; the refined mean error is far below the base layer's."""
-    cfg = synth.CONFIGS[4]
+    cfg = synth.SHAPE_70B_GQA_16K
     E = 4
     print(f"\n[fullsize refine] {cfg.name}: generating", flush=True)
     p = synth.params(cfg)

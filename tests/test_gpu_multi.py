@@ -21,7 +21,7 @@ DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
 
 class Requests:
     def __init__(self):
-        base = synth.small_config(2, 96, 3700, n_levels=3, index=91)
+        base = synth.small_config(2, 96, 3700, n_levels=3, seed_index=91)
         self.d = kvc.make_desc(base.n_layers, base.n_channels, base.delta_bits)
         od = oracle.desc_for(base)
         kvp = synth.make_profile_kv(base)
@@ -29,7 +29,7 @@ class Requests:
         self.tables = kvc.profile(self.d, torch.from_numpy(kvp.view(np.int16)).to(DEV))
         self.req = []
         for idx, T, levels in ((91, 3700, [0, 2, 1]), (92, 1600, [1, 0]), (93, 900, [2])):
-            cfg = synth.small_config(2, 96, T, n_levels=3, index=idx)
+            cfg = synth.small_config(2, 96, T, n_levels=3, seed_index=idx)
             kv = synth.make_kv(cfg)
             cont = oracle.encode(od, otb, kv, levels)
             want = oracle.decode(od, otb, cont, levels, T)

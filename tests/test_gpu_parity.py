@@ -48,17 +48,17 @@ class Case:
 
 
 CASES = {
-    "tiny": lambda: Case(synth.CONFIGS[0], synth.CONFIGS[0].chunk_levels()),
+    "tiny": lambda: Case(synth.TINY, synth.TINY.chunk_levels()),
     # ragged channel count (96 = 64 + 32), 6 layers, partial last chunk of 700 tokens
-    "mixed": lambda: Case(synth.small_config(6, 96, 3700, n_levels=3, index=91), [0, 2, 1]),
+    "mixed": lambda: Case(synth.small_config(6, 96, 3700, n_levels=3, seed_index=91), [0, 2, 1]),
     # C = 70 (ragged block), 5 layers (thirds 2/1/2), last chunk of 11 tokens
-    "ragged": lambda: Case(synth.small_config(5, 70, 1511, n_levels=2, index=94), [1, 0]),
+    "ragged": lambda: Case(synth.small_config(5, 70, 1511, n_levels=2, seed_index=94), [1, 0]),
     # per-channel rho, one token in the last chunk
-    "rho": lambda: Case(synth.small_config(3, 64, 3001, n_levels=1, index=95, rho_mode=1), [0, 0, 0]),
+    "rho": lambda: Case(synth.small_config(3, 64, 3001, n_levels=1, seed_index=95, rho_mode=1), [0, 0, 0]),
     # white noise (no token locality): long, high-entropy streams
-    "noise": lambda: Case(synth.small_config(3, 128, 3000, n_levels=2, index=98, rho=0.0), [0, 1]),
+    "noise": lambda: Case(synth.small_config(3, 128, 3000, n_levels=2, seed_index=98, rho=0.0), [0, 1]),
     # nine chunks in one call: two chunk groups per workgroup grid, mixed levels
-    "many": lambda: Case(synth.small_config(2, 64, 13000, n_levels=3, index=99),
+    "many": lambda: Case(synth.small_config(2, 64, 13000, n_levels=3, seed_index=99),
                          [0, 1, 2, 2, 1, 0, 0, 2, 1]),
 }
 
@@ -271,7 +271,7 @@ def test_nonfinite_input_reported(mixed):
 def test_constant_and_extreme_channels_bit_exact():
     """Constant channels (zero scales), tiny subnormal-range values and values
     near the binary16 maximum, against the oracle."""
-    cfg = synth.small_config(3, 64, 1500, n_levels=1, index=96)
+    cfg = synth.small_config(3, 64, 1500, n_levels=1, seed_index=96)
     kv = synth.make_kv(cfg).copy()
     kv[0, 0, :, 0] = np.float16(1.5).view(np.uint16)
     kv[0, 1, :, 3] = 0
@@ -304,7 +304,7 @@ def test_quantizer_ties_bit_exact():
       channel 2: anchors all 1.0 (sa = 0, ahat = 1), deltas (2k + 1) / 128
         for k = -M..M-1 plus one of M / 64 in each chunk, so dl = 2^-6 and
         d / dl = k + 1/2 (M = 31, 15, 7 in the three layers' thirds)."""
-    cfg = synth.small_config(3, 64, 3000, n_levels=1, index=97)
+    cfg = synth.small_config(3, 64, 3000, n_levels=1, seed_index=97)
     kv = synth.make_kv(cfg).copy()
     n = cfg.n_tokens
     f16 = lambda a: np.asarray(a, np.float16).view(np.uint16)

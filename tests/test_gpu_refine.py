@@ -52,7 +52,7 @@ CASES = {
 def test_refinement_bit_exact(name):
     L, C, T, G, chunk, bits, levels, E, index = CASES[name]
     print(f"\n[gpu refine] {name}", flush=True)
-    cfg = synth.small_config(L, C, T, n_levels=len(bits), index=index)
+    cfg = synth.small_config(L, C, T, n_levels=len(bits), seed_index=index)
     kv = synth.make_kv(cfg)
     kvp = synth.make_profile_kv(cfg)
     od = oracle.Desc(L, C, G, chunk, 8, tuple(tuple(b) for b in bits), 15)
@@ -78,7 +78,7 @@ def test_refinement_bit_exact(name):
 def test_refined_chunks_to_other_positions():
     L, C, T, G, chunk, bits, levels, E, index = CASES["mixed_levels_E4"]
     print("\n[gpu refine] chunks to other positions", flush=True)
-    cfg = synth.small_config(L, C, T, n_levels=len(bits), index=index)
+    cfg = synth.small_config(L, C, T, n_levels=len(bits), seed_index=index)
     kv = synth.make_kv(cfg)
     kvp = synth.make_profile_kv(cfg)
     od = oracle.desc_for(cfg)
@@ -103,7 +103,7 @@ def test_refined_chunks_to_other_positions():
 def test_refinement_errors_reported():
     L, C, T, G, chunk, bits, levels, E, index = CASES["mixed_levels_E4"]
     print("\n[gpu refine] error paths", flush=True)
-    cfg = synth.small_config(L, C, T, n_levels=len(bits), index=index)
+    cfg = synth.small_config(L, C, T, n_levels=len(bits), seed_index=index)
     kv = synth.make_kv(cfg)
     kvp = synth.make_profile_kv(cfg)
     d = kvc.make_desc(L, C, bits)

@@ -26,7 +26,7 @@ class Ctx:
     """Nine chunks (13,000 tokens: the last one 1,000) at mixed levels."""
 
     def __init__(self):
-        cfg = synth.small_config(2, 64, 13000, n_levels=3, index=99)
+        cfg = synth.small_config(2, 64, 13000, n_levels=3, seed_index=99)
         self.cfg = cfg
         self.levels = [0, 1, 2, 2, 1, 0, 0, 2, 1]
         kv = synth.make_kv(cfg)

@@ -30,7 +30,7 @@ def _busy_current_stream():
 
 def test_side_stream_calls_bit_exact():
     print("\n[gpu streams] 4 layers x 192 channels, 3,100 tokens, mixed levels", flush=True)
-    cfg = synth.small_config(4, 192, 3100, n_levels=3, schedule="mixed", index=95)
+    cfg = synth.small_config(4, 192, 3100, n_levels=3, schedule="mixed", seed_index=95)
     levels = [1, 2, 0]
     kv = synth.make_kv(cfg)
     kvp = synth.make_profile_kv(cfg)

@@ -39,7 +39,7 @@ def _f16_ulp(h_bits):
 
 @pytest.fixture(scope="module")
 def tiny():
-    cfg = synth.CONFIGS[0]
+    cfg = synth.TINY
     d = oracle.desc_for(cfg)
     kv = synth.make_kv(cfg)
     tb = oracle.profile(d, synth.make_profile_kv(cfg))
@@ -52,7 +52,7 @@ def tiny():
 def mixed():
     """Reduced mixed-level configuration: 6 layers (thirds 2/2/2), 96
     channels, 3 levels, 3,700 tokens -> chunks of 1500, 1500, 700."""
-    cfg = synth.small_config(6, 96, 3700, n_levels=3, schedule="mixed", index=91)
+    cfg = synth.small_config(6, 96, 3700, n_levels=3, schedule="mixed", seed_index=91)
     d = oracle.desc_for(cfg)
     kv = synth.make_kv(cfg)
     tb = oracle.profile(d, synth.make_profile_kv(cfg))
@@ -124,7 +124,7 @@ def test_no_clamp_changes_rint(mixed):
 def test_anchor_precision_above_delta_precision():
     """8-bit anchors are above every level's delta bits, and deeper layer
     thirds never get finer deltas than shallower ones."""
-    for cfg in synth.CONFIGS.values():
+    for cfg in synth.WORKLOADS.values():
         for row in cfg.delta_bits:
             assert all(b < 8 for b in row)
             assert row[0] >= row[1] >= row[2]
@@ -294,7 +294,7 @@ def test_coder_bound_and_gibbs_per_stream(mixed):
 def test_payload_vs_empirical_entropy_self_profile():
     """Profile on the very data that is encoded: payload bits >= the empirical
     entropy H_emp (Gibbs) and <= H_emp + 0.03 bit/symbol + 32 bits/stream."""
-    cfg = synth.small_config(3, 64, 1500, n_levels=1, schedule="level0", index=92)
+    cfg = synth.small_config(3, 64, 1500, n_levels=1, schedule="level0", seed_index=92)
     d = oracle.desc_for(cfg)
     kv = synth.make_kv(cfg)
     tb = oracle.profile(d, kv)  # models fitted to the encoded chunk itself

@@ -55,7 +55,7 @@ def test_block_order_short_streams():
 
 @pytest.fixture(scope="module")
 def mixed():
-    cfg = synth.small_config(3, 150, 3100, index=95)  # 3 channel blocks per row (64, 64, 22)
+    cfg = synth.small_config(3, 150, 3100, seed_index=95)  # 3 channel blocks per row (64, 64, 22)
     d = oracle.desc_for(cfg)
     kv = synth.make_kv(cfg)
     tb = oracle.profile(d, synth.make_profile_kv(cfg))

@@ -33,7 +33,7 @@ RED = -math.log2(1 - 2.0 ** -9)
 
 @pytest.fixture(scope="module")
 def mixed():
-    cfg = synth.small_config(6, 96, 3700, n_levels=3, schedule="mixed", index=98)
+    cfg = synth.small_config(6, 96, 3700, n_levels=3, schedule="mixed", seed_index=98)
     d = oracle.desc_for(cfg)
     kv = synth.make_kv(cfg)
     kvp = synth.make_profile_kv(cfg)

@@ -37,21 +37,20 @@ def test_innovations_are_standard_normal():
 
 
 def test_outlier_count_exact_per_row():
-    for idx in (1, 3, 4):
-        cfg = synth.CONFIGS[idx]
+    for cfg in (synth.SHAPE_7B_9K, synth.SHAPE_34B_GQA_80K, synth.SHAPE_70B_GQA_16K):
         p = synth.params(cfg)
         per_row = p.is_outlier.reshape(2 * cfg.n_layers, cfg.n_channels).sum(axis=1)
         assert np.all(per_row == round(0.01 * cfg.n_channels))
-    p0 = synth.params(synth.CONFIGS[0])
+    p0 = synth.params(synth.TINY)
     assert p0.is_outlier.sum() == 0
 
 
 def test_rho_per_channel_range():
-    cfg = synth.CONFIGS[3]
+    cfg = synth.SHAPE_34B_GQA_80K
     p = synth.params(cfg)
     assert p.rho.min() >= 0.8 and p.rho.max() <= 0.97
     assert np.std(p.rho) > 0.04  # U(0.8, 0.97) has sd 0.049
-    assert np.all(synth.params(synth.CONFIGS[4]).rho == 0.9)
+    assert np.all(synth.params(synth.SHAPE_70B_GQA_16K).rho == 0.9)
 
 
 def test_lag_difference_variance_closed_form():
@@ -104,9 +103,9 @@ def test_profile_chunks_share_processes_not_innovations():
 
 
 def test_level_schedule_is_seeded_and_mixed():
-    cfg = synth.CONFIGS[4]
+    cfg = synth.SHAPE_70B_GQA_16K
     lv = cfg.chunk_levels()
     assert len(lv) == 11 and set(lv) == {0, 1, 2}
     assert lv == cfg.chunk_levels()
-    assert synth.CONFIGS[2].chunk_levels() == [1] * 11
-    assert synth.CONFIGS[3].n_chunks == 54
+    assert synth.SHAPE_13B_16K.chunk_levels() == [1] * 11
+    assert synth.SHAPE_34B_GQA_80K.n_chunks == 54

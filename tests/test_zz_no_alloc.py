@@ -22,7 +22,7 @@ def _t(a):
 
 def test_decode_static_equals_decode_two_calls():
     print("\n[gpu no-alloc] 8 layers x 320 channels, 6,100 tokens, mixed levels", flush=True)
-    cfg = synth.small_config(8, 320, 6100, n_levels=3, schedule="mixed", index=96)
+    cfg = synth.small_config(8, 320, 6100, n_levels=3, schedule="mixed", seed_index=96)
     levels = [2, 0, 1, 1, 0]
     d = kvc.make_desc(cfg.n_layers, cfg.n_channels, cfg.delta_bits)
     tables = kvc.profile(d, _t(synth.make_profile_kv(cfg)))
