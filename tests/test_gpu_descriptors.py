@@ -22,6 +22,13 @@ CASES = {
     "two_token_chunks": (2, 64, 9, 2, 2, ((6, 5, 4),), [0] * 5, 75),
     "smallest_alphabets": (3, 64, 1700, 10, 1500, ((2, 2, 2),), [0, 0], 76),
     "largest_alphabets": (3, 64, 1700, 5, 1500, ((6, 6, 6),), [0, 0], 77),
+    # the largest chunk the descriptor allows, then a ragged one
+    "longest_chunks": (2, 64, 65535 + 100, 10, 65535, ((6, 5, 4), (4, 3, 2)), [0, 1], 79),
+    # one group over a whole 65,535-token chunk: one anchor, then 65,534 deltas
+    "longest_group": (1, 64, 65535, 65535, 65535, ((5, 4, 3),), [0], 80),
+    # the most levels a descriptor holds
+    "four_levels": (3, 96, 5600, 10, 1500, ((6, 5, 4), (5, 4, 3), (4, 3, 2), (3, 2, 2)),
+                    [3, 1, 2, 0], 86),
 }
 
 

@@ -45,6 +45,9 @@ CASES = {
     # three levels
     "E6_many_small_chunks": (2, 64, 3000, 10, 50, ((6, 5, 4), (5, 4, 3), (4, 3, 2)),
                              [(7 * i) % 3 for i in range(60)], 6, 85),
+    # the largest chunk the descriptor allows, then a ragged one; four levels
+    "E3_longest_chunks": (2, 64, 65535 + 77, 10, 65535,
+                          ((6, 5, 4), (5, 4, 3), (4, 3, 2), (3, 2, 2)), [3, 0], 3, 87),
 }
 
 
