@@ -32,11 +32,14 @@
 //                        information, its two scales and the exact coded
 //                        length of its refinement symbols;
 //   k_refine_emit      : per (chunk, unit), one wave: each stream's bytes
-//                        into linear scratch (carries added into the bytes
-//                        already there), then the reading rule replayed to
-//                        put every block in its place;
+//                        (the newest 8 held in a register, where a carry is
+//                        one add; older ones in the wave's lane-interleaved
+//                        scratch), then the reading rule replayed to put
+//                        every block in its place;
 //   k_refine_header    : the 64-byte headers.
-// Encode is offline: these kernels favour plainness over speed.
+// Both coding kernels copy each lane's two models into LDS once per item.
+// Encode is offline: one wave per item and a replay pass after the coder
+// keep the kernels short, at about 3x the base encode's time.
 #include "kvc_internal.h"
 
 namespace kvc {
