@@ -669,6 +669,25 @@ def main() -> int:
                       f"{one_bytes / 1e9:.2f} GB of binary16) in {one_s:.2f} s on one thread",
         }
         log(f"oracle on one core: {one_bytes / 1e9:.2f} GB in {one_s:.1f} s")
+        # and on the tiny workload (one 1,500-token chunk of 4 layers x 512
+        # channels), also on one core
+        tiny = synth.TINY
+        tkv = synth.make_kv(tiny)
+        tod = oracle.desc_for(tiny)
+        ttb = oracle.profile(tod, synth.make_profile_kv(tiny))
+        tlev = tiny.chunk_levels()
+        tcont = oracle.encode(tod, ttb, tkv, tlev)
+        oracle.set_threads(1)
+        t0 = time.perf_counter()
+        oracle.decode(tod, ttb, tcont, tlev, tiny.n_tokens)
+        tiny_s = time.perf_counter() - t0
+        oracle.set_threads(threads)
+        result["cpu_baseline_tiny_one_core"] = {
+            "value": round(tiny.fp16_bytes() / tiny_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"oracle decode of the whole {tiny.name} workload ({tiny.fp16_bytes() / 1e6:.1f} MB "
+                      f"of binary16) in {tiny_s:.2f} s on one thread",
+        }
     print(json.dumps(result), flush=True)
     return 0
 
