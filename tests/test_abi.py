@@ -244,3 +244,40 @@ def test_refinement_size_queries_and_argument_errors(L):
     refs[0].n_tokens = 10
     assert L.kvc_decode_refined(ctypes.byref(d), 4096, 4096, 4, refs, 1, 4096, 16000, 4096,
                                 1 << 40, 4096, None) == kvc.ERR_INVALID_ARG
+
+
+def test_refined_decode_synchronous_shape_errors(L):
+    """kvc_decode_refined rejects bad chunk lists before anything is queued
+    (no device call happens, so fake device addresses do)."""
+    d = kvc.make_desc(4, 128, delta_bits=((6, 5, 4), (4, 3, 2)))
+    S = 2 * 4 * 128
+    ws = 1 << 40
+
+    def refs(*spec):
+        arr = (kvc.RefinedChunkRef * len(spec))()
+        for i, (first, n, level) in enumerate(spec):
+            arr[i].container = 4096 * (2 * i + 1)
+            arr[i].refinement = 4096 * (2 * i + 2)
+            arr[i].container_bytes = arr[i].refinement_bytes = 64 + 16 * S + 64
+            arr[i].first_token = first
+            arr[i].n_tokens = n
+            arr[i].level = level
+        return arr
+
+    def call(arr, T_total=3000, ws_bytes=ws):
+        return L.kvc_decode_refined(ctypes.byref(d), 4096, 4096, 4, arr, len(arr), 4096, T_total,
+                                    4096, ws_bytes, 4096, None)
+
+    assert call(refs((0, 1500, 0), (1000, 1500, 1))) == kvc.ERR_SHAPE  # overlapping ranges
+    assert call(refs((0, 1501, 0))) == kvc.ERR_SHAPE                   # longer than a chunk
+    assert call(refs((2000, 1500, 0))) == kvc.ERR_SHAPE                # past T_total
+    assert call(refs((0, 0, 0))) == kvc.ERR_SHAPE                      # empty chunk
+    assert call(refs((0, 1500, 2))) == kvc.ERR_INVALID_ARG             # no such level
+    bad = refs((0, 1500, 0))
+    bad[0].reserved = 1
+    assert call(bad) == kvc.ERR_INVALID_ARG
+    small = refs((0, 1500, 0))
+    small[0].refinement_bytes = 64 + 16 * S - 1                        # records cut short
+    assert call(small) == kvc.ERR_SHAPE
+    need = L.kvc_decode_refined_ws_bytes(ctypes.byref(d), 1)
+    assert call(refs((0, 1500, 0)), ws_bytes=need - 1) == kvc.ERR_CAPACITY

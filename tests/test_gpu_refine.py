@@ -159,3 +159,16 @@ def test_refinement_errors_reported():
     with pytest.raises(kvc.KvcError) as e:
         kvc.decode_refined(d, tables, rtables, E, kvc.refined_chunk_refs(enc, enc), T)
     assert e.value.code == kvc.ERR_CORRUPT_STREAM
+
+
+def test_refined_decode_of_no_chunks_is_a_no_op():
+    L, C, T, G, chunk, bits, levels, E, index = CASES["E2_one_level"]
+    print("\n[gpu refine] no chunks", flush=True)
+    cfg = synth.small_config(L, C, T, n_levels=len(bits), seed_index=index)
+    kvp = synth.make_profile_kv(cfg)
+    d = kvc.make_desc(L, C, bits, group_tokens=G, chunk_tokens=chunk)
+    tables = kvc.profile(d, _t(kvp))
+    rtables = kvc.profile_refine(d, tables, _t(kvp), E)
+    out = torch.full((L, 2, T, C), 0x1234, dtype=torch.int16, device=DEV)
+    kvc.decode_refined(d, tables, rtables, E, [], T, out=out)
+    assert bool((out == 0x1234).all())
