@@ -49,13 +49,25 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def strip_comments(text: str) -> str:
+    """C/HIP source without its comments and blank lines (the sources hold no
+    string literal with comment markers), so that documentation edits keep
+    the counters' provenance while any code change breaks it."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def decode_source_hash() -> str:
+    """SHA-256 of the decode kernel's sources, comments stripped."""
     import hashlib
 
     h = hashlib.sha256()
     for f in DECODE_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(strip_comments(fh.read()).encode())
     return h.hexdigest()
 
 

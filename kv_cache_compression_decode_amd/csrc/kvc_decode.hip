@@ -51,6 +51,12 @@
 //    harmless (past the container end it reads as zero);
 //  * blocks are numbered so that the groups of one (row, channel block) run
 //    on the same XCD.
+//
+// The same file holds k_decode_refined (CacheGen page, 局限与 Future Work:
+// refinement bits sent after a low-quality KV): the same decomposition, each
+// lane decoding its stream's base layer and refinement layer side by side
+// (two rings, one fused step per token whose two binary searches issue their
+// LDS probes in lockstep) and storing binary16(fma(q, D, xh)) once.
 #include "kvc_internal.h"
 
 namespace kvc {
