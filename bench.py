@@ -387,6 +387,9 @@ def measure_refine(kvc, d, tables, rtables, ebits, enc, kv_dev, base_out, cfg, l
         "decoded_GBps": round(fp16_bytes / (med * 1e-3) / 1e9, 2),
         "algorithmic_GBps": round((fp16_bytes + enc.total_bytes() + renc.total_bytes())
                                   / (med * 1e-3) / 1e9, 2),
+        # binary16 written + both layers' containers read, against 8 TB/s
+        "hbm_frac": round((fp16_bytes + enc.total_bytes() + renc.total_bytes())
+                          / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "mean_abs_error_base": err_b / (fp16_bytes // 2),
         "mean_abs_error_refined": err_r / (fp16_bytes // 2),
     }
